@@ -1,0 +1,7 @@
+"""CPU oracle for the q4_K x q8 quantized matmul (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path never does.
+"""
+from .oracle import (blockdots, build, f16_bits, f16_to_f64, load, out_f64,  # noqa: F401
+                     q4k_unpack, quantize, set_threads, get_threads)

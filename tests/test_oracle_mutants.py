@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one (so that a passing pin suite means something)."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, planted mistake); each original occurs exactly once.
+MUTANTS = [
+    ("drop_min_term", "acc += main_term - corr_term;", "acc += main_term;"),
+    ("min_term_sign", "acc += main_term - corr_term;", "acc += main_term + corr_term;"),
+    ("sc_m_swapped", "(d * sc[j]) * da", "(d * mn[j]) * da"),
+    ("nibble_halves_swapped", "q[64 * p + i] = qs[32 * p + i] & 15;",
+     "q[64 * p + i] = qs[32 * p + i] >> 4;"),
+    ("subblock_index_off", "(dmin * mn[j]) * da", "(dmin * mn[(j + 1) & 7]) * da"),
+    ("high_scale_bits_wrong", "sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);",
+     "sc[j] = (s[j + 4] & 15) | ((s[j] >> 6) << 4);"),
+    ("ties_to_even", "float r = roundf(xb[i] / da);", "float r = rintf(xb[i] / da);"),
+    ("reciprocal_multiply", "float r = roundf(xb[i] / da);",
+     "float r = roundf(xb[i] * (1.0f / da));"),
+    ("scale_128", "const float da = amax / 127.0f;", "const float da = amax / 128.0f;"),
+    ("ssum_high_half_unsigned", "const int ssum = (int16_t)(uint16_t)(word >> 16);",
+     "const int ssum = (uint16_t)(word >> 16);"),
+    ("f16_truncates", "const double n = rint(a / quantum);",
+     "const double n = floor(a / quantum);"),
+    ("f16_no_subnormals", "v = ldexp((double)f, -24);", "v = 0.0;"),
+    ("dmin_is_d", "*dmin = oracle_f16_to_double(hm);", "*dmin = oracle_f16_to_double(hd);"),
+    ("dot_skips_last", "for (int i = 0; i < 32; i++)\n                        D += q4[j * 32 + i] * a[i];",
+     "for (int i = 0; i < 31; i++)\n                        D += q4[j * 32 + i] * a[i];"),
+]
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, orig, bad):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, "mutation anchor for %s not unique" % name
+    msrc = tmp_path / "oracle_mut.c"
+    msrc.write_text(src.replace(orig, bad))
+    so = str(tmp_path / "liboracle_mut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(msrc),
+                    "-o", so, "-lm"], check=True)
+    lib = oracle.load(so)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, "no pin caught planted mistake %s" % name
