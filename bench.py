@@ -1,0 +1,186 @@
+"""Benchmark of the q4_K x q8 MMQ hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+q8-quantize each activation matrix (q8_quantize_rows) and run every
+projection's MMQ with the two-term fold (mmq_q4k_q8_fp32out).  Inputs are
+resident in HBM before timing starts; several copies of the weights and
+activations are rotated so that the 256 MB last-level cache cannot hold a
+step's working set.
+
+Default workload: the 7B q-projection prefill, W[4096 x 4096] q4_K times
+X[2630 x 4096].  Prints one JSON line (see the keys in ``main``).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload qproj]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MMQ int8 TOPS (+% MFMA peak) and prefill tok/s over 7B projections"
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, published
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def build_workload(name: str):
+    """-> (description dict, inputs {name: X}, mats [(label, fields, input name)])."""
+    from q4_q8_integer_amd import synth
+    if name == "qproj":
+        f, x = synth.qproj_inputs()
+        return ({"workload": "7B q-proj prefill: q4_K W[4096x4096] x q8 X[2630x4096] -> fp32 [2630x4096]",
+                 "m": 4096, "k": 4096, "n": 2630},
+                {"x": x}, [("q", f, "x")])
+    if name == "ffn":
+        return ({"workload": "7B FFN prefill: gate,up q4_K [11008x4096] on X[2630x4096], "
+                             "down [4096x11008] on SiLU input [2630x11008]", "n": 2630},
+                {"x": synth.ffn_inputs("x"), "x_down": synth.ffn_inputs("x_down")},
+                [("gate", synth.ffn_inputs("gate"), "x"), ("up", synth.ffn_inputs("up"), "x"),
+                 ("down", synth.ffn_inputs("down"), "x_down")])
+    if name.startswith("layer"):
+        n = int(name[5:])
+        src = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in",
+               "gate": "ffn_in", "up": "ffn_in", "down": "down_in"}
+        inputs = {s: synth.layer_activation(s, n) for s in sorted(set(src.values()))}
+        mats = [(nm, synth.layer_weights(nm), src[nm]) for nm, _, _ in synth.LAYER_MATS]
+        return ({"workload": "7B layer projection set q,k,v,o,gate,up,down at N=%d "
+                             "(4 quantizes + 7 MMQs; 1%% of inputs x20)" % n, "n": n},
+                inputs, mats)
+    if name.startswith("wide_in") or name.startswith("wide_out"):
+        wname, n = name.rsplit("_n", 1)
+        n = int(n)
+        f = synth.weight_bound_weights(wname)
+        return ({"workload": "weight-bound q4_K W[%dx%d] at N=%d (10%% of sub-blocks sc=0)"
+                             % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
+                {"x": synth.weight_bound_activation(wname, n)}, [(wname, f, "x")])
+    raise SystemExit("unknown workload %r" % name)
+
+
+def cpu_baseline(mats, inputs, budget_s: float = 12.0):
+    """Time the oracle (as it stands) on a bounded token sample of the same
+    workload: quantize + float64 fold for every projection."""
+    import oracle
+    from q4_q8_integer_amd import synth
+
+    packed = [(synth.pack_q4k(f), f.m, f.k, src) for _, f, src in mats]
+    n_full = min(x.shape[0] for x in inputs.values())
+
+    def run(nt):
+        t0 = time.perf_counter()
+        qs = {s: oracle.quantize(x[:nt]) for s, x in inputs.items()}
+        for w, m, k, src in packed:
+            q, ds = qs[src]
+            oracle.out_f64(w, m, k, q, ds)
+        return time.perf_counter() - t0
+
+    probe = min(4, n_full)
+    t = run(probe)
+    nt = int(max(probe, min(n_full, probe * budget_s / max(t, 1e-6))))
+    t = run(nt)
+    ops = sum(2.0 * nt * m * k for _, m, k, _ in packed)
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.get_threads(),
+            "kind": "oracle", "tok_per_s": nt / t,
+            "sample": "first %d tokens of every input, all rows, quantize + float64 fold "
+                      "(%.1f s)" % (nt, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qproj")
+    ap.add_argument("--copies", type=int, default=3, help="rotated input copies (cache defeat)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from q4_q8_integer_amd import binding, synth
+
+    desc, inputs, mats = build_workload(args.workload)
+    dev = torch.device("cuda:0")
+    binding.load_library()
+
+    # resident inputs, several copies
+    sets = []
+    for _ in range(max(1, args.copies)):
+        xs = {s: torch.from_numpy(x).to(dev) for s, x in inputs.items()}
+        ws = [(lbl, torch.from_numpy(synth.pack_q4k(f)).to(dev), f.m, f.k, src)
+              for lbl, f, src in mats]
+        qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
+                  torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
+              for s, x in xs.items()}
+        outs = [torch.empty((xs[src].shape[0], m), dtype=torch.float32, device=dev)
+                for _, _, m, _, src in ws]
+        sets.append((xs, ws, qs, outs))
+    torch.cuda.synchronize()
+
+    n_tok = max(x.shape[0] for x in inputs.values())
+    mmq_ops = sum(2.0 * inputs[src].shape[0] * f.m * f.k for _, f, src in mats)
+    mmq_alg_bytes = sum(0.5625 * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
+                        + 4.0 * inputs[src].shape[0] * f.m for _, f, src in mats)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, timed):
+        xs, ws, qs, outs = sets[i % len(sets)]
+        for s, x in xs.items():
+            q, ds = qs[s]
+            binding.q8_quantize_rows(x, x.shape[0], x.shape[1], q, ds)
+        if timed:
+            ev[timed - 1][0].record()
+        for (lbl, w, m, k, src), out in zip(ws, outs):
+            q, ds = qs[src]
+            binding.mmq_q4k_q8_fp32out(w, m, k, q, ds, q.shape[0], out)
+        if timed:
+            ev[timed - 1][1].record()
+
+    for i in range(args.warmup):
+        step(i, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, i + 1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    mmq_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    achieved = mmq_ops / (mmq_ms * 1e-3) / 1e12
+    value = mmq_ops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": dict(desc, step="q8_quantize_rows + mmq_q4k_q8_fp32out per projection",
+                       copies=len(sets)),
+        "tok_per_s": round(n_tok / (ms_step * 1e-3), 1),
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "mmq_q4k_q8_fp32out", "achieved": round(achieved, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
+                     "alg_bytes_per_step": mmq_alg_bytes,
+                     "alg_gbs": round(mmq_alg_bytes / (mmq_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(mats, inputs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

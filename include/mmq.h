@@ -1,0 +1,113 @@
+/*
+ * mmq.h - C ABI of the q4_K x q8 quantized matrix multiply (MMQ) for MI355X.
+ *
+ * The operation (the yusiwen.cn "minfer" pages: r31 "q-major sda scale-read
+ * repack", sections 1 and 2, and r22 "qa8 XOR swizzle"): LLM prefill
+ * multiplies a weight matrix W[m x k], stored as 4-bit k-quant (q4_K)
+ * super-blocks, by activations X[n x k] that are quantized per token and per
+ * 32-element block to int8 with a per-block scale word.  Each 32-element
+ * chunk is an exact integer dot product, rescaled by the two-term rank-1 fold
+ *
+ *   out[t][o] = sum_c (d*sc)[o,c]*da[t,c]*D[t][o][c] - (dmin*m)[o,c]*da[t,c]*ssum[t,c]
+ *   D[t][o][c] = sum_{i<32} q4[o][32c+i] * q8[t][32c+i]
+ *
+ * Data formats
+ *   q4_K weights: m rows, each row k/256 super-blocks of 144 bytes, rows
+ *     contiguous (row o's super-block b at byte (o*(k/256) + b)*144).  Block:
+ *     d (binary16) at 0, dmin (binary16) at 2, twelve bytes of 6-bit (sc, m)
+ *     pairs at 4 (GGUF k-quant packing), 128 bytes of nibbles at 16: weight
+ *     64p+i is the low nibble of byte 32p+i, weight 64p+32+i its high nibble.
+ *   q8 activations: q int8 [n][k] row-major and one 32-bit scale word per
+ *     (token, 32-element block), ds uint32 [n][k/32]: binary16 da in the low
+ *     16 bits, ssum = sum of the block's 32 q values as a two's-complement
+ *     16-bit integer in the high 16 bits (r31 page, section 3.2).
+ *
+ * Conventions for every call
+ *   - All array pointers are DEVICE pointers, allocated and owned by the
+ *     caller; the library allocates nothing, keeps no pointer after
+ *     returning, and keeps no global state other than a per-device
+ *     "is this a gfx950" check.  Calls are reentrant.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream); the caller keeps every buffer alive until the stream has
+ *     finished.  Output buffers must not overlap inputs.
+ *   - Every pointer must be 16-byte aligned.
+ *   - n or m equal to 0 is an empty call: it returns MMQ_OK and touches
+ *     nothing (pointers may then be NULL).  Negative sizes are MMQ_ERR_SHAPE.
+ *   - Argument errors are detected on the host before any HIP call and
+ *     before anything is enqueued.  No call throws or aborts.
+ *   - Inputs must be finite.
+ */
+#ifndef Q4Q8_MMQ_H
+#define Q4Q8_MMQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+enum mmq_status {
+    MMQ_OK = 0,
+    MMQ_ERR_NULL = -1,      /* a required pointer is NULL */
+    MMQ_ERR_SHAPE = -2,     /* negative size, k not a multiple of 32 (quantize) or 256 (MMQ), k == 0 */
+    MMQ_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
+    MMQ_ERR_OVERFLOW = -4,  /* a size beyond the kernels' index range (see limits below) */
+    MMQ_ERR_DEVICE = -5,    /* no HIP device, or the current device is not gfx950 */
+    MMQ_ERR_HIP = -6        /* the HIP runtime reported an error at launch */
+};
+
+/* Size limits (MMQ_ERR_OVERFLOW beyond them): n, m <= 2^31 - 1; k <= 2^24;
+ * n*k and m*k/256*144 below 2^40; for mmq_q4k_q8 also n*m*(k/32) < 2^40. */
+
+/*
+ * q8_quantize_rows - per-token, per-32-element q8 quantization of activations.
+ * (Workload definition of the q8 activations: da = max|x|/127, q = round(x/da),
+ * ssum = sum q; packed scale word as in the r31 page, section 3.2.)
+ *
+ *   x   : float [n][k], row-major, k % 32 == 0.
+ *   q   : int8 [n][k] (out).   q = round(x / da), fp32 division, ties away from
+ *         zero, in [-127, 127]; da = fp32(max|x| / 127) of the block.
+ *   ds  : uint32 [n][k/32] (out).  binary16(da) (round to nearest even,
+ *         subnormals kept) | (uint16)ssum << 16.  An all-zero block gives
+ *         q = 0 and ds = 0.
+ */
+int q8_quantize_rows(const float *x, int64_t n, int64_t k, int8_t *q, uint32_t *ds,
+                     hipStream_t stream);
+
+/*
+ * mmq_q4k_q8 - exact per-block integer dot products (the int32 result of the
+ * 32-deep integer contraction, before the two-term rescale; r31 page, section 1).
+ *
+ *   w    : q4_K super-blocks of W [m][k] (m*(k/256)*144 bytes), k % 256 == 0.
+ *   q    : int8 [n][k] q8 activations.
+ *   ds   : the activations' scale words; accepted for a signature uniform with
+ *          mmq_q4k_q8_fp32out and not read (may be NULL).
+ *   dots : int32 [n][m][k/32] (out), dots[t][o][c] = D[t][o][c], exact.
+ * A parity/inspection entry: its output is 4*n*m*k/32 bytes.
+ */
+int mmq_q4k_q8(const void *w, int64_t m, int64_t k, const int8_t *q, const uint32_t *ds,
+               int64_t n, int32_t *dots, hipStream_t stream);
+
+/*
+ * mmq_q4k_q8_fp32out - the quantized matmul with the two-term rank-1 fold
+ * applied per 32-element chunk (r31 page, sections 1-2), float32 result.
+ *
+ *   w   : q4_K super-blocks of W [m][k], k % 256 == 0.
+ *   q   : int8 [n][k];  ds : uint32 [n][k/32] (as written by q8_quantize_rows).
+ *   out : float [n][m] (out), token-major: out[t][o].  The summation order is
+ *         the kernel's; results agree with the exact value to float32
+ *         rounding of the accumulation (relative L2 error <= 1e-5).
+ */
+int mmq_q4k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
+                       const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *mmq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4Q8_MMQ_H */

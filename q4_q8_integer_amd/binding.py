@@ -1,0 +1,122 @@
+"""Thin ctypes binding over the C ABI of ``include/mmq.h``.
+
+Argument marshalling only: torch tensors give device pointers and the current
+HIP stream; every step of the computation runs in the HIP kernels of
+``libq4q8mmq.so``.  There is no fallback: if the library is missing or the
+device is not gfx950, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
+EXPORTS = ("q8_quantize_rows", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_status_string")
+_lib = None
+
+
+class MMQError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, text, status))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("HIP library %s is missing: build it with "
+                           "`python -m q4_q8_integer_amd.build` (or __graft_entry__.build())" % path)
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.q8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.mmq_q4k_q8.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+    lib.mmq_q4k_q8_fp32out.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+    for fn in (lib.q8_quantize_rows, lib.mmq_q4k_q8, lib.mmq_q4k_q8_fp32out):
+        fn.restype = ctypes.c_int
+    lib.mmq_status_string.argtypes = [ctypes.c_int]
+    lib.mmq_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mmq_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MMQError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous %s tensor on a HIP device" % (name, dtype))
+
+
+# -------------------------------------------------------------- raw entries
+def q8_quantize_rows(x, n, k, q, ds):
+    """Enqueue the quantizer on preallocated outputs (C ABI call, same name)."""
+    _check("q8_quantize_rows", load_library().q8_quantize_rows(
+        _ptr(x), n, k, _ptr(q), _ptr(ds), _stream()))
+
+
+def mmq_q4k_q8(w, m, k, q, ds, n, dots):
+    _check("mmq_q4k_q8", load_library().mmq_q4k_q8(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
+
+
+def mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out):
+    _check("mmq_q4k_q8_fp32out", load_library().mmq_q4k_q8_fp32out(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
+
+
+# --------------------------------------------------------- tensor helpers
+def quantize(x: torch.Tensor):
+    """x float32 [n, k] -> (q int8 [n, k], ds int32 [n, k/32] holding the uint32 words)."""
+    _need(x, torch.float32, "x")
+    n, k = x.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=x.device)
+    ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
+    q8_quantize_rows(x, n, k, q, ds)
+    return q, ds
+
+
+def blockdots(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds=None):
+    """Exact int32 block dots [n, m, k/32]."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    n = q.shape[0]
+    dots = torch.empty((n, m, k // 32), dtype=torch.int32, device=q.device)
+    mmq_q4k_q8(w, m, k, q, ds, n, dots)
+    return dots
+
+
+def fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """Two-term-fold output float32 [n, m]."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    _need(ds, torch.int32, "ds")
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, torch.float32, "out")
+    mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out)
+    return out

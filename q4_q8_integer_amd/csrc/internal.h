@@ -1,0 +1,24 @@
+// internal.h - launchers shared between the kernel translation units and the
+// C-ABI entry points.  Arguments are validated by the caller (mmq_api.hip);
+// each launcher only enqueues work and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmq {
+
+// Bytes of one q4_K super-block (256 weights).
+constexpr int kBlockBytes = 144;
+
+hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
+                              hipStream_t stream);
+
+// Exact int32 block dots, dots[t][o][c].
+hipError_t launch_mmq_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,
+                           int32_t* dots, hipStream_t stream);
+
+// Two-term fold, float32 out[t][o].
+hipError_t launch_mmq_fp32(const uint8_t* w, int m, int k, const int8_t* q,
+                           const uint32_t* ds, int n, float* out, hipStream_t stream);
+
+}  // namespace mmq

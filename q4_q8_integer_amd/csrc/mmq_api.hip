@@ -1,0 +1,120 @@
+// mmq_api.hip - the C ABI declared in include/mmq.h.
+//
+// Every argument is checked on the host before any HIP call; only then is
+// the current device checked (once per device: gfx950 or MMQ_ERR_DEVICE) and
+// the kernel enqueued on the caller's stream.  Nothing here allocates.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/mmq.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffffLL;      // n, m
+constexpr int64_t kMaxK = 1LL << 24;
+constexpr int64_t kMaxElems = 1LL << 40;       // n*k, m*k/256*144, n*m, n*m*k/32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 0 = not yet checked, 1 = gfx950, 2 = something else.
+std::atomic<int> g_device_ok[64];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return MMQ_ERR_DEVICE;
+    }
+    if (dev < 64) {
+        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return MMQ_OK;
+        if (known == 2) return MMQ_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MMQ_ERR_DEVICE;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MMQ_OK : MMQ_ERR_DEVICE;
+}
+
+// Shared checks of the two MMQ calls (before any HIP call).
+int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, const void* out,
+              bool* empty) {
+    if (n < 0 || m < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
+    if (n > kMaxDim || m > kMaxDim || k > kMaxK) return MMQ_ERR_OVERFLOW;
+    if (n * k >= kMaxElems || m * (k / 256) * 144 >= kMaxElems || n * m >= kMaxElems)
+        return MMQ_ERR_OVERFLOW;
+    *empty = (n == 0 || m == 0);
+    if (*empty) return MMQ_OK;
+    if (!w || !q || !out) return MMQ_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(out)) return MMQ_ERR_ALIGN;
+    return MMQ_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MMQ_OK;
+    (void)hipGetLastError();
+    return MMQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_quantize_rows(const float* x, int64_t n, int64_t k, int8_t* q, uint32_t* ds,
+                     hipStream_t stream) {
+    if (n < 0 || k <= 0 || (k & 31) != 0) return MMQ_ERR_SHAPE;
+    if (n > kMaxDim || k > kMaxK || n * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (n == 0) return MMQ_OK;
+    if (!x || !q || !ds) return MMQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(ds)) return MMQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != MMQ_OK) return dev;
+    return hip_status(mmq::launch_q8_quantize(x, n * (k / 32), q, ds, stream));
+}
+
+int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
+               int64_t n, int32_t* dots, hipStream_t stream) {
+    (void)ds;  // not read: the block dots do not depend on the scales
+    bool empty = false;
+    int rc = check_mmq(w, m, k, q, n, dots, &empty);
+    if (rc != MMQ_OK || empty) return rc;
+    if (n * m >= kMaxElems / (k / 32)) return MMQ_ERR_OVERFLOW;
+    if (ds && !aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    return hip_status(mmq::launch_mmq_dots(static_cast<const uint8_t*>(w), (int)m, (int)k, q,
+                                           (int)n, dots, stream));
+}
+
+int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
+                       const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(w, m, k, q, n, out, &empty);
+    if (rc != MMQ_OK || empty) return rc;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    return hip_status(mmq::launch_mmq_fp32(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds,
+                                           (int)n, out, stream));
+}
+
+const char* mmq_status_string(int status) {
+    switch (status) {
+        case MMQ_OK: return "MMQ_OK";
+        case MMQ_ERR_NULL: return "MMQ_ERR_NULL: a required pointer is NULL";
+        case MMQ_ERR_SHAPE: return "MMQ_ERR_SHAPE: invalid size (negative, k == 0, or k not a multiple of 32/256)";
+        case MMQ_ERR_ALIGN: return "MMQ_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MMQ_ERR_OVERFLOW: return "MMQ_ERR_OVERFLOW: size beyond the kernels' index range";
+        case MMQ_ERR_DEVICE: return "MMQ_ERR_DEVICE: no HIP device, or the current device is not gfx950";
+        case MMQ_ERR_HIP: return "MMQ_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown mmq status";
+    }
+}
+
+}  // extern "C"

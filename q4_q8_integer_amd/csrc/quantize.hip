@@ -1,0 +1,93 @@
+// quantize.hip - q8 activation quantizer for gfx950.
+//
+// Per token and 32-element block (the q8 activation definition: da =
+// max|x|/127, q = round(x/da), ssum = sum q; the packed scale word of the
+// r31 page, section 3.2: binary16 da low, signed 16-bit ssum high).
+//
+// The input rows are contiguous and k % 32 == 0, so the n*k/32 blocks are
+// simply consecutive 128-byte runs of x: the kernel maps over blocks, not
+// rows.  A DPP quad (4 lanes) owns one block, 8 floats per lane (two 16-byte
+// loads); the block max and the sum are reduced inside the quad with
+// quad_perm DPP moves (no LDS).  A wave reads 2 KiB contiguously and writes
+// 512 contiguous bytes of q; the quantizer is HBM-bound (4 B read + 1.125 B
+// written per element).
+//
+// Numerics: x/da is the IEEE fp32 division (hipcc's default correctly
+// rounded divide; never built with fast-math), roundf rounds ties away from
+// zero, and v_cvt_f16_f32 rounds to nearest even keeping subnormals.
+#include "internal.h"
+
+namespace mmq {
+namespace {
+
+// quad_perm controls: lane i of each quad reads lane i^1, or lane i^2.
+constexpr int kQuadXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // [2,3,0,1]
+
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                __builtin_bit_cast(int, v), kQuadXor1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                __builtin_bit_cast(int, v), kQuadXor2, 0xF, 0xF, false)));
+    return v;
+}
+
+__device__ __forceinline__ int quad_sum(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, false);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void q8_quantize_kernel(const float* __restrict__ x,
+                                                          int64_t nblocks,
+                                                          int8_t* __restrict__ q,
+                                                          uint32_t* __restrict__ ds) {
+    const int64_t lane_id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = lane_id >> 2;  // quads are aligned, so a quad is all in or all out
+    if (blk >= nblocks) return;
+    const int part = threadIdx.x & 3;
+
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f* src = reinterpret_cast<const v4f*>(x + blk * 32 + part * 8);
+    const v4f lo = __builtin_nontemporal_load(src);      // read once: do not keep in cache
+    const v4f hi = __builtin_nontemporal_load(src + 1);
+    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = quad_max(amax);
+
+    uint32_t packed[2] = {0u, 0u};
+    int sum = 0;
+    uint32_t word = 0u;
+    if (amax > 0.0f) {
+        const float da = amax / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = roundf(v[i] / da);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            const int qi = (int)r;
+            sum += qi;
+            packed[i >> 2] |= (uint32_t)(qi & 0xFF) << (8 * (i & 3));
+        }
+        word = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)da);
+    }
+    sum = quad_sum(sum);
+    word |= (uint32_t)(uint16_t)(int16_t)sum << 16;
+
+    *reinterpret_cast<uint2*>(q + blk * 32 + part * 8) = make_uint2(packed[0], packed[1]);
+    if (part == 0) ds[blk] = word;
+}
+
+}  // namespace
+
+hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
+                              hipStream_t stream) {
+    const int64_t lanes = nblocks * 4;
+    const unsigned grid = (unsigned)((lanes + 255) / 256);
+    void* args[] = {(void*)&x, (void*)&nblocks, (void*)&q, (void*)&ds};
+    return hipLaunchKernel((const void*)q8_quantize_kernel, dim3(grid), dim3(256), args, 0, stream);
+}
+
+}  // namespace mmq
