@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--workload", default="qproj")
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one 1 GiB device copy (known bytes) so that "
+                         "profiler byte counters can be calibrated against it")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -177,6 +180,13 @@ def main():
                      "alg_bytes_per_step": mmq_alg_bytes,
                      "alg_gbs": round(mmq_alg_bytes / (mmq_ms * 1e-3) / 1e9, 1)},
     }
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = 2 * src.numel() * 4
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(mats, inputs)
     print(json.dumps(res), flush=True)

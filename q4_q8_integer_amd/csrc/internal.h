@@ -17,8 +17,13 @@ hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32
 hipError_t launch_mmq_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,
                            int32_t* dots, hipStream_t stream);
 
-// Two-term fold, float32 out[t][o].
+// Two-term fold, float32 out[t][o], int8 MFMA + three-operation epilogue.
 hipError_t launch_mmq_fp32(const uint8_t* w, int m, int k, const int8_t* q,
                            const uint32_t* ds, int n, float* out, hipStream_t stream);
+
+// Two-term fold, float32 out[t][o], binary16 MFMA on exact sc*q4 and q8
+// operands + float32 MFMA for the min term (the default).
+hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
+                               const uint32_t* ds, int n, float* out, hipStream_t stream);
 
 }  // namespace mmq

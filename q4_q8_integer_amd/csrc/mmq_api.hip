@@ -4,6 +4,7 @@
 // the current device checked (once per device: gfx950 or MMQ_ERR_DEVICE) and
 // the kernel enqueued on the caller's stream.  Nothing here allocates.
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/mmq.h"
@@ -55,6 +56,17 @@ int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, c
     return MMQ_OK;
 }
 
+// Kernel behind mmq_q4k_q8_fp32out: the binary16-MFMA kernel unless the
+// environment sets MMQ_FP32_KERNEL=i8 (the int8-MFMA kernel, kept for
+// comparison).  Both meet the same float32 accuracy bar.
+bool use_i8_fp32_kernel() {
+    static const bool i8 = [] {
+        const char* v = std::getenv("MMQ_FP32_KERNEL");
+        return v && std::strcmp(v, "i8") == 0;
+    }();
+    return i8;
+}
+
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return MMQ_OK;
     (void)hipGetLastError();
@@ -100,8 +112,9 @@ int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    return hip_status(mmq::launch_mmq_fp32(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds,
-                                           (int)n, out, stream));
+    const auto launch = use_i8_fp32_kernel() ? mmq::launch_mmq_fp32 : mmq::launch_mmq_fp32_f16;
+    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
+                             stream));
 }
 
 const char* mmq_status_string(int status) {

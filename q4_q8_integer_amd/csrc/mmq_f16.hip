@@ -1,0 +1,397 @@
+// mmq_f16.hip - q4_K x q8 quantized matmul, float32 result, on gfx950 f16 MFMA.
+//
+// Same method as mmq_i8.hip (the yusiwen.cn "minfer" r31 page, sections 1-2:
+// exact per-32 dot products, then the two-term rank-1 fold), re-associated so
+// that the per-chunk work left for the vector ALU is one FMA per output:
+//
+//   * A operand = sc*q4 as binary16.  sc*q4 <= 63*15 = 945 is an integer
+//     below 2048, so it is exact; the B operand q8 in [-127, 127] is exact as
+//     well.  Every partial sum of a chunk's 32 products is an integer below
+//     945*127*32 < 2^22, so the two chained v_mfma_f32_32x32x16_f16 of a chunk
+//     return P = sc*D exactly, in float32.
+//   * Per chunk:       acc_b += da[t,c] * P          (da is a per-lane scalar)
+//     Per super-block: out   += d[o] * acc_b         (8 chunks share d)
+//   * The min term  -(dmin*m)[o,c] * (da*ssum)[t,c]  is a rank-1 update per
+//     chunk; over the chunks it is a float32 GEMM of depth k/32, done on
+//     v_mfma_f32_32x32x2_f32 (two chunks per instruction) straight into out.
+//
+// The int8 alternative needs three VALU operations per output and chunk
+// (int multiply by sc, convert, FMA) against one here; the vector ALU, not the
+// matrix core, is what bounds this operation on gfx950.
+//
+// Tiling: workgroup 128 rows x 128 tokens; 4 consumer waves of 64x64 (2x2
+// tiles of 32x32) and 4 producer waves; k is staged 128 at a time (half a
+// super-block, 4 chunks) in two alternating LDS stages (~141 KB, one
+// workgroup per CU).  Producers convert each weight and each activation once
+// per workgroup into binary16 operand slots laid out
+// [chunk][k-half][lane-half][row or token][8 halves], so that the 32 lanes of
+// a half-wave read 32 consecutive 16-byte slots (conflict-free) and each
+// staging store is a run of consecutive slots.
+#include "internal.h"
+
+namespace mmq {
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128;
+constexpr int CT = 256;          // consumer threads (4 waves of 64x64)
+constexpr int PT = 256;          // producer threads (4 waves)
+constexpr int NT = CT + PT;
+constexpr int CS = 4;  // chunks per stage (128 k)
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
+__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 r = __builtin_elementwise_fma(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b),
+                                     __builtin_bit_cast(h2, c));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) + __builtin_bit_cast(h2, b));
+}
+
+// Two packed binary16 (1024 + nibble) from the nibbles at bit offsets
+// `shift` and `shift + 16` of x.
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x, int shift) {
+    return ((x >> shift) & 0x000F000Fu) | 0x64006400u;
+}
+
+// 4 qs bytes -> 4 packed pairs: chunk-lo halves [b0,b2],[b1,b3], chunk-hi the same.
+// sc2 = (sc, sc) and nb2 = (-1024 sc, -1024 sc) as packed binary16:
+// fma(1024 + n, sc, -1024 sc) = sc*n exactly (an integer <= 945).
+__device__ __forceinline__ void unpack_word(uint32_t x, uint32_t sclo, uint32_t nblo, uint32_t schi,
+                                            uint32_t nbhi, uint32_t& lo02, uint32_t& lo13,
+                                            uint32_t& hi02, uint32_t& hi13) {
+    lo02 = pk_fma_f16(nib_pair(x, 0), sclo, nblo);
+    lo13 = pk_fma_f16(nib_pair(x, 8), sclo, nblo);
+    hi02 = pk_fma_f16(nib_pair(x, 4), schi, nbhi);
+    hi13 = pk_fma_f16(nib_pair(x, 12), schi, nbhi);
+}
+
+// 4 int8 -> packed binary16 pairs [b0,b2], [b1,b3] (exact): byte ^ 0x80 =
+// q + 128, placed under exponent 0x64 gives 1152 + q, minus 1152.
+__device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13) {
+    const uint32_t z = y ^ 0x80808080u;
+    const uint32_t m1152 = 0xE480E480u;  // (-1152, -1152)
+    p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
+    p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
+}
+
+// 6-bit (sc, m) of sub-block j (0..7) from the twelve scale bytes held in
+// three dwords s03 = bytes 0-3, s47 = bytes 4-7, s811 = bytes 8-11 (GGUF
+// k-quant packing): j < 4 keeps the low 6 bits of bytes j and j+4; j >= 4
+// takes the nibbles of byte j+4 and the top 2 bits of bytes j-4 and j.
+// Register bit-field extracts only (a byte array here would live in scratch).
+__device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
+                                          int& sc, int& mn) {
+    const int sh = 8 * (j & 3);
+    const int by = (s03 >> sh) & 0xFF, bz = (s47 >> sh) & 0xFF, bw = (s811 >> sh) & 0xFF;
+    const bool hi = j >= 4;
+    sc = hi ? ((bw & 15) | ((by >> 6) << 4)) : (by & 63);
+    mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
+}
+
+__device__ __forceinline__ uint32_t f16x2_splat(float v) {
+    const unsigned short h = __builtin_bit_cast(unsigned short, (_Float16)v);
+    return (uint32_t)h | ((uint32_t)h << 16);
+}
+
+// One stage of operands (128 k = 4 chunks) in LDS.
+struct Stage {
+    uint4 A[CS][2][2][BM];   // sc*q4 binary16 operand slots [chunk][k-half][lane-half][row]
+    uint4 B[CS][2][2][BN];   // q8 binary16 operand slots [chunk][k-half][lane-half][token]
+    float D[BM];             // d of the stage's super-block
+    float CA[CS][BM];        // -dmin*m per (chunk, row)
+    float Da[CS][BN];        // da per (chunk, token)
+    float Dass[CS][BN];      // da*ssum per (chunk, token)
+};
+
+// Raw global data of one stage, as one producer thread loads it.
+struct Raw {
+    uint4 hdr[2], qs[2];     // two weight pieces: block header + 16 nibble bytes
+    uint4 y[4];              // four activation pieces of 16 q8 bytes
+    uint32_t word[2];        // two activation scale words
+};
+
+// Per-thread source pointers of a producer's pieces at stage 0; stage st adds
+// (st/2)*144 to the weight pointers (+64 more for the nibbles of the second
+// half of the super-block), 128*st bytes to the q8 pointers, 4*st words to
+// the scale-word pointers.
+struct Src {
+    const uint8_t* blk[2];   // start of the row's first q4_K block
+    int qoff[2];             // nibble offset inside a block for this piece
+    const int8_t* y[4];
+    const uint32_t* word[2];
+};
+
+__device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
+                                         const int8_t* __restrict__ q,
+                                         const uint32_t* __restrict__ ds, int pt, int row0,
+                                         int tok0, int M, int N, int K) {
+    const int S = K >> 8, C = K >> 5;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int i = pt + rr * PT;
+        const int row = (i & 15) | ((i >> 6) << 4);
+        const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
+        p.blk[rr] = w + (int64_t)min(row0 + row, M - 1) * S * kBlockBytes;
+        p.qoff[rr] = 16 + 32 * pl + 16 * gg;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int i = pt + rr * PT;
+        const int tok = (i & 15) | ((i >> 7) << 4);
+        const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
+        p.y[rr] = q + (int64_t)min(tok0 + tok, N - 1) * K + 32 * cl + 16 * gg;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int i = pt + rr * PT;
+        const int tok = i & (BN - 1), cl = i >> 7;
+        p.word[rr] = ds + (int64_t)min(tok0 + tok, N - 1) * C + cl;
+    }
+}
+
+__device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
+    const int boff = (st >> 1) * kBlockBytes, hoff = (st & 1) * 64;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        r.hdr[rr] = *reinterpret_cast<const uint4*>(p.blk[rr] + boff);
+        r.qs[rr] = *reinterpret_cast<const uint4*>(p.blk[rr] + boff + hoff + p.qoff[rr]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) r.y[rr] = *reinterpret_cast<const uint4*>(p.y[rr] + 128 * st);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) r.word[rr] = p.word[rr][4 * st];
+}
+
+__device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
+    const int hs = st & 1;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int i = pt + rr * PT;
+        const int row = (i & 15) | ((i >> 6) << 4);
+        const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
+        const uint4 hdr = r.hdr[rr], qs = r.qs[rr];
+        const int c0 = 2 * (2 * hs + pl);
+        int sclo, schi, mn;
+        scale_min(hdr.y, hdr.z, hdr.w, c0, sclo, mn);
+        scale_min(hdr.y, hdr.z, hdr.w, c0 + 1, schi, mn);
+        const uint32_t sl2 = f16x2_splat((float)sclo), nl2 = f16x2_splat(-1024.0f * sclo);
+        const uint32_t sh2 = f16x2_splat((float)schi), nh2 = f16x2_splat(-1024.0f * schi);
+        uint32_t lo[8], hi[8];
+        const uint32_t xw[4] = {qs.x, qs.y, qs.z, qs.w};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+            unpack_word(xw[k4], sl2, nl2, sh2, nh2, lo[2 * k4], lo[2 * k4 + 1], hi[2 * k4],
+                        hi[2 * k4 + 1]);
+        sg.A[2 * pl][0][gg][row] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        sg.A[2 * pl][1][gg][row] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        sg.A[2 * pl + 1][0][gg][row] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        sg.A[2 * pl + 1][1][gg][row] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        if (j == 0) {
+            const float d = half_bits_to_float(hdr.x);
+            const float dmin = half_bits_to_float(hdr.x >> 16);
+            sg.D[row] = d;
+#pragma unroll
+            for (int cl = 0; cl < CS; ++cl) {
+                int sc, m;
+                scale_min(hdr.y, hdr.z, hdr.w, 4 * hs + cl, sc, m);
+                sg.CA[cl][row] = -(dmin * (float)m);
+            }
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int i = pt + rr * PT;
+        const int tok = (i & 15) | ((i >> 7) << 4);
+        const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
+        const uint4 y = r.y[rr];
+        uint32_t p[8];
+        q8_word(y.x, p[0], p[1]);
+        q8_word(y.y, p[2], p[3]);
+        q8_word(y.z, p[4], p[5]);
+        q8_word(y.w, p[6], p[7]);
+        sg.B[cl][0][gg][tok] = make_uint4(p[0], p[1], p[2], p[3]);
+        sg.B[cl][1][gg][tok] = make_uint4(p[4], p[5], p[6], p[7]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int i = pt + rr * PT;
+        const int tok = i & (BN - 1), cl = i >> 7;
+        const float da = half_bits_to_float(r.word[rr]);
+        sg.Da[cl][tok] = da;
+        sg.Dass[cl][tok] = da * (float)(int16_t)(uint16_t)(r.word[rr] >> 16);  // exact
+    }
+}
+
+// Waves 0-3 consume (MFMA + fold), waves 4-7 produce (load, convert to
+// binary16 operand slots).  Two LDS stages alternate: while the consumers
+// work on stage s, the producers fill stage s+1 (their global loads run one
+// stage further ahead, in registers).  One workgroup barrier per stage.
+__global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
+                                                     const int8_t* __restrict__ q,
+                                                     const uint32_t* __restrict__ ds,
+                                                     int M, int N, int K, int tiles_m,
+                                                     float* __restrict__ out) {
+    __shared__ Stage stage[2];
+
+    const int tid = threadIdx.x;
+    const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
+    const int row0 = bm * BM, tok0 = bn * BN;
+    const int stages = K >> 7;
+
+    if (tid >= CT) {
+        // ------------------------------------------------------- producer
+        // Two raw register sets alternate, so the loads for stage s+1 stay in
+        // flight while stage s is converted (a register copy would force a
+        // wait on them).
+        const int pt = tid - CT;
+        Src src;
+        init_src(src, w, q, ds, pt, row0, tok0, M, N, K);
+        Raw ra, rb;
+        load_stage(ra, src, 0);
+        // k is a multiple of 256, so the stage count is even and the loop
+        // runs whole (even, odd) pairs.  Every load is unconditional (the
+        // last prefetch re-reads the final stage), which lets the compiler
+        // wait only for the older register set.
+        for (int it = 0; it < stages; it += 2) {
+            load_stage(rb, src, it + 1);
+            convert_stage(ra, stage[0], pt, it);
+            __syncthreads();
+            load_stage(ra, src, min(it + 2, stages - 1));
+            convert_stage(rb, stage[1], pt, it + 1);
+            __syncthreads();
+        }
+        __syncthreads();  // the consumers' last stage
+        return;
+    }
+
+    // ----------------------------------------------------------- consumer
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int g = lane >> 5, l32 = lane & 31;
+
+    v16f acc[2][2], accb[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                acc[a][b][v] = 0.0f;
+                accb[a][b][v] = 0.0f;
+            }
+
+    for (int it = 0; it <= stages; ++it) {
+        if (it >= 1) {
+            const int st = it - 1, hs = st & 1;
+            const Stage& sg = stage[st & 1];
+#pragma unroll
+            for (int cl = 0; cl < CS; ++cl) {
+                v8h b0[2], b1[2];
+                float da[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int t = wn * 64 + nt * 32 + l32;
+                    b0[nt] = __builtin_bit_cast(v8h, sg.B[cl][0][g][t]);
+                    b1[nt] = __builtin_bit_cast(v8h, sg.B[cl][1][g][t]);
+                    da[nt] = sg.Da[cl][t];
+                }
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int rr = wm * 64 + rt * 32 + l32;
+                    const v8h a0 = __builtin_bit_cast(v8h, sg.A[cl][0][g][rr]);
+                    const v8h a1 = __builtin_bit_cast(v8h, sg.A[cl][1][g][rr]);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        v16f p = {};
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0[nt], p, 0, 0, 0);
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1[nt], p, 0, 0, 0);
+                        if (hs == 0 && cl == 0)
+                            accb[rt][nt] = p * da[nt];
+                        else
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                accb[rt][nt][v] = fmaf(da[nt], p[v], accb[rt][nt][v]);
+                    }
+                }
+            }
+            // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA
+#pragma unroll
+            for (int cp = 0; cp < CS / 2; ++cp) {
+                float ca[2], cb[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 64 + rt * 32 + l32];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 64 + nt * 32 + l32];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
+            }
+            // end of a super-block: out += d * acc_b
+            if (hs == 1) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float4 d4 = *reinterpret_cast<const float4*>(&sg.D[wm * 64 + rt * 32 + 8 * jj + 4 * g]);
+                        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt)
+                                acc[rt][nt][4 * jj + i] = fmaf(dv[i], accb[rt][nt][4 * jj + i], acc[rt][nt][4 * jj + i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    const bool vec = (M & 3) == 0;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int tok = tok0 + wn * 64 + nt * 32 + l32;
+            if (tok >= N) continue;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int o = row0 + wm * 64 + rt * 32 + 8 * jj + 4 * g;
+                float* dst = out + (int64_t)tok * M + o;
+                if (vec && o + 3 < M) {
+                    *reinterpret_cast<float4*>(dst) =
+                        make_float4(acc[rt][nt][4 * jj], acc[rt][nt][4 * jj + 1],
+                                    acc[rt][nt][4 * jj + 2], acc[rt][nt][4 * jj + 3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (o + i < M) dst[i] = acc[rt][nt][4 * jj + i];
+                }
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                               int n, float* out, hipStream_t stream) {
+    int tiles_m = (m + BM - 1) / BM;
+    const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
+                    (void*)&tiles_m, (void*)&out};
+    return hipLaunchKernel((const void*)mmq_f16_kernel, dim3((unsigned)tiles), dim3(NT), args, 0,
+                           stream);
+}
+
+}  // namespace mmq
