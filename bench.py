@@ -64,6 +64,21 @@ def build_workload(name: str):
     raise SystemExit("unknown workload %r" % name)
 
 
+def measured_traffic(key: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record (profiles/traffic.txt), already scaled by the copy-probe factors;
+    None unless the record was taken on the kernel source as it is now."""
+    import hashlib
+    try:
+        rec = json.loads(open(os.path.join(ROOT, "profiles", "traffic.txt")).read())[key]
+        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sha256_16") != sha:
+        return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
+
+
 def cpu_baseline(mats, inputs, budget_s: float = 12.0):
     """Time the oracle (as it stands) on a bounded token sample of the same
     workload: quantize + float64 fold for every projection."""
@@ -175,7 +190,9 @@ def main():
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "mmq_q4k_q8_fp32out", "achieved": round(achieved, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                     "traffic": measured_traffic("mmq_q4k_q8_fp32out|" + args.workload,
+                                                 "q4_q8_integer_amd/csrc/mmq_f16.hip"),
                      "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
                      "alg_bytes_per_step": mmq_alg_bytes,
                      "alg_gbs": round(mmq_alg_bytes / (mmq_ms * 1e-3) / 1e9, 1)},

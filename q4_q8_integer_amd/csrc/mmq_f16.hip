@@ -40,6 +40,8 @@ constexpr int CT = 256;          // consumer threads (4 waves of 64x64)
 constexpr int PT = 256;          // producer threads (4 waves)
 constexpr int NT = CT + PT;
 constexpr int CS = 4;  // chunks per stage (128 k)
+// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx950.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
@@ -57,22 +59,28 @@ __device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) + __builtin_bit_cast(h2, b));
 }
 
-// Two packed binary16 (1024 + nibble) from the nibbles at bit offsets
-// `shift` and `shift + 16` of x.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t x, int shift) {
-    return ((x >> shift) & 0x000F000Fu) | 0x64006400u;
+// 4 qs bytes x = [b0 b1 b2 b3] -> binary16 pairs of sc*nibble, exactly:
+//   low nibbles (chunk 2p):   (x & 0x000F000F) | 0x64006400 = (1024 + n, 1024 + n')
+//                             fma(1024 + n, sc, -1024 sc) = sc*n
+//   high nibbles (2p+1):      (x & 0x00F000F0) | 0x64006400 = (1024 + 16n, ...)
+//                             fma(1024 + 16n, sc/16, -64 sc) = sc*n
+// and the same on x >> 8 for bytes b1, b3.  Pair order: [b0,b2], [b1,b3].
+// sc, sc/16, -1024 sc and -64 sc are exact binary16 for sc <= 63.
+// (x & mask) | bits in one VALU instruction (the compiler otherwise emits two).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
+    return r;
 }
 
-// 4 qs bytes -> 4 packed pairs: chunk-lo halves [b0,b2],[b1,b3], chunk-hi the same.
-// sc2 = (sc, sc) and nb2 = (-1024 sc, -1024 sc) as packed binary16:
-// fma(1024 + n, sc, -1024 sc) = sc*n exactly (an integer <= 945).
 __device__ __forceinline__ void unpack_word(uint32_t x, uint32_t sclo, uint32_t nblo, uint32_t schi,
                                             uint32_t nbhi, uint32_t& lo02, uint32_t& lo13,
                                             uint32_t& hi02, uint32_t& hi13) {
-    lo02 = pk_fma_f16(nib_pair(x, 0), sclo, nblo);
-    lo13 = pk_fma_f16(nib_pair(x, 8), sclo, nblo);
-    hi02 = pk_fma_f16(nib_pair(x, 4), schi, nbhi);
-    hi13 = pk_fma_f16(nib_pair(x, 12), schi, nbhi);
+    const uint32_t y = x >> 8;
+    lo02 = pk_fma_f16(and_or(x, 0x000F000Fu, 0x64006400u), sclo, nblo);
+    lo13 = pk_fma_f16(and_or(y, 0x000F000Fu, 0x64006400u), sclo, nblo);
+    hi02 = pk_fma_f16(and_or(x, 0x00F000F0u, 0x64006400u), schi, nbhi);
+    hi13 = pk_fma_f16(and_or(y, 0x00F000F0u, 0x64006400u), schi, nbhi);
 }
 
 // 4 int8 -> packed binary16 pairs [b0,b2], [b1,b3] (exact): byte ^ 0x80 =
@@ -120,15 +128,17 @@ struct Raw {
     uint32_t word[2];        // two activation scale words
 };
 
-// Per-thread source pointers of a producer's pieces at stage 0; stage st adds
-// (st/2)*144 to the weight pointers (+64 more for the nibbles of the second
-// half of the super-block), 128*st bytes to the q8 pointers, 4*st words to
-// the scale-word pointers.
+// Producer loads go through buffer resources: one resource per operand,
+// based at the workgroup's first row / token, with the per-lane byte offset
+// fixed for the whole k loop and the per-stage advance in the scalar offset
+// (no vector address arithmetic in the loop).  The resource's record count is
+// the extent the workgroup may read, so an out-of-range offset would read
+// zeros instead of faulting.
 struct Src {
-    const uint8_t* blk[2];   // start of the row's first q4_K block
-    int qoff[2];             // nibble offset inside a block for this piece
-    const int8_t* y[4];
-    const uint32_t* word[2];
+    __amdgpu_buffer_rsrc_t w, q, ds;
+    int wh[2], wq[2];        // weight piece offsets: block header, nibbles
+    int y[4];                // q8 piece offsets
+    int word[2];             // scale-word offsets
 };
 
 __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
@@ -136,40 +146,51 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                          const uint32_t* __restrict__ ds, int pt, int row0,
                                          int tok0, int M, int N, int K) {
     const int S = K >> 8, C = K >> 5;
+    const int rows = min(BM, M - row0), toks = min(BN, N - tok0);
+    const int row_bytes = S * kBlockBytes;
+    p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * row_bytes), 0,
+                                            rows * row_bytes, kBufferFlags);
+    p.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q + (int64_t)tok0 * K), 0,
+                                            toks * K, kBufferFlags);
+    p.ds = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ds + (int64_t)tok0 * C), 0,
+                                             toks * C * 4, kBufferFlags);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int i = pt + rr * PT;
         const int row = (i & 15) | ((i >> 6) << 4);
         const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
-        p.blk[rr] = w + (int64_t)min(row0 + row, M - 1) * S * kBlockBytes;
-        p.qoff[rr] = 16 + 32 * pl + 16 * gg;
+        p.wh[rr] = min(row, rows - 1) * row_bytes;
+        p.wq[rr] = p.wh[rr] + 16 + 32 * pl + 16 * gg;
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
-        p.y[rr] = q + (int64_t)min(tok0 + tok, N - 1) * K + 32 * cl + 16 * gg;
+        p.y[rr] = min(tok, toks - 1) * K + 32 * cl + 16 * gg;
     }
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int i = pt + rr * PT;
         const int tok = i & (BN - 1), cl = i >> 7;
-        p.word[rr] = ds + (int64_t)min(tok0 + tok, N - 1) * C + cl;
+        p.word[rr] = (min(tok, toks - 1) * C + cl) * 4;
     }
 }
 
 __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
-    const int boff = (st >> 1) * kBlockBytes, hoff = (st & 1) * 64;
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const int boff = (st >> 1) * kBlockBytes, qoff = boff + (st & 1) * 64;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-        r.hdr[rr] = *reinterpret_cast<const uint4*>(p.blk[rr] + boff);
-        r.qs[rr] = *reinterpret_cast<const uint4*>(p.blk[rr] + boff + hoff + p.qoff[rr]);
+        r.hdr[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wh[rr], boff, 0));
+        r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) r.y[rr] = *reinterpret_cast<const uint4*>(p.y[rr] + 128 * st);
+    for (int rr = 0; rr < 4; ++rr)
+        r.y[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y[rr], 128 * st, 0));
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) r.word[rr] = p.word[rr][4 * st];
+    for (int rr = 0; rr < 2; ++rr)
+        r.word[rr] = __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word[rr], 16 * st, 0);
 }
 
 __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
@@ -185,7 +206,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         scale_min(hdr.y, hdr.z, hdr.w, c0, sclo, mn);
         scale_min(hdr.y, hdr.z, hdr.w, c0 + 1, schi, mn);
         const uint32_t sl2 = f16x2_splat((float)sclo), nl2 = f16x2_splat(-1024.0f * sclo);
-        const uint32_t sh2 = f16x2_splat((float)schi), nh2 = f16x2_splat(-1024.0f * schi);
+        const uint32_t sh2 = f16x2_splat(0.0625f * schi), nh2 = f16x2_splat(-64.0f * schi);
         uint32_t lo[8], hi[8];
         const uint32_t xw[4] = {qs.x, qs.y, qs.z, qs.w};
 #pragma unroll
@@ -196,16 +217,16 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         sg.A[2 * pl][1][gg][row] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
         sg.A[2 * pl + 1][0][gg][row] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
         sg.A[2 * pl + 1][1][gg][row] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-        if (j == 0) {
+        // The four pieces of a row share its header: piece j writes the min
+        // scale of the stage's chunk j, and all four write d (same value).
+        // No branch here, so the loop body stays straight-line.
+        {
             const float d = half_bits_to_float(hdr.x);
             const float dmin = half_bits_to_float(hdr.x >> 16);
+            int sc, m;
+            scale_min(hdr.y, hdr.z, hdr.w, 4 * hs + j, sc, m);
             sg.D[row] = d;
-#pragma unroll
-            for (int cl = 0; cl < CS; ++cl) {
-                int sc, m;
-                scale_min(hdr.y, hdr.z, hdr.w, 4 * hs + cl, sc, m);
-                sg.CA[cl][row] = -(dmin * (float)m);
-            }
+            sg.CA[j][row] = -(dmin * (float)m);
         }
     }
 #pragma unroll
