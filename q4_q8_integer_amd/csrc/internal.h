@@ -26,4 +26,12 @@ hipError_t launch_mmq_fp32(const uint8_t* w, int m, int k, const int8_t* q,
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
                                const uint32_t* ds, int n, float* out, hipStream_t stream);
 
+// Two-term fold, float32 out[t][o], for n <= 64 tokens: weight-streaming
+// int8-MFMA kernel (8 waves per 16 rows, each over a slice of k).
+hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q,
+                                 const uint32_t* ds, int n, float* out, hipStream_t stream);
+
+// Largest token count the few-token kernel takes.
+constexpr int kSmallMaxN = 64;
+
 }  // namespace mmq

@@ -56,15 +56,22 @@ int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, c
     return MMQ_OK;
 }
 
-// Kernel behind mmq_q4k_q8_fp32out: the binary16-MFMA kernel unless the
-// environment sets MMQ_FP32_KERNEL=i8 (the int8-MFMA kernel, kept for
-// comparison).  Both meet the same float32 accuracy bar.
-bool use_i8_fp32_kernel() {
-    static const bool i8 = [] {
+// Kernel behind mmq_q4k_q8_fp32out: the few-token weight-streaming kernel for
+// n <= 64, the binary16-MFMA kernel above that.  The environment variable
+// MMQ_FP32_KERNEL=i8|f16|small forces one kernel (for comparisons and tests;
+// "small" only where n <= 64).  All meet the same float32 accuracy bar.
+enum class Fp32Kernel { Auto, I8, F16, Small };
+
+Fp32Kernel forced_fp32_kernel() {
+    static const Fp32Kernel k = [] {
         const char* v = std::getenv("MMQ_FP32_KERNEL");
-        return v && std::strcmp(v, "i8") == 0;
+        if (!v) return Fp32Kernel::Auto;
+        if (std::strcmp(v, "i8") == 0) return Fp32Kernel::I8;
+        if (std::strcmp(v, "f16") == 0) return Fp32Kernel::F16;
+        if (std::strcmp(v, "small") == 0) return Fp32Kernel::Small;
+        return Fp32Kernel::Auto;
     }();
-    return i8;
+    return k;
 }
 
 int hip_status(hipError_t e) {
@@ -112,7 +119,10 @@ int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    const auto launch = use_i8_fp32_kernel() ? mmq::launch_mmq_fp32 : mmq::launch_mmq_fp32_f16;
+    const Fp32Kernel f = forced_fp32_kernel();
+    auto launch = n <= mmq::kSmallMaxN ? mmq::launch_mmq_fp32_small : mmq::launch_mmq_fp32_f16;
+    if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
+    if (f == Fp32Kernel::F16) launch = mmq::launch_mmq_fp32_f16;
     return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
                              stream));
 }

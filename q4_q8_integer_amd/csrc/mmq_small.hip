@@ -1,0 +1,182 @@
+// mmq_small.hip - q4_K x q8 matmul for few tokens (n <= 64), float32 result.
+//
+// Same method as the other kernels (the yusiwen.cn "minfer" r31 page, sections
+// 1-2: exact per-32 integer dots, then the two-term rank-1 fold).  With few
+// tokens the weights (0.5625 B each) are read once and used by at most 64
+// tokens, so the kernel is built to stream W at HBM speed:
+//
+//   * One v_mfma_i32_16x16x32_i8 is one chunk (k = 32) of 16 tokens x 16
+//     weight rows.  Weights are the B operand: a lane's 8 bytes are the
+//     nibbles of 8 consecutive qs bytes, & 0x0F0F0F0F for chunk 2p and
+//     >> 4 for chunk 2p+1 (no conversion beyond that), and the lane's output
+//     column is its own weight row, so sc, d and dmin are per-lane scalars.
+//   * Tokens are the A operand (q8 bytes at the same k), read straight from
+//     L2; their scale words are decoded per super-block into a small
+//     wave-private LDS table (da and da*ssum per token and chunk).
+//   * Per chunk: acc_b += da[t] * float(sc * D)   (int multiply, convert, FMA)
+//     Per super-block: out += d * acc_b;  min term on v_mfma_f32_16x16x4_f32
+//     (4 chunks per instruction) with A = da*ssum, B = -dmin*m.
+//   * A workgroup is 8 waves on the same 16 rows, each wave one eighth of the
+//     super-blocks (so even 8192-row matrices give 512 workgroups).  The 8
+//     partial sums are added in LDS in a fixed order: results do not depend
+//     on timing, and nothing outside the output is written.
+//   * T token tiles of 16 (n <= 16*T) reuse each unpacked weight operand.
+#include "internal.h"
+
+namespace mmq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 8;
+constexpr int NT = 64 * WAVES;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
+// 6-bit (sc, m) of sub-block j from the scale bytes in three dwords (GGUF
+// k-quant packing; see mmq_f16.hip).
+__device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
+                                          int& sc, int& mn) {
+    const int sh = 8 * (j & 3);
+    const int by = (s03 >> sh) & 0xFF, bz = (s47 >> sh) & 0xFF, bw = (s811 >> sh) & 0xFF;
+    const bool hi = j >= 4;
+    sc = hi ? ((bw & 15) | ((by >> 6) << 4)) : (by & 63);
+    mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
+}
+
+template <int T>
+__global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict__ w,
+                                                       const int8_t* __restrict__ q,
+                                                       const uint32_t* __restrict__ ds,
+                                                       int M, int N, int K,
+                                                       float* __restrict__ out) {
+    // per wave: da and da*ssum of its current super-block, [chunk][token]
+    __shared__ float sDa[WAVES][8][16 * T];
+    __shared__ float sDass[WAVES][8][16 * T];
+    // partial sums of the 8 waves, reduced in a fixed order at the end
+    __shared__ v4f sRed[WAVES][T][64];
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r = lane & 15, kg = lane >> 4;
+    const int row0 = blockIdx.x * 16;
+    const int S = K >> 8, C = K >> 5;
+    const int sb0 = (int)((int64_t)S * wv / WAVES), sb1 = (int)((int64_t)S * (wv + 1) / WAVES);
+
+    const uint8_t* blk = w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
+    // A-operand rows: token 16*tt + r (clamped; padded tokens repeat the last
+    // real one and are never stored)
+    const int8_t* qrow[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) qrow[tt] = q + (int64_t)min(16 * tt + r, N - 1) * K + 8 * kg;
+
+    v4f acc[T], accb[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+        acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        accb[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    for (int sb = sb0; sb < sb1; ++sb) {
+        const uint8_t* b = blk + (int64_t)sb * kBlockBytes;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(b);
+        uint2 qs[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) qs[p] = *reinterpret_cast<const uint2*>(b + 16 + 32 * p + 8 * kg);
+        int64_t a[T][8];
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                a[tt][c] = *reinterpret_cast<const int64_t*>(qrow[tt] + sb * 256 + 32 * c);
+        // scale words of this super-block: lane handles (token 16tt + r, chunks kg and kg + 4)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            const int tok = min(16 * tt + r, N - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t word = ds[(int64_t)tok * C + sb * 8 + kg + 4 * h];
+                const float da = half_bits_to_float(word);
+                sDa[wv][kg + 4 * h][16 * tt + r] = da;
+                sDass[wv][kg + 4 * h][16 * tt + r] = da * (float)(int16_t)(uint16_t)(word >> 16);
+            }
+        }
+        const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
+        // the LDS table is wave-private: in-order LDS access within the wave
+        // makes the writes above visible to the reads below
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            int sc, mn;
+            scale_min(hdr.y, hdr.z, hdr.w, c, sc, mn);
+            const uint2 x = qs[c >> 1];
+            const int64_t bw = (c & 1) ? (int64_t)(((uint64_t)((x.y >> 4) & 0x0F0F0F0Fu) << 32) | ((x.x >> 4) & 0x0F0F0F0Fu))
+                                       : (int64_t)(((uint64_t)(x.y & 0x0F0F0F0Fu) << 32) | (x.x & 0x0F0F0F0Fu));
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt) {
+                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[tt][c], bw, v4i{0, 0, 0, 0}, 0, 0, 0);
+                const float4 da4 = *reinterpret_cast<const float4*>(&sDa[wv][c][16 * tt + 4 * kg]);
+                const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i], (float)(D[i] * sc), accb[tt][i]);
+            }
+        }
+        // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int sc, mn;
+            scale_min(hdr.y, hdr.z, hdr.w, 4 * j + kg, sc, mn);
+            const float bneg = -(dmin * (float)mn);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt)
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sDass[wv][4 * j + kg][16 * tt + r], bneg,
+                                                               acc[tt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][i] = fmaf(d, accb[tt][i], acc[tt][i]);
+            accb[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) sRed[wv][tt][lane] = acc[tt];
+    __syncthreads();
+    // 64*T output values of 4 floats; the 8 waves share them, each summing the
+    // 8 partials in wave order.
+    for (int e = threadIdx.x; e < 64 * T; e += NT) {
+        const int tt = e >> 6, l = e & 63;
+        v4f s = sRed[0][tt][l];
+#pragma unroll
+        for (int v = 1; v < WAVES; ++v) s += sRed[v][tt][l];
+        const int row = row0 + (l & 15);
+        if (row >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * tt + 4 * (l >> 4) + i;
+            if (tok < N) out[(int64_t)tok * M + row] = s[i];
+        }
+    }
+}
+
+template <int T>
+hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
+                    float* out, hipStream_t stream) {
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k, (void*)&out};
+    return hipLaunchKernel((const void*)mmq_small_kernel<T>, dim3((unsigned)((m + 15) / 16)), dim3(NT),
+                           args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                                 int n, float* out, hipStream_t stream) {
+    if (n <= 16) return launch_t<1>(w, m, k, q, ds, n, out, stream);
+    if (n <= 32) return launch_t<2>(w, m, k, q, ds, n, out, stream);
+    if (n <= 48) return launch_t<3>(w, m, k, q, ds, n, out, stream);
+    return launch_t<4>(w, m, k, q, ds, n, out, stream);
+}
+
+}  // namespace mmq

@@ -1,0 +1,53 @@
+"""Every float32 kernel meets the same bar on shapes outside its default
+range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
+binary16-MFMA kernel, default above 64 tokens, here also on few tokens) and
+small (the few-token kernel, default up to 64 tokens).  The switch is read
+once per process, so each runs in one child process."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = r"""
+import sys
+sys.path.insert(0, %(root)r)
+sys.path.insert(0, %(tests)r)
+import numpy as np
+import oracle
+from gpu_helpers import check_fp32, gpu_quantize, to_dev
+from q4_q8_integer_amd import binding, synth
+import torch
+for seed, (n, m, k) in enumerate(%(shapes)s):
+    f = synth.random_fields(500 + seed, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(500 + seed, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    q, ds = gpu_quantize(x)
+    got = binding.fp32(to_dev(w), m, k, q, ds)
+    torch.cuda.synchronize()
+    rq, rds = oracle.quantize(x)
+    rel, worst = check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "forced kernel")
+    print("case", n, m, k, "rel %%.2e" %% rel, flush=True)
+print("ok")
+"""
+
+
+SHAPES = {
+    "i8": [(64, 256, 512), (77, 200, 768), (130, 129, 512), (5, 131, 2304)],
+    "f16": [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304)],
+    "small": [(1, 1, 256), (16, 17, 2304), (17, 200, 768), (48, 129, 512), (64, 256, 11008)],
+}
+
+
+@pytest.mark.parametrize("kernel", sorted(SHAPES))
+def test_forced_fp32_kernel_matches_oracle(kernel):
+    env = dict(os.environ, MMQ_FP32_KERNEL=kernel)
+    code = CHILD % {"root": ROOT, "tests": os.path.join(ROOT, "tests"), "shapes": repr(SHAPES[kernel])}
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    print(r.stdout, r.stderr[-2000:])
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok")
