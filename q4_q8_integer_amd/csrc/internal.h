@@ -31,6 +31,12 @@ hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q,
                                  const uint32_t* ds, int n, float* out, hipStream_t stream);
 
+// Two-term fold, float32 out[t][o], for 1 <= n <= kGemvMaxN tokens: 4-way
+// int8 dot products on the vector ALU, no token padding.
+hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
+                                const uint32_t* ds, int n, float* out, hipStream_t stream);
+constexpr int kGemvMaxN = 8;
+
 // Largest token count the few-token kernel takes.
 constexpr int kSmallMaxN = 64;
 

@@ -1,7 +1,8 @@
 """Every float32 kernel meets the same bar on shapes outside its default
 range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
-binary16-MFMA kernel, default above 64 tokens, here also on few tokens) and
-small (the few-token kernel, default up to 64 tokens).  The switch is read
+binary16-MFMA kernel, default above 64 tokens, here also on few tokens),
+small (the few-token int8-MFMA kernel, default from 9 to 64 tokens, here also
+on fewer) and gemv (the vector-ALU dot4 kernel, default up to 8 tokens).  The switch is read
 once per process, so each runs in one child process."""
 import os
 import subprocess
@@ -39,7 +40,10 @@ print("ok")
 SHAPES = {
     "i8": [(64, 256, 512), (77, 200, 768), (130, 129, 512), (5, 131, 2304)],
     "f16": [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304)],
-    "small": [(1, 1, 256), (16, 17, 2304), (17, 200, 768), (48, 129, 512), (64, 256, 11008)],
+    "small": [(1, 1, 256), (7, 31, 1280), (16, 17, 2304), (17, 200, 768), (48, 129, 512),
+              (64, 256, 11008)],
+    "gemv": [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
+             (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
 }
 
 
