@@ -36,7 +36,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWaves = 4;   // waves per workgroup (split of the super-blocks)
-constexpr int kStepSb = 4;     // super-blocks per wave step
 
 __device__ __forceinline__ float half_lo(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
@@ -44,19 +43,73 @@ __device__ __forceinline__ float half_lo(uint32_t h) {
 
 __device__ __forceinline__ v4u ld16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
 
-// The two chunk dots of pair p in super-block J of the step, for one token:
-//   D0 = sum_i dot4(lo[i], token word i),  D1 = sum_i dot4(hi[i], word 8 + i)
-// where token words 4c..4c+3 sit in lane 4J + c of the DPP row (row_newbcast).
-// Inline asm hides the instructions from the compiler's hazard checks, so
-// the block carries its own: s_nop 1 before (a DPP read needs 2 wait states
-// after a VALU write of its source) and s_nop 2 after (a VALU other than
-// another dot reading a v_dot4 result needs 3).  The two chains interleave.
+// Chunk dots of pair p in super-block J of the step, as float32 (exact:
+// |D| < 2^16):  D0 = sum_i dot4(lo[i], token word i), D1 = sum_i dot4(hi[i],
+// token word 8 + i), where token words 4c..4c+3 sit in lane 4J + c of the DPP
+// row (row_newbcast).  Inline asm hides these instructions from the
+// compiler's hazard checks, so the blocks keep the rules themselves: a DPP
+// read needs 2 wait states after a VALU write of its source (s_nop 1 first),
+// and a VALU other than a dot that reads a v_dot4 result needs 3 (the chains
+// are interleaved and converted in the order they finish).
 template <int J>
-__device__ __forceinline__ void dot_pair_bcast(int& D0, int& D1, v4u t, const int* lo,
+__device__ __forceinline__ void dots_two_tokens(float& a0, float& a1, float& b0, float& b1, v4u ta,
+                                                v4u tb, const int* lo, const int* hi) {
+    int A0 = 0, A1 = 0, B0 = 0, B1 = 0;
+    asm(
+        "s_nop 1\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %12 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %20 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %8, %12 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %8, %20 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %5, %13 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %5, %21 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %9, %13 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %9, %21 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %6, %14 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %6, %22 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %10, %14 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %10, %22 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %7, %15 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %7, %23 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %11, %15 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %11, %23 row_newbcast:%c30 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %16 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %24 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %8, %16 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %8, %24 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %5, %17 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %5, %25 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %9, %17 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %9, %25 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %6, %18 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %6, %26 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %10, %18 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %10, %26 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %7, %19 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %7, %27 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %11, %19 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %11, %27 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
+        "v_cvt_f32_i32 %0, %0\n\t"
+        "v_cvt_f32_i32 %1, %1\n\t"
+        "v_cvt_f32_i32 %2, %2\n\t"
+        "v_cvt_f32_i32 %3, %3"
+        : "+v"(A0), "+v"(A1), "+v"(B0), "+v"(B1)
+        : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3]), "v"(tb[0]), "v"(tb[1]), "v"(tb[2]), "v"(tb[3]),
+          "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(lo[4]), "v"(lo[5]), "v"(lo[6]), "v"(lo[7]),
+          "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(hi[4]), "v"(hi[5]), "v"(hi[6]), "v"(hi[7]),
+          "n"(4 * J), "n"(4 * J + 1), "n"(4 * J + 2), "n"(4 * J + 3));
+    a0 = __builtin_bit_cast(float, A0);
+    a1 = __builtin_bit_cast(float, A1);
+    b0 = __builtin_bit_cast(float, B0);
+    b1 = __builtin_bit_cast(float, B1);
+}
+
+template <int J>
+__device__ __forceinline__ void dots_one_token(float& a0, float& a1, v4u ta, const int* lo,
                                                const int* hi) {
-    D0 = 0;
-    D1 = 0;
-    asm("s_nop 1\n\t"
+    int A0 = 0, A1 = 0;
+    asm(
+        "s_nop 1\n\t"
         "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:%c22 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %1, %2, %14 row_newbcast:%c24 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %0, %3, %7 row_newbcast:%c22 row_mask:0xf bank_mask:0xf\n\t"
@@ -73,22 +126,48 @@ __device__ __forceinline__ void dot_pair_bcast(int& D0, int& D1, v4u t, const in
         "v_dot4c_i32_i8_dpp %1, %4, %20 row_newbcast:%c25 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %0, %5, %13 row_newbcast:%c23 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %1, %5, %21 row_newbcast:%c25 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2"
-        : "+v"(D0), "+v"(D1)
-        : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]),
+        "s_nop 1\n\t"
+        "v_cvt_f32_i32 %0, %0\n\t"
+        "v_cvt_f32_i32 %1, %1"
+        : "+v"(A0), "+v"(A1)
+        : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3]),
           "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(lo[4]), "v"(lo[5]), "v"(lo[6]), "v"(lo[7]),
           "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(hi[4]), "v"(hi[5]), "v"(hi[6]), "v"(hi[7]),
           "n"(4 * J), "n"(4 * J + 1), "n"(4 * J + 2), "n"(4 * J + 3));
+    a0 = __builtin_bit_cast(float, A0);
+    a1 = __builtin_bit_cast(float, A1);
 }
 
-// acc + a * (b of lane L of the DPP row)
-template <int L>
-__device__ __forceinline__ float fma_bcast(float acc, float b, float a) {
+// acc += da(2p) * x0 + da(2p+1) * x1 + dass(2p) * m0 + dass(2p+1) * m1, the
+// scales taken from lanes 2J (chunk 2p) and 2J + 1 (chunk 2p+1) of the row.
+template <int J>
+__device__ __forceinline__ void fold_one_token(float& acc, float da, float dass, float x0, float x1,
+                                               float m0, float m1) {
     asm("s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:%c8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_newbcast:%c8 row_mask:0xf bank_mask:0xf"
         : "+v"(acc)
-        : "v"(b), "v"(a), "n"(L));
-    return acc;
+        : "v"(da), "v"(dass), "v"(x0), "v"(x1), "v"(m0), "v"(m1), "n"(2 * J), "n"(2 * J + 1));
+}
+
+template <int J>
+__device__ __forceinline__ void fold_two_tokens(float& acca, float& accb, float daa, float dassa,
+                                                float dab, float dassb, float x0a, float x1a,
+                                                float x0b, float x1b, float m0, float m1) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %8 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:%c13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %9 row_newbcast:%c13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %10 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %11 row_newbcast:%c13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:%c13 row_mask:0xf bank_mask:0xf"
+        : "+v"(acca), "+v"(accb)
+        : "v"(daa), "v"(dassa), "v"(dab), "v"(dassb), "v"(x0a), "v"(x1a), "v"(x0b), "v"(x1b),
+          "v"(m0), "v"(m1), "n"(2 * J), "n"(2 * J + 1));
 }
 
 // One super-block J of the step for every token.  A slot past the wave's
@@ -123,19 +202,69 @@ __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb,
         hi[4 + i] = (int)((qb[i] >> 4) & 0x0F0F0F0Fu);
     }
 #pragma unroll
-    for (int t = 0; t < N; ++t) {
-        int D0, D1;
-        dot_pair_bcast<J>(D0, D1, tq[t], lo, hi);
-        float a = acc[t];
-        a = fma_bcast<2 * J>(a, tda[t], dsc0 * (float)D0);
-        a = fma_bcast<2 * J + 1>(a, tda[t], dsc1 * (float)D1);
-        a = fma_bcast<2 * J>(a, tdass[t], dmm0);
-        a = fma_bcast<2 * J + 1>(a, tdass[t], dmm1);
-        acc[t] = a;
+    for (int t = 0; t + 1 < N; t += 2) {
+        float a0, a1, b0, b1;
+        dots_two_tokens<J>(a0, a1, b0, b1, tq[t], tq[t + 1], lo, hi);
+        fold_two_tokens<J>(acc[t], acc[t + 1], tda[t], tdass[t], tda[t + 1], tdass[t + 1], dsc0 * a0,
+                           dsc1 * a1, dsc0 * b0, dsc1 * b1, dmm0, dmm1);
+    }
+    if constexpr ((N & 1) != 0) {
+        float a0, a1;
+        dots_one_token<J>(a0, a1, tq[N - 1], lo, hi);
+        fold_one_token<J>(acc[N - 1], tda[N - 1], tdass[N - 1], dsc0 * a0, dsc1 * a1, dmm0, dmm1);
     }
 }
 
-template <int N>
+// Registers of one wave step: SW super-blocks of the lane's row (header and
+// its 32 qs bytes), the lane's q8 piece and scale word of every token.
+template <int N, int SW>
+struct Step {
+    v4u hdr[SW], qa[SW], qb[SW];
+    v4u tq[N];
+    uint32_t tw[N];
+};
+
+// Issue the loads of the step starting at super-block s.  Every load is
+// unconditional: slots past the wave's last super-block re-read that block
+// (and are computed with live = false).
+template <int N, int SW>
+__device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
+                                          const int8_t* __restrict__ q,
+                                          const uint32_t* __restrict__ ds, int K, int C, int s,
+                                          int last, int p, int r) {
+    // q8: lane (p, r) holds piece r&3 of pair p of super-block s + (r>>2)
+    // (the wave reads up to 4 super-blocks of a token as one KiB)
+    const int64_t qoff = (int64_t)min(s + (r >> 2), last) * 256 + 64 * p + 16 * (r & 3);
+#pragma unroll
+    for (int t = 0; t < N; ++t) st.tq[t] = ld16(q + (int64_t)t * K + qoff);
+    // scale word of chunk 2p + (r&1) of super-block s + ((r>>1)&3)
+    const int64_t woff = (int64_t)min(s + ((r >> 1) & 3), last) * 8 + 2 * p + (r & 1);
+#pragma unroll
+    for (int t = 0; t < N; ++t) st.tw[t] = ds[(int64_t)t * C + woff];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+        const uint8_t* b = wrow + (int64_t)min(s + j, last) * kBlockBytes;
+        st.hdr[j] = ld16(b);
+        st.qa[j] = ld16(b + 16 + 32 * p);
+        st.qb[j] = ld16(b + 32 + 32 * p);
+    }
+}
+
+template <int N, int SW>
+__device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int p, float* acc) {
+    float tda[N], tdass[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        tda[t] = half_lo(st.tw[t]);
+        tdass[t] = tda[t] * (float)(int16_t)(uint16_t)(st.tw[t] >> 16);
+    }
+    gemv_sb<N, 0>(st.hdr[0], st.qa[0], st.qb[0], p, ns > 0, st.tq, tda, tdass, acc);
+    if constexpr (SW > 1) gemv_sb<N, 1>(st.hdr[1], st.qa[1], st.qb[1], p, ns > 1, st.tq, tda, tdass, acc);
+    if constexpr (SW > 2) gemv_sb<N, 2>(st.hdr[2], st.qa[2], st.qb[2], p, ns > 2, st.tq, tda, tdass, acc);
+    if constexpr (SW > 3) gemv_sb<N, 3>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
+}
+
+template <int N, int SW>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
                                                                   const int8_t* __restrict__ q,
                                                                   const uint32_t* __restrict__ ds,
@@ -156,44 +285,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
 #pragma unroll
     for (int t = 0; t < N; ++t) acc[t] = 0.0f;
 
-    for (int s = sb0; s < sb1; s += kStepSb) {
-        const int ns = min(kStepSb, sb1 - s);  // wave-uniform
-
-        // Every load is issued unconditionally (slots past the wave's last
-        // super-block re-read that block and are not used), so that all of a
-        // step's loads are in flight before the first wait.
-        // q8: lane (p, r) holds piece r&3 of pair p of super-block s + (r>>2)
-        // (the wave reads the step's q8 bytes of a token as one KiB)
-        v4u tq[N];
-        const int64_t qoff = (int64_t)min(s + (r >> 2), sb1 - 1) * 256 + 64 * p + 16 * (r & 3);
-#pragma unroll
-        for (int t = 0; t < N; ++t) tq[t] = ld16(q + (int64_t)t * K + qoff);
-        // scale word of chunk 2p + (r&1) of super-block s + ((r>>1)&3)
-        uint32_t tw[N];
-        const int64_t woff = (int64_t)min(s + ((r >> 1) & 3), sb1 - 1) * 8 + 2 * p + (r & 1);
-#pragma unroll
-        for (int t = 0; t < N; ++t) tw[t] = ds[(int64_t)t * C + woff];
-        v4u hdr[kStepSb], qa[kStepSb], qb[kStepSb];
-#pragma unroll
-        for (int j = 0; j < kStepSb; ++j) {
-            const uint8_t* b = wrow + (int64_t)min(s + j, sb1 - 1) * kBlockBytes;
-            hdr[j] = ld16(b);
-            qa[j] = ld16(b + 16 + 32 * p);
-            qb[j] = ld16(b + 32 + 32 * p);
-        }
-        // keep every load of the step above the math (the scheduler would
-        // otherwise trade the overlap for registers)
+    // One step at a time: all of its loads are issued, then it is computed.
+    // (Prefetching the next step into a second register set measured
+    // slower: it halves the waves a CU holds, and a wave's own latency is not
+    // what limits the stream.)
+    const int last = sb1 - 1;
+    for (int s = sb0; s < sb1; s += SW) {
+        Step<N, SW> A;
+        load_step<N, SW>(A, wrow, q, ds, K, C, s, last, p, r);
         __builtin_amdgcn_sched_barrier(0);
-        float tda[N], tdass[N];
-#pragma unroll
-        for (int t = 0; t < N; ++t) {
-            tda[t] = half_lo(tw[t]);
-            tdass[t] = tda[t] * (float)(int16_t)(uint16_t)(tw[t] >> 16);
-        }
-        gemv_sb<N, 0>(hdr[0], qa[0], qb[0], p, true, tq, tda, tdass, acc);
-        gemv_sb<N, 1>(hdr[1], qa[1], qb[1], p, ns > 1, tq, tda, tdass, acc);
-        gemv_sb<N, 2>(hdr[2], qa[2], qb[2], p, ns > 2, tq, tda, tdass, acc);
-        gemv_sb<N, 3>(hdr[3], qa[3], qb[3], p, ns > 3, tq, tda, tdass, acc);
+        compute_step<N, SW>(A, sb1 - s, p, acc);
     }
 
     // the four chunk-pair lanes of a row (every lane ends with the same
@@ -218,13 +319,17 @@ hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint3
                     float* out, hipStream_t stream) {
     const int S = k / 256;
     const int rows = (m + 15) / 16;
-    // the super-blocks of a row are split over up to 4 waves, so that about
-    // 4096 waves (16 per CU) cover the matrix at once
-    int waves = 4096 / rows;
-    waves = waves < 1 ? 1 : waves > kMaxWaves ? kMaxWaves : waves;
+    // The super-blocks of a row are split over the waves of a workgroup.
+    // Measured on the 28672 x 8192 and 8192 x 28672 matrices: one token
+    // streams best with about 1024 waves in all (long runs per wave), two or
+    // more tokens, whose vector work per byte is larger, with 4 waves per row
+    // tile.
+    int waves = N == 1 ? 1024 / rows : 4;
+    waves = waves < 1 ? 1 : waves > 4 ? 4 : waves;
     waves = waves > S ? S : waves;
-    hipLaunchKernelGGL(mmq_gemv_kernel<N>, dim3(rows), dim3(64 * waves), 0, stream, w, q, ds, m, k,
-                       out);
+    constexpr int SW = 4;
+    hipLaunchKernelGGL((mmq_gemv_kernel<N, SW>), dim3(rows), dim3(64 * waves), 0, stream, w, q, ds,
+                       m, k, out);
     return hipGetLastError();
 }
 
