@@ -253,6 +253,87 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
     }
 }
 
+// One stage for one consumer wave (64 rows x 64 tokens as 2x2 tiles of 32x32).
+// HS is the stage's half of the super-block: HS = 0 starts acc_b (the first
+// chunk multiplies instead of accumulating), HS = 1 ends it with the d fold.
+// Per chunk all eight MFMAs are issued before any of the epilogue, so each
+// tile's FMAs find their MFMA results done instead of waiting on them.
+template <int HS>
+__device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, int g, int l32,
+                                              v16f (&acc)[2][2], v16f (&accb)[2][2]) {
+#pragma unroll
+    for (int cl = 0; cl < CS; ++cl) {
+        v8h a0[2], a1[2], b0[2], b1[2];
+        float da[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int t = wn * 64 + nt * 32 + l32;
+            b0[nt] = __builtin_bit_cast(v8h, sg.B[cl][0][g][t]);
+            b1[nt] = __builtin_bit_cast(v8h, sg.B[cl][1][g][t]);
+            da[nt] = sg.Da[cl][t];
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int rr = wm * 64 + rt * 32 + l32;
+            a0[rt] = __builtin_bit_cast(v8h, sg.A[cl][0][g][rr]);
+            a1[rt] = __builtin_bit_cast(v8h, sg.A[cl][1][g][rr]);
+        }
+        v16f pr[2][2];
+        const v16f zero = {};
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[rt], b0[nt], zero, 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[rt], b1[nt], pr[rt][nt], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                if (HS == 0 && cl == 0)
+                    accb[rt][nt] = pr[rt][nt] * da[nt];
+                else
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        accb[rt][nt][v] = fmaf(da[nt], pr[rt][nt][v], accb[rt][nt][v]);
+            }
+    }
+    // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA
+#pragma unroll
+    for (int cp = 0; cp < CS / 2; ++cp) {
+        float ca[2], cb[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 64 + rt * 32 + l32];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 64 + nt * 32 + l32];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
+    }
+    // end of a super-block: out += d * acc_b
+    if (HS == 1) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&sg.D[wm * 64 + rt * 32 + 8 * jj + 4 * g]);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        acc[rt][nt][4 * jj + i] = fmaf(dv[i], accb[rt][nt][4 * jj + i], acc[rt][nt][4 * jj + i]);
+            }
+        }
+    }
+}
+
 // Waves 0-3 consume (MFMA + fold), waves 4-7 produce (load, convert to
 // binary16 operand slots).  Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
@@ -306,76 +387,15 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                acc[a][b][v] = 0.0f;
-                accb[a][b][v] = 0.0f;
-            }
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-    for (int it = 0; it <= stages; ++it) {
-        if (it >= 1) {
-            const int st = it - 1, hs = st & 1;
-            const Stage& sg = stage[st & 1];
-#pragma unroll
-            for (int cl = 0; cl < CS; ++cl) {
-                v8h b0[2], b1[2];
-                float da[2];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int t = wn * 64 + nt * 32 + l32;
-                    b0[nt] = __builtin_bit_cast(v8h, sg.B[cl][0][g][t]);
-                    b1[nt] = __builtin_bit_cast(v8h, sg.B[cl][1][g][t]);
-                    da[nt] = sg.Da[cl][t];
-                }
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const int rr = wm * 64 + rt * 32 + l32;
-                    const v8h a0 = __builtin_bit_cast(v8h, sg.A[cl][0][g][rr]);
-                    const v8h a1 = __builtin_bit_cast(v8h, sg.A[cl][1][g][rr]);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        v16f p = {};
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0[nt], p, 0, 0, 0);
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1[nt], p, 0, 0, 0);
-                        if (hs == 0 && cl == 0)
-                            accb[rt][nt] = p * da[nt];
-                        else
-#pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                accb[rt][nt][v] = fmaf(da[nt], p[v], accb[rt][nt][v]);
-                    }
-                }
-            }
-            // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA
-#pragma unroll
-            for (int cp = 0; cp < CS / 2; ++cp) {
-                float ca[2], cb[2];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 64 + rt * 32 + l32];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 64 + nt * 32 + l32];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
-            }
-            // end of a super-block: out += d * acc_b
-            if (hs == 1) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float4 d4 = *reinterpret_cast<const float4*>(&sg.D[wm * 64 + rt * 32 + 8 * jj + 4 * g]);
-                        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt)
-                                acc[rt][nt][4 * jj + i] = fmaf(dv[i], accb[rt][nt][4 * jj + i], acc[rt][nt][4 * jj + i]);
-                    }
-                }
-            }
-        }
+    // Stages come in (first, second) half-super-block pairs: stage[0] holds
+    // even stages, stage[1] odd ones.  The barriers pair with the producers'.
+    __syncthreads();
+    for (int st = 0; st < stages; st += 2) {
+        consume_stage<0>(stage[0], wm, wn, g, l32, acc, accb);
+        __syncthreads();
+        consume_stage<1>(stage[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
     }
 
