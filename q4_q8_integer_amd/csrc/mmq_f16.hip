@@ -36,10 +36,14 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128;
-constexpr int CT = 256;          // consumer threads (4 waves of 64x64)
-constexpr int PT = 256;          // producer threads (4 waves)
+constexpr int CT = 512;          // consumer threads (8 waves of 64 rows x 32 tokens)
+constexpr int PT = 512;          // producer threads (8 waves)
 constexpr int NT = CT + PT;
+constexpr int WPC = 512 / PT;    // weight pieces per producer thread (128 rows x 4)
+constexpr int APC = 1024 / PT;   // q8 pieces per producer thread (128 tokens x 8)
+constexpr int SPC = 512 / PT;    // scale words per producer thread (128 tokens x 4)
 constexpr int CS = 4;  // chunks per stage (128 k)
+constexpr int NTW = 1;  // 32-token tiles per consumer wave
 // Word 3 of a raw (unformatted, stride 0) buffer resource on gfx950.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -123,9 +127,9 @@ struct Stage {
 
 // Raw global data of one stage, as one producer thread loads it.
 struct Raw {
-    uint4 hdr[2], qs[2];     // two weight pieces: block header + 16 nibble bytes
-    uint4 y[4];              // four activation pieces of 16 q8 bytes
-    uint32_t word[2];        // two activation scale words
+    uint4 hdr[WPC], qs[WPC]; // weight pieces: block header + 16 nibble bytes
+    uint4 y[APC];            // activation pieces of 16 q8 bytes
+    uint32_t word[SPC];      // activation scale words
 };
 
 // Producer loads go through buffer resources: one resource per operand,
@@ -136,9 +140,9 @@ struct Raw {
 // zeros instead of faulting.
 struct Src {
     __amdgpu_buffer_rsrc_t w, q, ds;
-    int wh[2], wq[2];        // weight piece offsets: block header, nibbles
-    int y[4];                // q8 piece offsets
-    int word[2];             // scale-word offsets
+    int wh[WPC], wq[WPC];    // weight piece offsets: block header, nibbles
+    int y[APC];              // q8 piece offsets
+    int word[SPC];           // scale-word offsets
 };
 
 __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
@@ -155,7 +159,7 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     p.ds = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ds + (int64_t)tok0 * C), 0,
                                              toks * C * 4, kBufferFlags);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < WPC; ++rr) {
         const int i = pt + rr * PT;
         const int row = (i & 15) | ((i >> 6) << 4);
         const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
@@ -163,14 +167,14 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
         p.wq[rr] = p.wh[rr] + 16 + 32 * pl + 16 * gg;
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int rr = 0; rr < APC; ++rr) {
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
         p.y[rr] = min(tok, toks - 1) * K + 32 * cl + 16 * gg;
     }
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < SPC; ++rr) {
         const int i = pt + rr * PT;
         const int tok = i & (BN - 1), cl = i >> 7;
         p.word[rr] = (min(tok, toks - 1) * C + cl) * 4;
@@ -181,22 +185,22 @@ __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     const int boff = (st >> 1) * kBlockBytes, qoff = boff + (st & 1) * 64;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < WPC; ++rr) {
         r.hdr[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wh[rr], boff, 0));
         r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
+    for (int rr = 0; rr < APC; ++rr)
         r.y[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y[rr], 128 * st, 0));
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
+    for (int rr = 0; rr < SPC; ++rr)
         r.word[rr] = __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word[rr], 16 * st, 0);
 }
 
 __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
     const int hs = st & 1;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < WPC; ++rr) {
         const int i = pt + rr * PT;
         const int row = (i & 15) | ((i >> 6) << 4);
         const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
@@ -230,7 +234,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         }
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int rr = 0; rr < APC; ++rr) {
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
@@ -244,7 +248,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         sg.B[cl][1][gg][tok] = make_uint4(p[4], p[5], p[6], p[7]);
     }
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < SPC; ++rr) {
         const int i = pt + rr * PT;
         const int tok = i & (BN - 1), cl = i >> 7;
         const float da = half_bits_to_float(r.word[rr]);
@@ -253,21 +257,21 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
     }
 }
 
-// One stage for one consumer wave (64 rows x 64 tokens as 2x2 tiles of 32x32).
+// One stage for one consumer wave (64 rows x 32*NTW tokens as 2 x NTW tiles of 32x32).
 // HS is the stage's half of the super-block: HS = 0 starts acc_b (the first
 // chunk multiplies instead of accumulating), HS = 1 ends it with the d fold.
 // Per chunk all eight MFMAs are issued before any of the epilogue, so each
 // tile's FMAs find their MFMA results done instead of waiting on them.
 template <int HS>
 __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, int g, int l32,
-                                              v16f (&acc)[2][2], v16f (&accb)[2][2]) {
+                                              v16f (&acc)[2][NTW], v16f (&accb)[2][NTW]) {
 #pragma unroll
     for (int cl = 0; cl < CS; ++cl) {
-        v8h a0[2], a1[2], b0[2], b1[2];
-        float da[2];
+        v8h a0[2], a1[2], b0[NTW], b1[NTW];
+        float da[NTW];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int t = wn * 64 + nt * 32 + l32;
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int t = wn * 32 * NTW + nt * 32 + l32;
             b0[nt] = __builtin_bit_cast(v8h, sg.B[cl][0][g][t]);
             b1[nt] = __builtin_bit_cast(v8h, sg.B[cl][1][g][t]);
             da[nt] = sg.Da[cl][t];
@@ -278,22 +282,22 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
             a0[rt] = __builtin_bit_cast(v8h, sg.A[cl][0][g][rr]);
             a1[rt] = __builtin_bit_cast(v8h, sg.A[cl][1][g][rr]);
         }
-        v16f pr[2][2];
+        v16f pr[2][NTW];
         const v16f zero = {};
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTW; ++nt)
                 pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[rt], b0[nt], zero, 0, 0, 0);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTW; ++nt)
                 pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[rt], b1[nt], pr[rt][nt], 0, 0, 0);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTW; ++nt) {
                 if (HS == 0 && cl == 0)
                     accb[rt][nt] = pr[rt][nt] * da[nt];
                 else
@@ -305,15 +309,15 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
     // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA
 #pragma unroll
     for (int cp = 0; cp < CS / 2; ++cp) {
-        float ca[2], cb[2];
+        float ca[2], cb[NTW];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 64 + rt * 32 + l32];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 64 + nt * 32 + l32];
+        for (int nt = 0; nt < NTW; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 32 * NTW + nt * 32 + l32];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTW; ++nt)
                 acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
     }
     // end of a super-block: out += d * acc_b
@@ -327,7 +331,7 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
+                    for (int nt = 0; nt < NTW; ++nt)
                         acc[rt][nt][4 * jj + i] = fmaf(dv[i], accb[rt][nt][4 * jj + i], acc[rt][nt][4 * jj + i]);
             }
         }
@@ -381,11 +385,11 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
     const int wm = wave & 1, wn = wave >> 1;
     const int g = lane >> 5, l32 = lane & 31;
 
-    v16f acc[2][2], accb[2][2];
+    v16f acc[2][NTW], accb[2][NTW];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NTW; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
@@ -403,8 +407,8 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int tok = tok0 + wn * 64 + nt * 32 + l32;
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int tok = tok0 + wn * 32 * NTW + nt * 32 + l32;
             if (tok >= N) continue;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
