@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--workload", default="qproj")
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--f16-out", action="store_true",
+                    help="time mmq_q4k_q8_f16out (binary16 output) instead of the float32 entry point")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (known bytes) so that "
                          "profiler byte counters can be calibrated against it")
@@ -141,15 +143,19 @@ def main():
         qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
                   torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
               for s, x in xs.items()}
-        outs = [torch.empty((xs[src].shape[0], m), dtype=torch.float32, device=dev)
+        odt = torch.float16 if args.f16_out else torch.float32
+        outs = [torch.empty((xs[src].shape[0], m), dtype=odt, device=dev)
                 for _, _, m, _, src in ws]
         sets.append((xs, ws, qs, outs))
     torch.cuda.synchronize()
 
     n_tok = max(x.shape[0] for x in inputs.values())
     mmq_ops = sum(2.0 * inputs[src].shape[0] * f.m * f.k for _, f, src in mats)
+    out_bytes = 2.0 if args.f16_out else 4.0
     mmq_alg_bytes = sum(0.5625 * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
-                        + 4.0 * inputs[src].shape[0] * f.m for _, f, src in mats)
+                        + out_bytes * inputs[src].shape[0] * f.m for _, f, src in mats)
+    mmq = binding.mmq_q4k_q8_f16out if args.f16_out else binding.mmq_q4k_q8_fp32out
+    mmq_name = "mmq_q4k_q8_f16out" if args.f16_out else "mmq_q4k_q8_fp32out"
 
     def step(i):
         xs, ws, qs, outs = sets[i % len(sets)]
@@ -158,7 +164,7 @@ def main():
             binding.q8_quantize_rows(x, x.shape[0], x.shape[1], q, ds)
         for (lbl, w, m, k, src), out in zip(ws, outs):
             q, ds = qs[src]
-            binding.mmq_q4k_q8_fp32out(w, m, k, q, ds, q.shape[0], out)
+            mmq(w, m, k, q, ds, q.shape[0], out)
 
     for i in range(args.warmup):
         step(i)
@@ -182,7 +188,7 @@ def main():
         xs, ws, qs, outs = sets[i % len(sets)]
         for (lbl, w, m, k, src), out in zip(ws, outs):
             q, ds = qs[src]
-            binding.mmq_q4k_q8_fp32out(w, m, k, q, ds, q.shape[0], out)
+            mmq(w, m, k, q, ds, q.shape[0], out)
     e1.record(stream)
     torch.cuda.synchronize()
     mmq_ms = e0.elapsed_time(e1) / rounds          # all projections of one step
@@ -199,8 +205,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved_tops, 2), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(achieved_tops / INT8_PEAK_TOPS, 4)}
     roof.update({
-        "kernel": "mmq_q4k_q8_fp32out",
-        "traffic": measured_traffic("mmq_q4k_q8_fp32out|" + args.workload),
+        "kernel": mmq_name,
+        "traffic": measured_traffic(mmq_name + "|" + args.workload),
         "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
         "launches_timed": rounds * len(mats),
         "alg_bytes_per_step": mmq_alg_bytes,
@@ -211,7 +217,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": dict(desc, step="q8_quantize_rows + mmq_q4k_q8_fp32out per projection",
+        "config": dict(desc, step="q8_quantize_rows + %s per projection" % mmq_name,
                        copies=len(sets)),
         "tok_per_s": round(n_tok / (ms_step * 1e-3), 1),
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),

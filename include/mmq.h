@@ -103,6 +103,23 @@ int mmq_q4k_q8(const void *w, int64_t m, int64_t k, const int8_t *q, const uint3
 int mmq_q4k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
                        const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
 
+/*
+ * mmq_q4k_q8_f16out - the same quantized matmul and fold as
+ * mmq_q4k_q8_fp32out, stored as IEEE binary16: out[t][o] is the float32
+ * result rounded to nearest-even (overflow to +-inf), halving the output
+ * bytes.  The pages only name a binary16 step after the output store (the
+ * r22 page's round index, "r23 - f16 wall decomposition"); a binary16 output
+ * is this library's reading of it.
+ *
+ *   w, q, ds : as for mmq_q4k_q8_fp32out.
+ *   out      : binary16 bit patterns [n][m] (out), token-major, 16-byte
+ *              aligned.  For the same inputs and binary, out[t][o] equals the
+ *              binary16 rounding of mmq_q4k_q8_fp32out's out[t][o] bit for bit.
+ * Errors and empty calls as for mmq_q4k_q8_fp32out.
+ */
+int mmq_q4k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
+                      const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);
 

@@ -14,7 +14,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
-EXPORTS = ("q8_quantize_rows", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_status_string")
+EXPORTS = ("q8_quantize_rows", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
+           "mmq_status_string")
 _lib = None
 
 
@@ -39,7 +40,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.mmq_q4k_q8.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.mmq_q4k_q8_fp32out.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
-    for fn in (lib.q8_quantize_rows, lib.mmq_q4k_q8, lib.mmq_q4k_q8_fp32out):
+    lib.mmq_q4k_q8_f16out.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+    for fn in (lib.q8_quantize_rows, lib.mmq_q4k_q8, lib.mmq_q4k_q8_fp32out, lib.mmq_q4k_q8_f16out):
         fn.restype = ctypes.c_int
     lib.mmq_status_string.argtypes = [ctypes.c_int]
     lib.mmq_status_string.restype = ctypes.c_char_p
@@ -87,6 +89,11 @@ def mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out):
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
+def mmq_q4k_q8_f16out(w, m, k, q, ds, n, out):
+    _check("mmq_q4k_q8_f16out", load_library().mmq_q4k_q8_f16out(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
+
+
 # --------------------------------------------------------- tensor helpers
 def quantize(x: torch.Tensor):
     """x float32 [n, k] -> (q int8 [n, k], ds int32 [n, k/32] holding the uint32 words)."""
@@ -119,4 +126,18 @@ def fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out
     else:
         _need(out, torch.float32, "out")
     mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out)
+    return out
+
+
+def fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """Two-term-fold output as binary16 [n, m] (the float32 result, rounded to nearest-even)."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    _need(ds, torch.int32, "ds")
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float16, device=q.device)
+    else:
+        _need(out, torch.float16, "out")
+    mmq_q4k_q8_f16out(w, m, k, q, ds, n, out)
     return out

@@ -17,24 +17,55 @@ hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32
 hipError_t launch_mmq_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,
                            int32_t* dots, hipStream_t stream);
 
-// Two-term fold, float32 out[t][o], int8 MFMA + three-operation epilogue.
+// Output element of the fold kernels: float32, or binary16 rounded to
+// nearest-even from the same float32 value (half_out).
+template <bool H>
+struct OutElem {
+    typedef float T;
+};
+template <>
+struct OutElem<true> {
+    typedef _Float16 T;
+};
+
+template <bool H>
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
+    reinterpret_cast<typename OutElem<H>::T*>(out)[i] = (typename OutElem<H>::T)v;
+}
+
+// Four consecutive outputs from index i (16-byte aligned for float32, 8 for binary16).
+template <bool H>
+__device__ __forceinline__ void store_out4(void* out, int64_t i, float a, float b, float c, float d) {
+    if (H) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(out) + i) =
+            h4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + i) = make_float4(a, b, c, d);
+    }
+}
+
+// Two-term fold, out[t][o] (float32 or binary16), int8 MFMA + three-operation epilogue.
 hipError_t launch_mmq_fp32(const uint8_t* w, int m, int k, const int8_t* q,
-                           const uint32_t* ds, int n, float* out, hipStream_t stream);
+                           const uint32_t* ds, int n, void* out, bool half_out, hipStream_t stream);
 
-// Two-term fold, float32 out[t][o], binary16 MFMA on exact sc*q4 and q8
-// operands + float32 MFMA for the min term (the default).
+// Two-term fold, out[t][o], binary16 MFMA on exact sc*q4 and q8 operands +
+// float32 MFMA for the min term (above 64 tokens).
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
-                               const uint32_t* ds, int n, float* out, hipStream_t stream);
+                               const uint32_t* ds, int n, void* out, bool half_out,
+                               hipStream_t stream);
 
-// Two-term fold, float32 out[t][o], for n <= 64 tokens: weight-streaming
-// int8-MFMA kernel (8 waves per 16 rows, each over a slice of k).
+// Two-term fold, out[t][o], for n <= 64 tokens: weight-streaming int8-MFMA
+// kernel (8 waves per 16 rows, each over a slice of k).
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q,
-                                 const uint32_t* ds, int n, float* out, hipStream_t stream);
+                                 const uint32_t* ds, int n, void* out, bool half_out,
+                                 hipStream_t stream);
 
-// Two-term fold, float32 out[t][o], for 1 <= n <= kGemvMaxN tokens: 4-way
-// int8 dot products on the vector ALU, no token padding.
+// Two-term fold, out[t][o], for 1 <= n <= kGemvMaxN tokens: 4-way int8 dot
+// products on the vector ALU, no token padding.
 hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
-                                const uint32_t* ds, int n, float* out, hipStream_t stream);
+                                const uint32_t* ds, int n, void* out, bool half_out,
+                                hipStream_t stream);
 constexpr int kGemvMaxN = 8;
 
 // Largest token count the few-token kernel takes.

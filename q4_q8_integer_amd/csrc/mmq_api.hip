@@ -82,6 +82,28 @@ int hip_status(hipError_t e) {
     return MMQ_ERR_HIP;
 }
 
+// The two fold entry points: same checks, same kernels, float32 or binary16
+// stores of the same float32 result.
+int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds, int64_t n,
+               void* out, bool half_out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(w, m, k, q, n, out, &empty);
+    if (rc != MMQ_OK || empty) return rc;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    const Fp32Kernel f = forced_fp32_kernel();
+    auto launch = n <= mmq::kGemvMaxN    ? mmq::launch_mmq_fp32_gemv
+                  : n <= mmq::kSmallMaxN ? mmq::launch_mmq_fp32_small
+                                         : mmq::launch_mmq_fp32_f16;
+    if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
+    if (f == Fp32Kernel::F16) launch = mmq::launch_mmq_fp32_f16;
+    if (f == Fp32Kernel::Small && n <= mmq::kSmallMaxN) launch = mmq::launch_mmq_fp32_small;
+    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
+                             half_out, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,22 +136,12 @@ int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
 
 int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
-    bool empty = false;
-    int rc = check_mmq(w, m, k, q, n, out, &empty);
-    if (rc != MMQ_OK || empty) return rc;
-    if (!ds) return MMQ_ERR_NULL;
-    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
-    rc = check_device();
-    if (rc != MMQ_OK) return rc;
-    const Fp32Kernel f = forced_fp32_kernel();
-    auto launch = n <= mmq::kGemvMaxN    ? mmq::launch_mmq_fp32_gemv
-                  : n <= mmq::kSmallMaxN ? mmq::launch_mmq_fp32_small
-                                         : mmq::launch_mmq_fp32_f16;
-    if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
-    if (f == Fp32Kernel::F16) launch = mmq::launch_mmq_fp32_f16;
-    if (f == Fp32Kernel::Small && n <= mmq::kSmallMaxN) launch = mmq::launch_mmq_fp32_small;
-    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
-                             stream));
+    return fold_entry(w, m, k, q, ds, n, out, false, stream);
+}
+
+int mmq_q4k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
+                      const uint32_t* ds, int64_t n, uint16_t* out, hipStream_t stream) {
+    return fold_entry(w, m, k, q, ds, n, out, true, stream);
 }
 
 const char* mmq_status_string(int status) {

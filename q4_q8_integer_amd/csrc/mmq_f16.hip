@@ -342,11 +342,12 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 // binary16 operand slots).  Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
+template <bool H>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
                                                      int M, int N, int K, int tiles_m,
-                                                     float* __restrict__ out) {
+                                                     void* __restrict__ out) {
     __shared__ Stage stage[2];
 
     const int tid = threadIdx.x;
@@ -413,15 +414,14 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int o = row0 + wm * 64 + rt * 32 + 8 * jj + 4 * g;
-                float* dst = out + (int64_t)tok * M + o;
+                const int64_t idx = (int64_t)tok * M + o;
                 if (vec && o + 3 < M) {
-                    *reinterpret_cast<float4*>(dst) =
-                        make_float4(acc[rt][nt][4 * jj], acc[rt][nt][4 * jj + 1],
-                                    acc[rt][nt][4 * jj + 2], acc[rt][nt][4 * jj + 3]);
+                    store_out4<H>(out, idx, acc[rt][nt][4 * jj], acc[rt][nt][4 * jj + 1],
+                                  acc[rt][nt][4 * jj + 2], acc[rt][nt][4 * jj + 3]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (o + i < M) dst[i] = acc[rt][nt][4 * jj + i];
+                        if (o + i < M) store_out<H>(out, idx + i, acc[rt][nt][4 * jj + i]);
                 }
             }
         }
@@ -430,13 +430,13 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 }  // namespace
 
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
-                               int n, float* out, hipStream_t stream) {
+                               int n, void* out, bool half_out, hipStream_t stream) {
     int tiles_m = (m + BM - 1) / BM;
     const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    return hipLaunchKernel((const void*)mmq_f16_kernel, dim3((unsigned)tiles), dim3(NT), args, 0,
-                           stream);
+    const void* f = half_out ? (const void*)mmq_f16_kernel<true> : (const void*)mmq_f16_kernel<false>;
+    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 
 }  // namespace mmq

@@ -264,12 +264,12 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int 
     if constexpr (SW > 3) gemv_sb<N, 3>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
 }
 
-template <int N, int SW>
+template <int N, int SW, bool H>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
                                                                   const int8_t* __restrict__ q,
                                                                   const uint32_t* __restrict__ ds,
                                                                   int M, int K,
-                                                                  float* __restrict__ out) {
+                                                                  void* __restrict__ out) {
     __shared__ float red[kMaxWaves][N][16];
 
     const int W = blockDim.x >> 6;
@@ -310,13 +310,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
         const int t = e >> 4, rr = e & 15;
         float sum = red[0][t][rr];
         for (int v = 1; v < W; ++v) sum += red[v][t][rr];
-        if (row0 + rr < M) out[(int64_t)t * M + row0 + rr] = sum;
+        if (row0 + rr < M) store_out<H>(out, (int64_t)t * M + row0 + rr, sum);
     }
 }
 
 template <int N>
 hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
-                    float* out, hipStream_t stream) {
+                    void* out, bool half_out, hipStream_t stream) {
     const int S = k / 256;
     const int rows = (m + 15) / 16;
     // The super-blocks of a row are split over the waves of a workgroup.
@@ -328,24 +328,29 @@ hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint3
     waves = waves < 1 ? 1 : waves > 4 ? 4 : waves;
     waves = waves > S ? S : waves;
     constexpr int SW = 4;
-    hipLaunchKernelGGL((mmq_gemv_kernel<N, SW>), dim3(rows), dim3(64 * waves), 0, stream, w, q, ds,
-                       m, k, out);
+    if (half_out)
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), 0, stream,
+                           w, q, ds, m, k, out);
+    else
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), 0, stream,
+                           w, q, ds, m, k, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
-                                const uint32_t* ds, int n, float* out, hipStream_t stream) {
+                                const uint32_t* ds, int n, void* out, bool half_out,
+                                hipStream_t stream) {
     switch (n) {
-        case 1: return launch_n<1>(w, m, k, q, ds, out, stream);
-        case 2: return launch_n<2>(w, m, k, q, ds, out, stream);
-        case 3: return launch_n<3>(w, m, k, q, ds, out, stream);
-        case 4: return launch_n<4>(w, m, k, q, ds, out, stream);
-        case 5: return launch_n<5>(w, m, k, q, ds, out, stream);
-        case 6: return launch_n<6>(w, m, k, q, ds, out, stream);
-        case 7: return launch_n<7>(w, m, k, q, ds, out, stream);
-        case 8: return launch_n<8>(w, m, k, q, ds, out, stream);
+        case 1: return launch_n<1>(w, m, k, q, ds, out, half_out, stream);
+        case 2: return launch_n<2>(w, m, k, q, ds, out, half_out, stream);
+        case 3: return launch_n<3>(w, m, k, q, ds, out, half_out, stream);
+        case 4: return launch_n<4>(w, m, k, q, ds, out, half_out, stream);
+        case 5: return launch_n<5>(w, m, k, q, ds, out, half_out, stream);
+        case 6: return launch_n<6>(w, m, k, q, ds, out, half_out, stream);
+        case 7: return launch_n<7>(w, m, k, q, ds, out, half_out, stream);
+        case 8: return launch_n<8>(w, m, k, q, ds, out, half_out, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -23,7 +23,8 @@
 //
 // Epilogues (template parameter):
 //   kDots  exact int32 dots[t][o][c] (parity / inspection entry point);
-//   kFp32  float32 out[t][o] with the two-term fold applied per chunk.
+//   kFp32  float32 out[t][o] with the two-term fold applied per chunk;
+//   kF16   the same, stored as binary16 (nearest-even from the float32 value).
 #include "internal.h"
 
 namespace mmq {
@@ -38,7 +39,7 @@ constexpr int NT = 256;            // threads per workgroup (4 waves)
 constexpr int W_STRIDE = 144;      // LDS bytes per weight row (one q4_K block)
 constexpr int X_STRIDE = 272;      // LDS bytes per token row (256 q8 + pad)
 
-enum { kDots = 0, kFp32 = 1 };
+enum { kDots = 0, kFp32 = 1, kF16 = 2 };
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
             const uint4 v = *reinterpret_cast<const uint4*>(
                 w + ((int64_t)row * S + sb) * kBlockBytes + p * 16);
             *reinterpret_cast<uint4*>(sW + r * W_STRIDE + p * 16) = v;
-            if (EPI == kFp32 && p == 0) {
+            if (EPI != kDots && p == 0) {
                 const float d = half_bits_to_float(v.x);
                 const float dmin = half_bits_to_float(v.x >> 16);
                 uint8_t s[12];
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
             const uint4 v = *reinterpret_cast<const uint4*>(q + (int64_t)tok * K + sb * 256 + p * 16);
             *reinterpret_cast<uint4*>(sX + t * X_STRIDE + p * 16) = v;
         }
-        if (EPI == kFp32) {
+        if (EPI != kDots) {
             for (int i = tid; i < BN * 8; i += NT) {
                 const int t = i >> 3, j = i & 7;
                 const int tok = min(tok0 + t, N - 1);
@@ -200,8 +201,8 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
         }
     }
 
-    if (EPI == kFp32) {
-        float* out = reinterpret_cast<float*>(outp);
+    if (EPI != kDots) {
+        constexpr bool H = EPI == kF16;
         const bool vec = (M & 3) == 0;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -212,15 +213,14 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int o = row0 + wm * 64 + mt * 32 + 8 * jj + 4 * g;
-                    float* dst = out + (int64_t)tok * M + o;
+                    const int64_t idx = (int64_t)tok * M + o;
                     if (vec && o + 3 < M) {
-                        *reinterpret_cast<float4*>(dst) =
-                            make_float4(acc[mt][nt][4 * jj], acc[mt][nt][4 * jj + 1],
-                                        acc[mt][nt][4 * jj + 2], acc[mt][nt][4 * jj + 3]);
+                        store_out4<H>(outp, idx, acc[mt][nt][4 * jj], acc[mt][nt][4 * jj + 1],
+                                      acc[mt][nt][4 * jj + 2], acc[mt][nt][4 * jj + 3]);
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (o + i < M) dst[i] = acc[mt][nt][4 * jj + i];
+                            if (o + i < M) store_out<H>(outp, idx + i, acc[mt][nt][4 * jj + i]);
                     }
                 }
             }
@@ -246,8 +246,9 @@ hipError_t launch_mmq_dots(const uint8_t* w, int m, int k, const int8_t* q, int 
 }
 
 hipError_t launch_mmq_fp32(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
-                           int n, float* out, hipStream_t stream) {
-    return launch<kFp32>(w, m, k, q, ds, n, out, stream);
+                           int n, void* out, bool half_out, hipStream_t stream) {
+    return half_out ? launch<kF16>(w, m, k, q, ds, n, out, stream)
+                    : launch<kFp32>(w, m, k, q, ds, n, out, stream);
 }
 
 }  // namespace mmq

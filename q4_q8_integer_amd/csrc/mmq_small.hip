@@ -47,12 +47,12 @@ __device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s
     mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
 }
 
-template <int T>
+template <int T, bool H>
 __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict__ w,
                                                        const int8_t* __restrict__ q,
                                                        const uint32_t* __restrict__ ds,
                                                        int M, int N, int K,
-                                                       float* __restrict__ out) {
+                                                       void* __restrict__ out) {
     // per wave: da and da*ssum of its current super-block, [chunk][token]
     __shared__ float sDa[WAVES][8][16 * T];
     __shared__ float sDass[WAVES][8][16 * T];
@@ -156,27 +156,27 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = 16 * tt + 4 * (l >> 4) + i;
-            if (tok < N) out[(int64_t)tok * M + row] = s[i];
+            if (tok < N) store_out<H>(out, (int64_t)tok * M + row, s[i]);
         }
     }
 }
 
 template <int T>
 hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
-                    float* out, hipStream_t stream) {
+                    void* out, bool half_out, hipStream_t stream) {
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k, (void*)&out};
-    return hipLaunchKernel((const void*)mmq_small_kernel<T>, dim3((unsigned)((m + 15) / 16)), dim3(NT),
-                           args, 0, stream);
+    const void* f = half_out ? (const void*)mmq_small_kernel<T, true> : (const void*)mmq_small_kernel<T, false>;
+    return hipLaunchKernel(f, dim3((unsigned)((m + 15) / 16)), dim3(NT), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
-                                 int n, float* out, hipStream_t stream) {
-    if (n <= 16) return launch_t<1>(w, m, k, q, ds, n, out, stream);
-    if (n <= 32) return launch_t<2>(w, m, k, q, ds, n, out, stream);
-    if (n <= 48) return launch_t<3>(w, m, k, q, ds, n, out, stream);
-    return launch_t<4>(w, m, k, q, ds, n, out, stream);
+                                 int n, void* out, bool half_out, hipStream_t stream) {
+    if (n <= 16) return launch_t<1>(w, m, k, q, ds, n, out, half_out, stream);
+    if (n <= 32) return launch_t<2>(w, m, k, q, ds, n, out, half_out, stream);
+    if (n <= 48) return launch_t<3>(w, m, k, q, ds, n, out, half_out, stream);
+    return launch_t<4>(w, m, k, q, ds, n, out, half_out, stream);
 }
 
 }  // namespace mmq

@@ -66,7 +66,7 @@ def test_quantize_validation(lib, args, want):
     assert lib.q8_quantize_rows(*args, None) == want
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4k_q8", "mmq_q4k_q8_fp32out"])
+@pytest.mark.parametrize("fn", ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out"])
 @pytest.mark.parametrize("args,want", [
     ((A, 8, 512, A, A, -3, A), SHAPE),
     ((A, -8, 512, A, A, 3, A), SHAPE),
@@ -88,9 +88,10 @@ def test_mmq_validation(lib, fn, args, want):
     assert getattr(lib, fn)(*args, None) == want
 
 
-def test_fp32out_needs_scales(lib):
-    assert lib.mmq_q4k_q8_fp32out(A, 8, 512, A, 0, 3, A, None) == NULL
-    assert lib.mmq_q4k_q8_fp32out(A, 8, 512, A, MIS, 3, A, None) == ALIGN
+@pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out"])
+def test_fold_needs_scales(lib, fn):
+    assert getattr(lib, fn)(A, 8, 512, A, 0, 3, A, None) == NULL
+    assert getattr(lib, fn)(A, 8, 512, A, MIS, 3, A, None) == ALIGN
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a HIP device")
@@ -99,6 +100,7 @@ def test_valid_arguments_without_device_report_device_error(lib):
     # fails here before anything could be launched on the fake pointers.
     assert lib.q8_quantize_rows(A, 4, 64, A, A, None) == DEVICE
     assert lib.mmq_q4k_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.mmq_q4k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4k_q8(A, 8, 512, A, 0, 3, A, None) == DEVICE
 
 

@@ -2,8 +2,9 @@
 range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
 binary16-MFMA kernel, default above 64 tokens, here also on few tokens),
 small (the few-token int8-MFMA kernel, default from 9 to 64 tokens, here also
-on fewer) and gemv (the vector-ALU dot4 kernel, default up to 8 tokens).  The switch is read
-once per process, so each runs in one child process."""
+on fewer) and gemv (the vector-ALU dot4 kernel, default up to 8 tokens).  Each forced kernel's
+binary16 output must equal its float32 output rounded to nearest-even, bit for
+bit.  The switch is read once per process, so each runs in one child process."""
 import os
 import subprocess
 import sys
@@ -28,8 +29,12 @@ for seed, (n, m, k) in enumerate(%(shapes)s):
     x = synth.random_activations(500 + seed, n, k, "outliers")
     w = synth.pack_q4k(f)
     q, ds = gpu_quantize(x)
-    got = binding.fp32(to_dev(w), m, k, q, ds)
+    wd = to_dev(w)
+    got = binding.fp32(wd, m, k, q, ds)
+    got16 = binding.fp16(wd, m, k, q, ds)
     torch.cuda.synchronize()
+    assert np.array_equal(got16.cpu().numpy().view(np.uint16),
+                          got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16out != rounded fp32out"
     rq, rds = oracle.quantize(x)
     rel, worst = check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "forced kernel")
     print("case", n, m, k, "rel %%.2e" %% rel, flush=True)
