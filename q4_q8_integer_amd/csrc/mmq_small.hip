@@ -56,21 +56,31 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
     // per wave: da and da*ssum of its current super-block, [chunk][token]
     __shared__ float sDa[WAVES][8][16 * T];
     __shared__ float sDass[WAVES][8][16 * T];
+    // per wave: one 16-token tile of the super-block's q8 bytes, rows padded
+    // to 272 B so that the 16 lanes reading one chunk slot of 16 rows hit
+    // distinct banks
+    __shared__ uint4 sTok[WAVES][16][17];
     // partial sums of the 8 waves, reduced in a fixed order at the end
     __shared__ v4f sRed[WAVES][T][64];
 
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15, kg = lane >> 4;
     const int row0 = blockIdx.x * 16;
     const int S = K >> 8, C = K >> 5;
     const int sb0 = (int)((int64_t)S * wv / WAVES), sb1 = (int)((int64_t)S * (wv + 1) / WAVES);
 
     const uint8_t* blk = w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
-    // A-operand rows: token 16*tt + r (clamped; padded tokens repeat the last
-    // real one and are never stored)
-    const int8_t* qrow[T];
+    // q8 staging loads: piece j of a tile is tokens 4j .. 4j+3, lane -> token
+    // 4j + (lane >> 4), bytes 16*(lane & 15) of the super-block (one
+    // contiguous 256-byte run per token).  Padded tokens repeat the last real
+    // one and are never stored.
+    const int8_t* qpiece[T][4];
 #pragma unroll
-    for (int tt = 0; tt < T; ++tt) qrow[tt] = q + (int64_t)min(16 * tt + r, N - 1) * K + 8 * kg;
+    for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qpiece[tt][j] = q + (int64_t)min(16 * tt + 4 * j + (lane >> 4), N - 1) * K + 16 * (lane & 15);
 
     v4f acc[T], accb[T];
 #pragma unroll
@@ -85,12 +95,11 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
         uint2 qs[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) qs[p] = *reinterpret_cast<const uint2*>(b + 16 + 32 * p + 8 * kg);
-        int64_t a[T][8];
+        uint4 tq[T][4];
 #pragma unroll
         for (int tt = 0; tt < T; ++tt)
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                a[tt][c] = *reinterpret_cast<const int64_t*>(qrow[tt] + sb * 256 + 32 * c);
+            for (int j = 0; j < 4; ++j) tq[tt][j] = *reinterpret_cast<const uint4*>(qpiece[tt][j] + sb * 256);
         // scale words of this super-block: lane handles (token 16tt + r, chunks kg and kg + 4)
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
@@ -104,22 +113,33 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
             }
         }
         const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
-        // the LDS table is wave-private: in-order LDS access within the wave
-        // makes the writes above visible to the reads below
+        // The LDS areas are wave-private: LDS accesses of one wave complete in
+        // order, so each write below is seen by the reads after it, and a tile's
+        // reads finish before the next tile overwrites the area.
+        int64_t bw[8];
+        float scf[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             int sc, mn;
             scale_min(hdr.y, hdr.z, hdr.w, c, sc, mn);
+            scf[c] = (float)sc;
             const uint2 x = qs[c >> 1];
-            const int64_t bw = (c & 1) ? (int64_t)(((uint64_t)((x.y >> 4) & 0x0F0F0F0Fu) << 32) | ((x.x >> 4) & 0x0F0F0F0Fu))
-                                       : (int64_t)(((uint64_t)(x.y & 0x0F0F0F0Fu) << 32) | (x.x & 0x0F0F0F0Fu));
+            bw[c] = (c & 1) ? (int64_t)(((uint64_t)((x.y >> 4) & 0x0F0F0F0Fu) << 32) | ((x.x >> 4) & 0x0F0F0F0Fu))
+                            : (int64_t)(((uint64_t)(x.y & 0x0F0F0F0Fu) << 32) | (x.x & 0x0F0F0F0Fu));
+        }
 #pragma unroll
-            for (int tt = 0; tt < T; ++tt) {
-                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[tt][c], bw, v4i{0, 0, 0, 0}, 0, 0, 0);
+        for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sTok[wv][4 * j + (lane >> 4)][lane & 15] = tq[tt][j];
+            const uint8_t* arow = reinterpret_cast<const uint8_t*>(sTok[wv][r]) + 8 * kg;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int64_t a = *reinterpret_cast<const int64_t*>(arow + 32 * c);
+                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[c], v4i{0, 0, 0, 0}, 0, 0, 0);
                 const float4 da4 = *reinterpret_cast<const float4*>(&sDa[wv][c][16 * tt + 4 * kg]);
                 const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i], (float)(D[i] * sc), accb[tt][i]);
+                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i] * scf[c], (float)D[i], accb[tt][i]);
             }
         }
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
