@@ -56,12 +56,13 @@ int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, c
     return MMQ_OK;
 }
 
-// Kernel behind mmq_q4k_q8_fp32out: the vector-ALU dot4 kernel for n <= 8,
-// the few-token int8-MFMA kernel for n <= 64, the binary16-MFMA kernel above
-// that.  The environment variable MMQ_FP32_KERNEL=i8|f16|small|gemv forces
-// one kernel (for comparisons and tests; "small" only where n <= 64, "gemv"
-// only where n <= 8).  All meet the same float32 accuracy bar.
-enum class Fp32Kernel { Auto, I8, F16, Small, Gemv };
+// Kernel behind the fold entry points, by token count: the vector-ALU dot4
+// kernel for n <= 8, the chunk-pair int8-MFMA kernel for n <= 16, the
+// few-token int8-MFMA kernel for n <= 64, the binary16-MFMA kernel above.
+// The environment variable MMQ_FP32_KERNEL=i8|f16|small|gemv|pair forces one
+// kernel (for comparisons and tests; "small" only where n <= 64, "pair" only
+// where n <= 16, "gemv" only where n <= 8).  All meet the same accuracy bar.
+enum class Fp32Kernel { Auto, I8, F16, Small, Gemv, Pair };
 
 Fp32Kernel forced_fp32_kernel() {
     static const Fp32Kernel k = [] {
@@ -71,6 +72,7 @@ Fp32Kernel forced_fp32_kernel() {
         if (std::strcmp(v, "f16") == 0) return Fp32Kernel::F16;
         if (std::strcmp(v, "small") == 0) return Fp32Kernel::Small;
         if (std::strcmp(v, "gemv") == 0) return Fp32Kernel::Gemv;
+        if (std::strcmp(v, "pair") == 0) return Fp32Kernel::Pair;
         return Fp32Kernel::Auto;
     }();
     return k;
@@ -95,11 +97,14 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
     if (rc != MMQ_OK) return rc;
     const Fp32Kernel f = forced_fp32_kernel();
     auto launch = n <= mmq::kGemvMaxN    ? mmq::launch_mmq_fp32_gemv
+                  : n <= mmq::kPairMaxN  ? mmq::launch_mmq_fp32_pair
                   : n <= mmq::kSmallMaxN ? mmq::launch_mmq_fp32_small
                                          : mmq::launch_mmq_fp32_f16;
     if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
     if (f == Fp32Kernel::F16) launch = mmq::launch_mmq_fp32_f16;
     if (f == Fp32Kernel::Small && n <= mmq::kSmallMaxN) launch = mmq::launch_mmq_fp32_small;
+    if (f == Fp32Kernel::Gemv && n <= mmq::kGemvMaxN) launch = mmq::launch_mmq_fp32_gemv;
+    if (f == Fp32Kernel::Pair && n <= mmq::kPairMaxN) launch = mmq::launch_mmq_fp32_pair;
     return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
                              half_out, stream));
 }

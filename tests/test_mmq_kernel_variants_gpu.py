@@ -1,8 +1,10 @@
 """Every float32 kernel meets the same bar on shapes outside its default
 range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
 binary16-MFMA kernel, default above 64 tokens, here also on few tokens),
-small (the few-token int8-MFMA kernel, default from 9 to 64 tokens, here also
-on fewer) and gemv (the vector-ALU dot4 kernel, default up to 8 tokens).  Each forced kernel's
+small (the few-token int8-MFMA kernel, default from 17 to 64 tokens, here also
+on fewer), pair (the chunk-pair int8-MFMA kernel, default from 9 to 16 tokens,
+here also on fewer) and gemv (the vector-ALU dot4 kernel, default up to 8
+tokens).  Each forced kernel's
 binary16 output must equal its float32 output rounded to nearest-even, bit for
 bit.  The switch is read once per process, so each runs in one child process."""
 import os
@@ -49,6 +51,8 @@ SHAPES = {
               (64, 256, 11008)],
     "gemv": [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
              (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
+    "pair": [(1, 1, 256), (2, 17, 2304), (4, 33, 512), (5, 200, 768), (7, 129, 4352),
+             (8, 16, 256), (9, 131, 2304), (12, 64, 1280), (16, 256, 11008)],
 }
 
 
