@@ -1,5 +1,6 @@
 /*
- * oracle.c - plain, slow CPU reference for the q4_K x q8 quantized matmul.
+ * oracle.c - plain, slow CPU reference for the q4_K (and q6_K) x q8 quantized
+ * matmul.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file or the library built from it; only the tests, the smoke
@@ -28,6 +29,12 @@
  * super-block: d, dmin binary16; twelve bytes of packed 6-bit (sc, m); 128
  * bytes of nibbles, low nibbles of bytes 32p..32p+31 = weights 64p..64p+31,
  * high nibbles = weights 64p+32..64p+63.
+ *
+ * q6_K weights (the second k-quant format; named in the r31 page's closing
+ * notes, no layout printed): GGUF super-block of 210 bytes, signed 8-bit
+ * scale per 16 weights, 6-bit codes q with weight d*sc*(q - 32).  Group dots
+ * D[t][o][g] = sum_{i<16} (q - 32)*q8 (exact), output
+ * sum_g d*sc[g]*da[t][g/2]*D in float64 in group order (no min term).
  *
  * Readings taken where the pages are silent: rounding ties go away from zero
  * (C roundf); q is computed from the fp32 da, the rescale uses the binary16
@@ -241,6 +248,116 @@ int oracle_out_f64(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,
                     const double main_term = (d * sc[j]) * da * (double)D;
                     const double corr_term = (dmin * mn[j]) * da * (double)ssum;
                     acc += main_term - corr_term;
+                }
+                out[t * m + o] = acc;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------ q6_K decoding */
+/* q6_K (the second k-quant weight format; the pages name it, in the r31
+ * page's closing notes, but print no layout).  The GGUF k-quant super-block
+ * of 256 weights in 210 bytes: ql[128] low nibbles, qh[64] high bit pairs,
+ * sixteen signed 8-bit scales (one per 16 weights), binary16 d.  Weight
+ * e = 128h + 32g + l has the code
+ *     q = (nibble g/2 of ql[64h + 32(g%2) + l]) | (bits 2g..2g+1 of qh[32h + l]) << 4
+ * and the value d * sc[e/16] * (q - 32). */
+static void decode_q6k_block(const uint8_t *b, double *d, int sc[16], int q[256])
+{
+    const uint8_t *ql = b, *qh = b + 128;
+    *d = oracle_f16_to_double((uint16_t)(b[208] | (b[209] << 8)));
+    for (int j = 0; j < 16; j++)
+        sc[j] = (int8_t)b[192 + j];
+    for (int h = 0; h < 2; h++)
+        for (int g = 0; g < 4; g++)
+            for (int l = 0; l < 32; l++) {
+                const int lo = (ql[64 * h + 32 * (g & 1) + l] >> (4 * (g >> 1))) & 15;
+                const int hi = (qh[32 * h + l] >> (2 * g)) & 3;
+                q[128 * h + 32 * g + l] = lo | (hi << 4);
+            }
+}
+
+/* Unpack an m x k q6_K matrix into plain fields (for round-trip checks).
+ * q: [m][k] codes 0..63; sc: [m][k/16]; d: binary16 bits [m][k/256]. */
+int oracle_q6k_unpack(const uint8_t *w, int64_t m, int64_t k, uint8_t *q,
+                      int8_t *sc, uint16_t *d)
+{
+    if (m < 0 || k < 0 || k % 256)
+        return -1;
+    const int64_t S = k / 256;
+    for (int64_t o = 0; o < m; o++) {
+        for (int64_t b = 0; b < S; b++) {
+            const uint8_t *blk = w + (o * S + b) * 210;
+            double dd;
+            int s16[16], q256[256];
+            decode_q6k_block(blk, &dd, s16, q256);
+            d[o * S + b] = (uint16_t)(blk[208] | (blk[209] << 8));
+            for (int j = 0; j < 16; j++)
+                sc[o * (k / 16) + b * 16 + j] = (int8_t)s16[j];
+            for (int i = 0; i < 256; i++)
+                q[o * k + b * 256 + i] = (uint8_t)q256[i];
+        }
+    }
+    return 0;
+}
+
+/* Group dots: dots[t][o][g] = sum_{i<16} (q6[o][16g+i] - 32) * q8[t][16g+i]
+ * (int32, exact; one value per 16-weight scale group). */
+int oracle_q6k_dots(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,
+                    int64_t n, int32_t *dots)
+{
+    if (m < 0 || n < 0 || k < 0 || k % 256)
+        return -1;
+    const int64_t S = k / 256, G = k / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t o = 0; o < m; o++) {
+        for (int64_t b = 0; b < S; b++) {
+            double dd;
+            int sc[16], q6[256];
+            decode_q6k_block(w + (o * S + b) * 210, &dd, sc, q6);
+            for (int64_t t = 0; t < n; t++) {
+                for (int j = 0; j < 16; j++) {
+                    const int8_t *a = q8 + t * k + b * 256 + j * 16;
+                    int32_t acc = 0;
+                    for (int i = 0; i < 16; i++)
+                        acc += (q6[j * 16 + i] - 32) * a[i];
+                    dots[(t * m + o) * G + b * 16 + j] = acc;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* out[t][o] = sum_g d * sc[g] * da16[t][g/2] * D[t][o][g] in float64, in
+ * group order.  Each product is exact in float64 (at most 11 + 8 + 11 + 17
+ * significant bits), so only the additions round. */
+int oracle_q6k_out_f64(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,
+                       const uint32_t *ds, int64_t n, double *out)
+{
+    if (m < 0 || n < 0 || k < 0 || k % 256)
+        return -1;
+    const int64_t S = k / 256, C = k / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t o = 0; o < m; o++) {
+        for (int64_t t = 0; t < n; t++)
+            out[t * m + o] = 0.0;
+        for (int64_t b = 0; b < S; b++) {
+            double d;
+            int sc[16], q6[256];
+            decode_q6k_block(w + (o * S + b) * 210, &d, sc, q6);
+            for (int64_t t = 0; t < n; t++) {
+                double acc = out[t * m + o];
+                for (int j = 0; j < 16; j++) {
+                    const int8_t *a = q8 + t * k + b * 256 + j * 16;
+                    int32_t D = 0;
+                    for (int i = 0; i < 16; i++)
+                        D += (q6[j * 16 + i] - 32) * a[i];
+                    const uint32_t word = ds[t * C + b * 8 + j / 2];
+                    const double da = oracle_f16_to_double((uint16_t)(word & 0xffffu));
+                    acc += (d * sc[j]) * da * (double)D;
                 }
                 out[t * m + o] = acc;
             }

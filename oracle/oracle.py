@@ -33,6 +33,9 @@ def _declare(lib):
     lib.oracle_q4k_unpack.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]
     lib.oracle_blockdots.argtypes = [c_p, c_i64, c_i64, c_p, c_i64, c_p]
     lib.oracle_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
+    lib.oracle_q6k_unpack.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p]
+    lib.oracle_q6k_dots.argtypes = [c_p, c_i64, c_i64, c_p, c_i64, c_p]
+    lib.oracle_q6k_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
     lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_f16_to_double.restype = ctypes.c_double
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
@@ -40,7 +43,8 @@ def _declare(lib):
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
     for fn in (lib.oracle_q8_quantize, lib.oracle_q4k_unpack, lib.oracle_blockdots,
-               lib.oracle_out_f64):
+               lib.oracle_out_f64, lib.oracle_q6k_unpack, lib.oracle_q6k_dots,
+               lib.oracle_q6k_out_f64):
         fn.restype = ctypes.c_int
     return lib
 
@@ -124,6 +128,41 @@ def out_f64(w: np.ndarray, m: int, k: int, q: np.ndarray, ds: np.ndarray,
     n = q.shape[0]
     out = np.empty((n, m), dtype=np.float64)
     _check(lib.oracle_out_f64(_ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out)), "out_f64")
+    return out
+
+
+def q6k_unpack(w: np.ndarray, m: int, k: int, lib=None):
+    """q6_K bytes [m, (k/256)*210] -> dict of fields (q codes, sc int8, d as f16)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    q = np.empty((m, k), dtype=np.uint8)
+    sc = np.empty((m, k // 16), dtype=np.int8)
+    d = np.empty((m, k // 256), dtype=np.uint16)
+    _check(lib.oracle_q6k_unpack(_ptr(w), m, k, _ptr(q), _ptr(sc), _ptr(d)), "q6k_unpack")
+    return dict(q=q, sc=sc, d=d.view(np.float16))
+
+
+def q6k_dots(w: np.ndarray, m: int, k: int, q: np.ndarray, lib=None) -> np.ndarray:
+    """Exact q6_K group dots: int32 [n, m, k/16]."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    n = q.shape[0]
+    dots = np.empty((n, m, k // 16), dtype=np.int32)
+    _check(lib.oracle_q6k_dots(_ptr(w), m, k, _ptr(q), n, _ptr(dots)), "q6k_dots")
+    return dots
+
+
+def q6k_out_f64(w: np.ndarray, m: int, k: int, q: np.ndarray, ds: np.ndarray,
+                lib=None) -> np.ndarray:
+    """q6_K output in float64: [n, m]."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    ds = np.ascontiguousarray(ds, dtype=np.uint32)
+    n = q.shape[0]
+    out = np.empty((n, m), dtype=np.float64)
+    _check(lib.oracle_q6k_out_f64(_ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out)), "q6k_out_f64")
     return out
 
 

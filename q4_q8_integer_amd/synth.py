@@ -102,6 +102,76 @@ def pack_q4k(f: Q4KFields) -> np.ndarray:
     return out.reshape(m, s * BLOCK_BYTES)
 
 
+# ------------------------------------------------------------------ q6_K
+# q6_K super-block byte layout (256 weights in 210 bytes).  The pages only
+# name the format (the r31 page's closing notes speak of a "q6_K line" of
+# rounds); the layout is the GGUF k-quant one, written out here:
+#
+# * bytes 0-127    ql: low 4 bits of the quants
+# * bytes 128-191  qh: high 2 bits of the quants
+# * bytes 192-207  sc: sixteen signed 8-bit scales, one per 16 weights
+# * bytes 208-209  d:  binary16 super-block scale
+#
+# Weight e = 128h + 32g + l of the super-block (h = 0..1, g = 0..3, l = 0..31)
+# has the 6-bit code q = lo | hi << 4 with
+#   lo = nibble g // 2 (0 = low, 1 = high) of ql[64h + 32(g % 2) + l],
+#   hi = bits 2g, 2g+1 of qh[32h + l],
+# and the dequantized weight is d * sc[e // 16] * (q - 32).
+Q6K_BLOCK_BYTES = 210
+QK6 = 16            # weights per q6_K scale group
+
+
+@dataclass
+class Q6KFields:
+    """Unpacked q6_K fields of an ``m x k`` weight matrix (rows = outputs)."""
+
+    q: np.ndarray      # uint8 [m, k], 0..63 (the stored code; the weight uses q - 32)
+    sc: np.ndarray     # int8 [m, k/16]
+    d: np.ndarray      # float16 [m, k/256]
+
+    @property
+    def m(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.q.shape[1]
+
+
+def gen_q6k_fields(rng: np.random.Generator, m: int, k: int,
+                   sc_zero_frac: float = 0.0) -> Q6KFields:
+    """Draw q6_K fields in a fixed order: q ~ U{0..63}, sc ~ U{-128..127},
+    d = binary16(|N(0,1)| * 1e-3), then the sc=0 mask."""
+    if k % QK_K:
+        raise ValueError("k must be a multiple of 256")
+    g, s = k // QK6, k // QK_K
+    q = rng.integers(0, 64, size=(m, k), dtype=np.uint8)
+    sc = rng.integers(-128, 128, size=(m, g), dtype=np.int16).astype(np.int8)
+    d = (np.abs(rng.standard_normal((m, s))) * 1e-3).astype(np.float16)
+    if sc_zero_frac > 0.0:
+        mask = rng.random((m, g)) < sc_zero_frac
+        sc[mask] = 0
+    return Q6KFields(q=q, sc=sc, d=d)
+
+
+def pack_q6k(f: Q6KFields) -> np.ndarray:
+    """Lay the fields out as q6_K super-blocks: uint8 [m, (k/256)*210]."""
+    m, k = f.q.shape
+    s = k // QK_K
+    out = np.empty((m, s, Q6K_BLOCK_BYTES), dtype=np.uint8)
+    q = f.q.reshape(m, s, 2, 4, 32)          # [row, sb, half h, group g, l]
+    lo, hi = q & 15, q >> 4
+    ql = np.empty((m, s, 2, 2, 32), dtype=np.uint8)   # [row, sb, h, g % 2, l]
+    ql[:, :, :, 0, :] = lo[:, :, :, 0, :] | (lo[:, :, :, 2, :] << 4)
+    ql[:, :, :, 1, :] = lo[:, :, :, 1, :] | (lo[:, :, :, 3, :] << 4)
+    out[:, :, 0:128] = ql.reshape(m, s, 128)
+    qh = hi[:, :, :, 0, :] | (hi[:, :, :, 1, :] << 2) | (hi[:, :, :, 2, :] << 4) | (hi[:, :, :, 3, :] << 6)
+    out[:, :, 128:192] = qh.reshape(m, s, 64)
+    out[:, :, 192:208] = f.sc.reshape(m, s, 16).view(np.uint8)
+    out[:, :, 208:210] = f.d.astype("<f2").view(np.uint8).reshape(m, s, 2)
+    return out.reshape(m, s * Q6K_BLOCK_BYTES)
+
+
 def gen_normal(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
     """X ~ N(0,1), float32 [n, k]."""
     return rng.standard_normal((n, k), dtype=np.float32)
@@ -199,6 +269,32 @@ def weight_bound_activation(name: str, n: int) -> np.ndarray:
     mi = [nm for nm, _, _ in WEIGHT_BOUND_MATS].index(name)
     ni = WEIGHT_BOUND_TOKENS.index(n) if n in WEIGHT_BOUND_TOKENS else 4 + n
     return gen_normal(rng_for(4, 2 + 16 * mi + ni), n, k)
+
+
+# q6_K workloads (stream 5): the q-projection shape at prefill and the
+# weight-bound wide matrix, with q6_K weights in place of q4_K.
+Q6K_MATS = (("qproj", 4096, 4096), ("wide_in", 28672, 8192))
+
+
+def q6k_weights(name: str) -> Q6KFields:
+    """q6_K W[4096 x 4096] ("qproj") or W[28672 x 8192] ("wide_in", 10% of
+    scale groups with sc = 0)."""
+    for tid, (nm, m, k) in enumerate(Q6K_MATS):
+        if nm == name:
+            return gen_q6k_fields(rng_for(5, tid), m, k, sc_zero_frac=0.1 if nm == "wide_in" else 0.0)
+    raise ValueError(name)
+
+
+def q6k_activation(name: str, n: int) -> np.ndarray:
+    """X ~ N(0,1) [n x K] for the q6_K matrix ``name``."""
+    k = dict((nm, kk) for nm, _, kk in Q6K_MATS)[name]
+    mi = [nm for nm, _, _ in Q6K_MATS].index(name)
+    return gen_normal(rng_for(5, 2 + (1 << 20) * mi + n), n, k)
+
+
+def random_q6k_fields(seed: int, m: int, k: int, sc_zero_frac: float = 0.0) -> Q6KFields:
+    """q6_K fields for ad-hoc test shapes, from stream [102, seed]."""
+    return gen_q6k_fields(rng_for(102, seed), m, k, sc_zero_frac)
 
 
 def random_fields(seed: int, m: int, k: int, sc_zero_frac: float = 0.0) -> Q4KFields:

@@ -305,7 +305,150 @@ def pin_one_superblock(lib):
     assert oracle.out_f64(w, 1, 256, q, ds, lib=lib)[0, 0] == out
 
 
+# ------------------------------------------------------------------ q6_K
+def golden_q6k_block():
+    kv, _ = read_kv("q6k_block.txt")
+    sc = np.array([int(v) for v in kv["sc"].split()], dtype=np.int8)
+    e = np.arange(256)
+    h, g, l = e // 128, (e // 32) % 4, e % 32
+    q = ((3 * l + 7 * g + 11 * h) % 64).astype(np.uint8)
+    f = synth.Q6KFields(q=q[None, :], sc=sc[None, :],
+                        d=np.array([[int(kv["d_f16"], 16)]], dtype=np.uint16).view(np.float16))
+    expected = {int(k): int(v, 16) for k, v in kv.items() if k.isdigit()}
+    return f, expected
+
+
+def golden_q6k_one_superblock():
+    kv, _ = read_kv("q6k_one_superblock.txt")
+    f, _ = golden_q6k_block()
+    x = np.zeros((1, 256), dtype=np.float32)
+    for j in range(16):
+        x[0, 16 * j] = 127.0
+        x[0, 16 * j + 1] = -(j + 1)
+    dots = np.array([int(v) for v in kv["dots"].split()], dtype=np.int32)
+    return f, x, dots, float(kv["out"])
+
+
+def deq_q6k_weights(f: synth.Q6KFields) -> np.ndarray:
+    """d*sc*(q - 32) in float64 from the generator's unpacked fields."""
+    d = f.d.astype(np.float64).repeat(256, axis=1)
+    sc = f.sc.astype(np.float64).repeat(16, axis=1)
+    return d * sc * (f.q.astype(np.float64) - 32.0)
+
+
+def brute_q6k_dots(f: synth.Q6KFields, q8: np.ndarray) -> np.ndarray:
+    """int64 per-16 group dots of the offset codes: [n, m, k/16]."""
+    m, k = f.q.shape
+    a = f.q.astype(np.int64).reshape(m, k // 16, 16) - 32
+    b = q8.astype(np.int64).reshape(q8.shape[0], k // 16, 16)
+    return np.einsum("ogi,tgi->tog", a, b)
+
+
+def pin_q6k_golden_block(lib):
+    """Packing the hand-chosen fields gives the hand-derived bytes, and the
+    oracle's decoder gives the fields back."""
+    f, expected = golden_q6k_block()
+    w = synth.pack_q6k(f)
+    assert w.shape == (1, 210)
+    for off, byte in expected.items():
+        assert w[0, off] == byte, "packer byte %d: %02x != %02x" % (off, w[0, off], byte)
+    u = oracle.q6k_unpack(w, 1, 256, lib=lib)
+    assert np.array_equal(u["q"], f.q)
+    assert np.array_equal(u["sc"], f.sc)
+    assert np.array_equal(u["d"].view(np.uint16), f.d.view(np.uint16))
+
+
+def pin_q6k_roundtrip(lib):
+    """Unpack(pack(fields)) == fields on random matrices (odd super-block
+    counts included, so blocks start at every alignment)."""
+    for seed, (m, k) in enumerate([(3, 256), (5, 768), (2, 1024)]):
+        f = synth.random_q6k_fields(seed, m, k)
+        u = oracle.q6k_unpack(synth.pack_q6k(f), m, k, lib=lib)
+        assert np.array_equal(u["q"], f.q)
+        assert np.array_equal(u["sc"], f.sc)
+        assert np.array_equal(u["d"].view(np.uint16), f.d.view(np.uint16))
+
+
+def pin_q6k_dots_bruteforce(lib):
+    """Group dots = int64 dot products of (code - 32) with q8 from the
+    generator's unpacked codes."""
+    for seed, (n, m, k) in enumerate([(3, 4, 256), (5, 7, 512), (1, 1, 768), (9, 2, 256)]):
+        f = synth.random_q6k_fields(10 + seed, m, k)
+        x = synth.random_activations(60 + seed, n, k)
+        q, _ = oracle.quantize(x, lib=lib)
+        got = oracle.q6k_dots(synth.pack_q6k(f), m, k, q, lib=lib)
+        assert np.array_equal(got, brute_q6k_dots(f, q))
+
+
+def pin_q6k_dots_closed_forms(lib):
+    """Code 32 (weight 0) gives 0; code 63 with q8 = 127 gives 31*127*16 =
+    62992; code 0 with q8 = -127 gives 32*127*16 = 65024 (the largest
+    magnitude); code c gives (c - 32) times the q8 sum over the 16 weights."""
+    f = synth.random_q6k_fields(20, 3, 256)
+    x = synth.random_activations(21, 4, 256, "outliers")
+    q, _ = oracle.quantize(x, lib=lib)
+    f.q[:] = 32
+    assert not oracle.q6k_dots(synth.pack_q6k(f), 3, 256, q, lib=lib).any()
+    s16 = q.astype(np.int64).reshape(4, 16, 16).sum(axis=2)
+    for c in (0, 1, 31, 33, 63):
+        f.q[:] = c
+        got = oracle.q6k_dots(synth.pack_q6k(f), 3, 256, q, lib=lib)
+        assert np.array_equal(got, np.broadcast_to((c - 32) * s16[:, None, :], got.shape))
+    f.q[:] = 63
+    qp = np.full((2, 256), 127, dtype=np.int8)
+    assert (oracle.q6k_dots(synth.pack_q6k(f), 3, 256, qp, lib=lib) == 62992).all()
+    f.q[:] = 0
+    assert (oracle.q6k_dots(synth.pack_q6k(f), 3, 256, -qp, lib=lib) == 65024).all()
+
+
+def pin_q6k_out_bruteforce(lib):
+    """fp64 output = numpy float64 matmul of the dequantized operands."""
+    cases = [(1 + 3 * s, 1 + 5 * s, 256 * (1 + s % 3)) for s in range(10)]
+    for seed, (n, m, k) in enumerate(cases):
+        f = synth.random_q6k_fields(30 + seed, m, k, sc_zero_frac=0.1 * (seed % 2))
+        x = synth.random_activations(70 + seed, n, k, ("normal", "outliers", "silu")[seed % 3])
+        q, ds = oracle.quantize(x, lib=lib)
+        got = oracle.q6k_out_f64(synth.pack_q6k(f), m, k, q, ds, lib=lib)
+        ref = deq_acts(q, ds) @ deq_q6k_weights(f).T
+        scale = np.abs(ref).max()
+        assert np.abs(got - ref).max() <= 1e-12 * scale, "case %d" % seed
+
+
+def pin_q6k_out_special_cases(lib):
+    """A group with sc = 0 contributes exactly 0 (scrambling its codes leaves
+    the output bit-identical); negating every scale negates the output
+    exactly; d = 0 or every code = 32 gives exactly 0."""
+    n, m, k = 4, 5, 512
+    f = synth.random_q6k_fields(50, m, k)
+    f.sc[f.sc == -128] = -127
+    x = synth.random_activations(50, n, k)
+    q, ds = oracle.quantize(x, lib=lib)
+    f.sc[:, 5] = 0
+    base = oracle.q6k_out_f64(synth.pack_q6k(f), m, k, q, ds, lib=lib)
+    f.q[:, 80:96] = (f.q[:, 80:96] + 29) % 64
+    assert np.array_equal(base, oracle.q6k_out_f64(synth.pack_q6k(f), m, k, q, ds, lib=lib))
+    neg = synth.Q6KFields(q=f.q, sc=-f.sc, d=f.d)
+    assert np.array_equal(-base, oracle.q6k_out_f64(synth.pack_q6k(neg), m, k, q, ds, lib=lib))
+    zero_d = synth.Q6KFields(q=f.q, sc=f.sc, d=np.zeros_like(f.d))
+    assert not oracle.q6k_out_f64(synth.pack_q6k(zero_d), m, k, q, ds, lib=lib).any()
+    mid = synth.Q6KFields(q=np.full_like(f.q, 32), sc=f.sc, d=f.d)
+    assert not oracle.q6k_out_f64(synth.pack_q6k(mid), m, k, q, ds, lib=lib).any()
+
+
+def pin_q6k_one_superblock(lib):
+    """The hand-worked single q6_K super-block example."""
+    f, x, dots, out = golden_q6k_one_superblock()
+    q, ds = oracle.quantize(x, lib=lib)
+    assert np.array_equal(q, x.astype(np.int8))
+    w = synth.pack_q6k(f)
+    assert np.array_equal(oracle.q6k_dots(w, 1, 256, q, lib=lib)[0, 0], dots)
+    assert oracle.q6k_out_f64(w, 1, 256, q, ds, lib=lib)[0, 0] == out
+
+
 ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundtrip,
             pin_q8_golden, pin_q8_invariants, pin_q8_zero_block, pin_dots_bruteforce,
             pin_dots_closed_forms, pin_out_bruteforce, pin_out_special_cases,
-            pin_out_zero_scale_block, pin_one_superblock]
+            pin_out_zero_scale_block, pin_one_superblock,
+            pin_q6k_golden_block, pin_q6k_roundtrip, pin_q6k_dots_bruteforce,
+            pin_q6k_dots_closed_forms, pin_q6k_out_bruteforce, pin_q6k_out_special_cases,
+            pin_q6k_one_superblock]

@@ -14,7 +14,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = [
     ("drop_min_term", "acc += main_term - corr_term;", "acc += main_term;"),
     ("min_term_sign", "acc += main_term - corr_term;", "acc += main_term + corr_term;"),
-    ("sc_m_swapped", "(d * sc[j]) * da", "(d * mn[j]) * da"),
+    ("sc_m_swapped", "main_term = (d * sc[j]) * da", "main_term = (d * mn[j]) * da"),
     ("nibble_halves_swapped", "q[64 * p + i] = qs[32 * p + i] & 15;",
      "q[64 * p + i] = qs[32 * p + i] >> 4;"),
     ("subblock_index_off", "(dmin * mn[j]) * da", "(dmin * mn[(j + 1) & 7]) * da"),
@@ -32,6 +32,18 @@ MUTANTS = [
     ("dmin_is_d", "*dmin = oracle_f16_to_double(hm);", "*dmin = oracle_f16_to_double(hd);"),
     ("dot_skips_last", "for (int i = 0; i < 32; i++)\n                        D += q4[j * 32 + i] * a[i];",
      "for (int i = 0; i < 31; i++)\n                        D += q4[j * 32 + i] * a[i];"),
+    ("q6_offset_dropped", "D += (q6[j * 16 + i] - 32) * a[i];", "D += q6[j * 16 + i] * a[i];"),
+    ("q6_dots_offset_dropped", "acc += (q6[j * 16 + i] - 32) * a[i];", "acc += q6[j * 16 + i] * a[i];"),
+    ("q6_qh_shift_wrong", "(qh[32 * h + l] >> (2 * g)) & 3", "(qh[32 * h + l] >> g) & 3"),
+    ("q6_nibble_choice_wrong", ">> (4 * (g >> 1))) & 15", ">> (4 * (g & 1))) & 15"),
+    ("q6_ql_half_wrong", "ql[64 * h + 32 * (g & 1) + l]", "ql[64 * h + 32 * (g >> 1) + l]"),
+    ("q6_scale_unsigned", "sc[j] = (int8_t)b[192 + j];", "sc[j] = b[192 + j];"),
+    ("q6_da_chunk_wrong", "ds[t * C + b * 8 + j / 2]", "ds[t * C + b * 8 + (j & 7)]"),
+    ("q6_scale_per_32", "acc += (d * sc[j]) * da * (double)D;", "acc += (d * sc[j & 14]) * da * (double)D;"),
+    ("q6_d_from_block_start", "*d = oracle_f16_to_double((uint16_t)(b[208] | (b[209] << 8)));",
+     "*d = oracle_f16_to_double((uint16_t)(b[0] | (b[1] << 8)));"),
+    ("q6_group_skips_last", "for (int i = 0; i < 16; i++)\n                        acc += (q6",
+     "for (int i = 0; i < 15; i++)\n                        acc += (q6"),
 ]
 
 

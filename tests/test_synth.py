@@ -40,3 +40,23 @@ def test_layer_and_weight_bound_shapes():
     assert x.shape == (512, 11008)
     x = synth.weight_bound_activation("wide_out", 7)
     assert x.shape == (7, 28672)
+
+
+def test_q6k_fields_and_block_bytes():
+    f = synth.random_q6k_fields(7, 64, 768, sc_zero_frac=0.1)
+    assert f.q.min() == 0 and f.q.max() == 63
+    assert f.sc.dtype == np.int8 and f.sc.min() == -128 and f.sc.max() == 127
+    assert 0.09 < (f.sc == 0).mean() < 0.12
+    assert f.d.dtype == np.float16 and (f.d >= 0).all()
+    w = synth.pack_q6k(f)
+    assert w.shape == (64, 3 * 210) and w.dtype == np.uint8
+    # scales and d sit at fixed offsets of each 210-byte block
+    blk = w.reshape(64, 3, 210)
+    assert np.array_equal(blk[:, :, 192:208].view(np.int8).reshape(64, 48), f.sc)
+    assert np.array_equal(blk[:, :, 208:210].copy().view("<f2").reshape(64, 3), f.d)
+
+
+def test_q6k_workload_shapes():
+    x = synth.q6k_activation("wide_in", 1)
+    assert x.shape == (1, 8192) and x.dtype == np.float32
+    assert np.array_equal(x, synth.q6k_activation("wide_in", 1))
