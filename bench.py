@@ -54,6 +54,17 @@ def build_workload(name: str):
         return ({"workload": "7B layer projection set q,k,v,o,gate,up,down at N=%d "
                              "(4 quantizes + 7 MMQs; 1%% of inputs x20)" % n, "n": n},
                 inputs, mats)
+    if name == "q6k_qproj":
+        f = synth.q6k_weights("qproj")
+        return ({"workload": "q-proj prefill with q6_K weights: q6_K W[4096x4096] x q8 X[2630x4096] "
+                             "-> fp32 [2630x4096]", "m": 4096, "k": 4096, "n": 2630},
+                {"x": synth.q6k_activation("qproj", 2630)}, [("q", f, "x")])
+    if name.startswith("q6k_wide_in_n"):
+        n = int(name.rsplit("_n", 1)[1])
+        f = synth.q6k_weights("wide_in")
+        return ({"workload": "weight-bound q6_K W[%dx%d] at N=%d (10%% of scale groups sc=0)"
+                             % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
+                {"x": synth.q6k_activation("wide_in", n)}, [("wide_in", f, "x")])
     if name.startswith("wide_in") or name.startswith("wide_out"):
         wname, n = name.rsplit("_n", 1)
         n = int(n)
@@ -62,6 +73,15 @@ def build_workload(name: str):
                              % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
                 {"x": synth.weight_bound_activation(wname, n)}, [(wname, f, "x")])
     raise SystemExit("unknown workload %r" % name)
+
+
+def weight_format(f):
+    """'q6k' for q6_K fields, 'q4k' for q4_K: (packer, weight bytes per weight,
+    C-ABI name prefix, oracle output function name)."""
+    from q4_q8_integer_amd import synth
+    if isinstance(f, synth.Q6KFields):
+        return synth.pack_q6k, 210.0 / 256.0, "mmq_q6k_q8", "q6k_out_f64"
+    return synth.pack_q4k, 144.0 / 256.0, "mmq_q4k_q8", "out_f64"
 
 
 def measured_traffic(key: str):
@@ -86,22 +106,23 @@ def cpu_baseline(mats, inputs, budget_s: float = 12.0):
     import oracle
     from q4_q8_integer_amd import synth
 
-    packed = [(synth.pack_q4k(f), f.m, f.k, src) for _, f, src in mats]
+    packed = [(weight_format(f)[0](f), f.m, f.k, src, getattr(oracle, weight_format(f)[3]))
+              for _, f, src in mats]
     n_full = min(x.shape[0] for x in inputs.values())
 
     def run(nt):
         t0 = time.perf_counter()
         qs = {s: oracle.quantize(x[:nt]) for s, x in inputs.items()}
-        for w, m, k, src in packed:
+        for w, m, k, src, out_f64 in packed:
             q, ds = qs[src]
-            oracle.out_f64(w, m, k, q, ds)
+            out_f64(w, m, k, q, ds)
         return time.perf_counter() - t0
 
     probe = min(4, n_full)
     t = run(probe)
     nt = int(max(probe, min(n_full, probe * budget_s / max(t, 1e-6))))
     t = run(nt)
-    ops = sum(2.0 * nt * m * k for _, m, k, _ in packed)
+    ops = sum(2.0 * nt * m * k for _, m, k, _, _ in packed)
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.get_threads(),
             "kind": "oracle", "tok_per_s": nt / t,
             "sample": "first %d tokens of every input, all rows, quantize + float64 fold "
@@ -117,7 +138,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--f16-out", action="store_true",
-                    help="time mmq_q4k_q8_f16out (binary16 output) instead of the float32 entry point")
+                    help="time the binary16-output entry point (mmq_*_f16out) instead of the float32 one")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (known bytes) so that "
                          "profiler byte counters can be calibrated against it")
@@ -138,7 +159,7 @@ def main():
     sets = []
     for _ in range(max(1, args.copies)):
         xs = {s: torch.from_numpy(x).to(dev) for s, x in inputs.items()}
-        ws = [(lbl, torch.from_numpy(synth.pack_q4k(f)).to(dev), f.m, f.k, src)
+        ws = [(lbl, torch.from_numpy(weight_format(f)[0](f)).to(dev), f.m, f.k, src)
               for lbl, f, src in mats]
         qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
                   torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
@@ -152,17 +173,19 @@ def main():
     n_tok = max(x.shape[0] for x in inputs.values())
     mmq_ops = sum(2.0 * inputs[src].shape[0] * f.m * f.k for _, f, src in mats)
     out_bytes = 2.0 if args.f16_out else 4.0
-    mmq_alg_bytes = sum(0.5625 * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
+    mmq_alg_bytes = sum(weight_format(f)[1] * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
                         + out_bytes * inputs[src].shape[0] * f.m for _, f, src in mats)
-    mmq = binding.mmq_q4k_q8_f16out if args.f16_out else binding.mmq_q4k_q8_fp32out
-    mmq_name = "mmq_q4k_q8_f16out" if args.f16_out else "mmq_q4k_q8_fp32out"
+    suffix = "_f16out" if args.f16_out else "_fp32out"
+    names = sorted({weight_format(f)[2] + suffix for _, f, _ in mats})
+    mmq_name = "+".join(names)
+    calls = [getattr(binding, weight_format(f)[2] + suffix) for _, f, _ in mats]
 
     def step(i):
         xs, ws, qs, outs = sets[i % len(sets)]
         for s, x in xs.items():
             q, ds = qs[s]
             binding.q8_quantize_rows(x, x.shape[0], x.shape[1], q, ds)
-        for (lbl, w, m, k, src), out in zip(ws, outs):
+        for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
             q, ds = qs[src]
             mmq(w, m, k, q, ds, q.shape[0], out)
 
@@ -175,7 +198,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Duration of the dominant kernel (mmq_q4k_q8_fp32out) with HIP events on
+    # Duration of the dominant kernel (the MMQ entry point) with HIP events on
     # the stream it runs on: R rounds of every projection's MMQ, back to back,
     # behind a GPU spin long enough for the host to enqueue them all, so that
     # host launch latency is not counted.
@@ -186,7 +209,7 @@ def main():
     e0.record(stream)
     for i in range(rounds):
         xs, ws, qs, outs = sets[i % len(sets)]
-        for (lbl, w, m, k, src), out in zip(ws, outs):
+        for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
             q, ds = qs[src]
             mmq(w, m, k, q, ds, q.shape[0], out)
     e1.record(stream)

@@ -120,6 +120,56 @@ int mmq_q4k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
 int mmq_q4k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
                       const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
 
+/*
+ * q6_K weights: the second k-quant format, named in the r31 page's closing
+ * notes (its "q6_K line" of rounds); the pages print no layout, and the
+ * GGUF k-quant super-block is taken: 256 weights in 210 bytes, rows
+ * contiguous (row o's super-block b at byte (o*(k/256) + b)*210, so blocks
+ * are only 2-byte aligned).  Block: ql[128] at 0 (low nibbles), qh[64] at 128
+ * (2-bit high parts), sixteen int8 scales at 192 (one per 16 weights),
+ * binary16 d at 208.  Weight 128h + 32g + l (h < 2, g < 4, l < 32) has the
+ * code q = (nibble g/2 of ql[64h + 32(g%2) + l]) | (bits 2g..2g+1 of
+ * qh[32h + l]) << 4 and the value d*sc[(128h + 32g + l)/16]*(q - 32).  The
+ * same q8 activations as above.  There is no min term: with G = k/16 groups,
+ *
+ *   out[t][o] = sum_g d[o]*sc[o,g]*da[t,g/2]*D[t][o][g]
+ *   D[t][o][g] = sum_{i<16} (q[o][16g+i] - 32) * q8[t][16g+i]
+ *
+ * Limits, errors, alignment (of w itself) and empty calls as above, with
+ * m*(k/256)*210 below 2^40 and, for mmq_q6k_q8, n*m*(k/16) below 2^40.
+ */
+
+/*
+ * mmq_q6k_q8 - exact per-group integer dot products of q6_K weights.
+ *
+ *   w    : q6_K super-blocks of W [m][k] (m*(k/256)*210 bytes), k % 256 == 0.
+ *   q    : int8 [n][k] q8 activations.
+ *   ds   : accepted for a uniform signature, not read (may be NULL).
+ *   dots : int32 [n][m][k/16] (out), dots[t][o][g] = D[t][o][g], exact.
+ */
+int mmq_q6k_q8(const void *w, int64_t m, int64_t k, const int8_t *q, const uint32_t *ds,
+               int64_t n, int32_t *dots, hipStream_t stream);
+
+/*
+ * mmq_q6k_q8_fp32out - the q6_K quantized matmul, float32 result.
+ *
+ *   w   : q6_K super-blocks of W [m][k], k % 256 == 0.
+ *   q   : int8 [n][k];  ds : uint32 [n][k/32] (as written by q8_quantize_rows;
+ *         only the binary16 da is read).
+ *   out : float [n][m] (out), token-major.  The summation order is the
+ *         kernel's; the same accuracy bar as mmq_q4k_q8_fp32out.
+ */
+int mmq_q6k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
+                       const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
+/*
+ * mmq_q6k_q8_f16out - mmq_q6k_q8_fp32out's float32 result stored as binary16
+ * (nearest-even, bit for bit the rounding of the float32 result of the same
+ * inputs and binary), as mmq_q4k_q8_f16out is for q4_K.
+ */
+int mmq_q6k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
+                      const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);
 

@@ -15,7 +15,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-           "mmq_status_string")
+           "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_status_string")
+_MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
+              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out")
 _lib = None
 
 
@@ -38,10 +40,10 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.q8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
-    lib.mmq_q4k_q8.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
-    lib.mmq_q4k_q8_fp32out.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
-    lib.mmq_q4k_q8_f16out.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
-    for fn in (lib.q8_quantize_rows, lib.mmq_q4k_q8, lib.mmq_q4k_q8_fp32out, lib.mmq_q4k_q8_f16out):
+    lib.q8_quantize_rows.restype = ctypes.c_int
+    for name in _MMQ_CALLS:
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
         fn.restype = ctypes.c_int
     lib.mmq_status_string.argtypes = [ctypes.c_int]
     lib.mmq_status_string.restype = ctypes.c_char_p
@@ -94,6 +96,21 @@ def mmq_q4k_q8_f16out(w, m, k, q, ds, n, out):
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
+def mmq_q6k_q8(w, m, k, q, ds, n, dots):
+    _check("mmq_q6k_q8", load_library().mmq_q6k_q8(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
+
+
+def mmq_q6k_q8_fp32out(w, m, k, q, ds, n, out):
+    _check("mmq_q6k_q8_fp32out", load_library().mmq_q6k_q8_fp32out(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
+
+
+def mmq_q6k_q8_f16out(w, m, k, q, ds, n, out):
+    _check("mmq_q6k_q8_f16out", load_library().mmq_q6k_q8_f16out(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
+
+
 # --------------------------------------------------------- tensor helpers
 def quantize(x: torch.Tensor):
     """x float32 [n, k] -> (q int8 [n, k], ds int32 [n, k/32] holding the uint32 words)."""
@@ -140,4 +157,42 @@ def fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out
     else:
         _need(out, torch.float16, "out")
     mmq_q4k_q8_f16out(w, m, k, q, ds, n, out)
+    return out
+
+
+def q6k_dots(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds=None):
+    """Exact int32 q6_K group dots [n, m, k/16]."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    n = q.shape[0]
+    dots = torch.empty((n, m, k // 16), dtype=torch.int32, device=q.device)
+    mmq_q6k_q8(w, m, k, q, ds, n, dots)
+    return dots
+
+
+def q6k_fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """q6_K output float32 [n, m]."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    _need(ds, torch.int32, "ds")
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, torch.float32, "out")
+    mmq_q6k_q8_fp32out(w, m, k, q, ds, n, out)
+    return out
+
+
+def q6k_fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """q6_K output as binary16 [n, m] (the float32 result, rounded to nearest-even)."""
+    _need(w, torch.uint8, "w")
+    _need(q, torch.int8, "q")
+    _need(ds, torch.int32, "ds")
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float16, device=q.device)
+    else:
+        _need(out, torch.float16, "out")
+    mmq_q6k_q8_f16out(w, m, k, q, ds, n, out)
     return out

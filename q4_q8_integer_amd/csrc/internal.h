@@ -78,4 +78,18 @@ constexpr int kPairMaxN = 16;
 // Largest token count the few-token kernel takes.
 constexpr int kSmallMaxN = 64;
 
+// q6_K weights (210-byte super-blocks, one int8 scale per 16 weights).
+// Exact int32 group dots, dots[t][o][g] (g = k/16 groups).
+hipError_t launch_q6k_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,
+                           int32_t* dots, hipStream_t stream);
+
+// out[t][o] (float32 or binary16) for any n: int8 MFMA per scale group.
+hipError_t launch_q6k_i8(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                         int n, void* out, bool half_out, hipStream_t stream);
+
+// out[t][o] for 1 <= n <= kQ6kGemvMaxN: 4-way int8 dots on the vector ALU.
+hipError_t launch_q6k_gemv(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                           int n, void* out, bool half_out, hipStream_t stream);
+constexpr int kQ6kGemvMaxN = 8;
+
 }  // namespace mmq

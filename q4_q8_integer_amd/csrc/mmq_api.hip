@@ -9,6 +9,7 @@
 
 #include "../../include/mmq.h"
 #include "internal.h"
+#include "q6k_device.h"
 
 namespace {
 
@@ -42,12 +43,13 @@ int check_device() {
     return ok ? MMQ_OK : MMQ_ERR_DEVICE;
 }
 
-// Shared checks of the two MMQ calls (before any HIP call).
+// Shared checks of the MMQ calls (before any HIP call); block_bytes is the
+// weight format's super-block size (144 for q4_K, 210 for q6_K).
 int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, const void* out,
-              bool* empty) {
+              bool* empty, int64_t block_bytes = 144) {
     if (n < 0 || m < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
     if (n > kMaxDim || m > kMaxDim || k > kMaxK) return MMQ_ERR_OVERFLOW;
-    if (n * k >= kMaxElems || m * (k / 256) * 144 >= kMaxElems || n * m >= kMaxElems)
+    if (n * k >= kMaxElems || m * (k / 256) * block_bytes >= kMaxElems || n * m >= kMaxElems)
         return MMQ_ERR_OVERFLOW;
     *empty = (n == 0 || m == 0);
     if (*empty) return MMQ_OK;
@@ -109,6 +111,31 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
                              half_out, stream));
 }
 
+// q6_K kernel behind the fold entry points: the vector-ALU dot4 kernel for
+// n <= 8, the int8-MFMA tile kernel above.  MMQ_Q6K_KERNEL=i8 forces the
+// tile kernel (for comparisons and tests).
+bool q6k_forced_i8() {
+    static const bool f = [] {
+        const char* v = std::getenv("MMQ_Q6K_KERNEL");
+        return v && std::strcmp(v, "i8") == 0;
+    }();
+    return f;
+}
+
+int q6k_fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
+                   int64_t n, void* out, bool half_out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(w, m, k, q, n, out, &empty, mmq::kQ6kBlockBytes);
+    if (rc != MMQ_OK || empty) return rc;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    auto launch = n <= mmq::kQ6kGemvMaxN && !q6k_forced_i8() ? mmq::launch_q6k_gemv : mmq::launch_q6k_i8;
+    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
+                             half_out, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +174,30 @@ int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
 int mmq_q4k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
                       const uint32_t* ds, int64_t n, uint16_t* out, hipStream_t stream) {
     return fold_entry(w, m, k, q, ds, n, out, true, stream);
+}
+
+int mmq_q6k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
+               int64_t n, int32_t* dots, hipStream_t stream) {
+    (void)ds;  // not read: the group dots do not depend on the scales
+    bool empty = false;
+    int rc = check_mmq(w, m, k, q, n, dots, &empty, mmq::kQ6kBlockBytes);
+    if (rc != MMQ_OK || empty) return rc;
+    if (n * m >= kMaxElems / (k / 16)) return MMQ_ERR_OVERFLOW;
+    if (ds && !aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    return hip_status(mmq::launch_q6k_dots(static_cast<const uint8_t*>(w), (int)m, (int)k, q,
+                                           (int)n, dots, stream));
+}
+
+int mmq_q6k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
+                       const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    return q6k_fold_entry(w, m, k, q, ds, n, out, false, stream);
+}
+
+int mmq_q6k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
+                      const uint32_t* ds, int64_t n, uint16_t* out, hipStream_t stream) {
+    return q6k_fold_entry(w, m, k, q, ds, n, out, true, stream);
 }
 
 const char* mmq_status_string(int status) {

@@ -1,0 +1,229 @@
+// mmq_q6k_gemv.hip - q6_K x q8 matmul for very few tokens (1 <= n <= 8),
+// float32 result, on the vector ALU's 4-way int8 dot product.
+//
+// Method as in mmq_q6k_i8.hip (q6_K, the second k-quant weight format named
+// in the r31 page's closing notes of the yusiwen.cn "minfer" pages): per
+// 16-weight group an exact integer dot D = sum (q - 32) * q8, then
+// out[t][o] = sum_g d*sc[g] * da[t, g/2] * D.
+//
+//   * A wave owns 16 weight rows.  Lane 16p + r takes row r and quarter
+//     p = 2h + e of every super-block: the weights 128h + 32g + 16e + [0, 16)
+//     for g = 0..3 (four scale groups, in the four chunks 4h + g).  Its bytes
+//     are three 16-byte fields of the block (two of ql, one of qh), decoded to
+//     signed codes q - 32 with one v_perm_b32 table lookup per 4 weights.
+//   * The 16 lanes of a DPP row share the quarter, so they need the same 64
+//     token bytes: lane r loads token dword (g, i) = (r >> 2, r & 3) (the 64
+//     lanes of a wave together read a token's 256-byte super-block in one
+//     coalesced load), and v_dot4c reads it from lane 4g + i through a
+//     row_newbcast DPP operand.  Lanes 0-3 of a row hold the scale words of
+//     chunks 4h + 0..3, broadcast the same way into v_fmac.
+//   * A wave step covers 16 rows x 4 consecutive super-blocks (runs of 840
+//     contiguous bytes per row).  A workgroup is 16 rows; its waves split the
+//     super-blocks, and the partial sums are added in a fixed order (the four
+//     quarter lanes of a row by a butterfly, then the waves in index order).
+#include "internal.h"
+#include "q6k_device.h"
+
+namespace mmq {
+namespace {
+
+constexpr int kMaxWaves = 4;   // waves per workgroup (split of the super-blocks)
+
+// Four group dots of one token: D_g = sum_i dot4(cw[g][i], token word 4g + i
+// of the DPP row), as float32 (exact: |D| <= 65024).  The asm keeps the
+// hazard rules the compiler cannot see: 2 wait states before a DPP read of a
+// VALU-written source (s_nop 1), and 3 between a v_dot4 result and a non-dot
+// VALU reading it (four interleaved chains, converted in the order they end).
+__device__ __forceinline__ void group_dots(float (&Df)[4], uint32_t tok, const uint32_t (&cw)[4][4]) {
+    int A0 = 0, A1 = 0, A2 = 0, A3 = 0;
+    asm("s_nop 1\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 0\n\t"
+        "v_cvt_f32_i32 %0, %0\n\t"
+        "v_cvt_f32_i32 %1, %1\n\t"
+        "v_cvt_f32_i32 %2, %2\n\t"
+        "v_cvt_f32_i32 %3, %3"
+        : "+v"(A0), "+v"(A1), "+v"(A2), "+v"(A3)
+        : "v"(tok), "v"(cw[0][0]), "v"(cw[0][1]), "v"(cw[0][2]), "v"(cw[0][3]), "v"(cw[1][0]),
+          "v"(cw[1][1]), "v"(cw[1][2]), "v"(cw[1][3]), "v"(cw[2][0]), "v"(cw[2][1]), "v"(cw[2][2]),
+          "v"(cw[2][3]), "v"(cw[3][0]), "v"(cw[3][1]), "v"(cw[3][2]), "v"(cw[3][3]));
+    Df[0] = __builtin_bit_cast(float, A0);
+    Df[1] = __builtin_bit_cast(float, A1);
+    Df[2] = __builtin_bit_cast(float, A2);
+    Df[3] = __builtin_bit_cast(float, A3);
+}
+
+// acc += sum_g da(lane g of the DPP row) * y[g]
+__device__ __forceinline__ void fold4(float& acc, float da, const float (&y)[4]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(da), "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
+}
+
+// Registers of one wave step: SW super-blocks of the lane's row quarter
+// (three code fields, the scale field and d) and the lane's token dword and
+// scale word of every token.
+template <int N, int SW>
+struct Step {
+    uint32_t ql0[SW][5], ql1[SW][5], qh[SW][5], sc[SW][5];
+    uint32_t dh[SW];
+    uint32_t tq[N][SW], tw[N][SW];
+};
+
+// Every load is unconditional: slots past the wave's last super-block
+// re-read that block (and are computed with d = 0).
+template <int N, int SW>
+__device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* __restrict__ w,
+                                          int64_t rowS, const int8_t* __restrict__ q,
+                                          const uint32_t* __restrict__ ds, int K, int C, int s,
+                                          int last, int h, int e, int r) {
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+        const int sb = min(s + j, last);
+        const int64_t B = (rowS + sb) * kQ6kBlockBytes;
+        const uint32_t sh = (uint32_t)B & 3u;
+        q6k::load_run(w, B, q6k::ql0_off(h, e), sh, st.ql0[j]);
+        q6k::load_run(w, B, q6k::ql1_off(h, e), sh, st.ql1[j]);
+        q6k::load_run(w, B, q6k::qh_off(h, e), sh, st.qh[j]);
+        q6k::load_run(w, B, 192, sh, st.sc[j], 12);
+        st.dh[j] = *reinterpret_cast<const uint16_t*>(w + B + 208);
+        const int64_t toff = (int64_t)sb * 256 + 128 * h + 32 * (r >> 2) + 16 * e + 4 * (r & 3);
+        const int64_t woff = (int64_t)sb * 8 + 4 * h + (r & 3);
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            st.tq[t][j] = q6k::ld32(reinterpret_cast<const uint8_t*>(q) + (int64_t)t * K + toff);
+            st.tw[t][j] = ds[(int64_t)t * C + woff];
+        }
+    }
+}
+
+template <int N, int SW>
+__device__ __forceinline__ void compute_step(const Step<N, SW>& st, int64_t rowS, int s, int last,
+                                             int h, int e, float* acc) {
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+        // the block load_step read for this slot
+        const uint32_t sh = (uint32_t)((rowS + min(s + j, last)) * kQ6kBlockBytes) & 3u;
+        uint32_t cw[4][4];
+        q6k::quarter_codes(st.ql0[j], st.ql1[j], st.qh[j], sh, cw);
+        const float d = s + j <= last ? q6k::half_to_float(st.dh[j]) : 0.0f;
+        // scales of groups 8h + 2g + e: byte 2(g & 1) + e of scale word 2h + (g >> 1)
+        const uint32_t w0 = q6k::run_word(st.sc[j], 0, sh), w1 = q6k::run_word(st.sc[j], 1, sh);
+        const uint32_t w2 = q6k::run_word(st.sc[j], 2, sh), w3 = q6k::run_word(st.sc[j], 3, sh);
+        const uint32_t lo = h ? w2 : w0, hi = h ? w3 : w1;
+        float dsc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            dsc[g] = d * (float)(int)(int8_t)(((g >> 1) ? hi : lo) >> (8 * (2 * (g & 1) + e)));
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            float Df[4], y[4];
+            group_dots(Df, st.tq[t][j], cw);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) y[g] = dsc[g] * Df[g];
+            fold4(acc[t], q6k::half_to_float(st.tw[t][j]), y);
+        }
+    }
+}
+
+template <int N, int SW, bool H>
+__global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint8_t* __restrict__ w,
+                                                                      const int8_t* __restrict__ q,
+                                                                      const uint32_t* __restrict__ ds,
+                                                                      int M, int K,
+                                                                      void* __restrict__ out) {
+    __shared__ float red[kMaxWaves][N][16];
+
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int p = lane >> 4, r = lane & 15, h = p >> 1, e = p & 1;
+    const int row0 = blockIdx.x * 16;
+    const int S = K >> 8, C = K >> 5;
+    const int sb0 = (int)((int64_t)S * wv / W), sb1 = (int)((int64_t)S * (wv + 1) / W);
+    const int64_t rowS = (int64_t)min(row0 + r, M - 1) * S;
+
+    float acc[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) acc[t] = 0.0f;
+
+    const int last = sb1 - 1;
+    for (int s = sb0; s < sb1; s += SW) {
+        Step<N, SW> A;
+        load_step<N, SW>(A, w, rowS, q, ds, K, C, s, last, h, e, r);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step<N, SW>(A, rowS, s, last, h, e, acc);
+    }
+
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        acc[t] += __shfl_xor(acc[t], 16);
+        acc[t] += __shfl_xor(acc[t], 32);
+        if (p == 0) red[wv][t][r] = acc[t];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * N; i += blockDim.x) {
+        const int t = i >> 4, rr = i & 15;
+        float sum = red[0][t][rr];
+        for (int v = 1; v < W; ++v) sum += red[v][t][rr];
+        if (row0 + rr < M) store_out<H>(out, (int64_t)t * M + row0 + rr, sum);
+    }
+}
+
+template <int N>
+hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                    void* out, bool half_out, hipStream_t stream) {
+    const int S = k / 256;
+    const int rows = (m + 15) / 16;
+    // Same split as the q4_K vector-ALU kernel: about 1024 waves in all for
+    // one token, 4 waves per row tile for more.
+    int waves = N == 1 ? 1024 / rows : 4;
+    waves = waves < 1 ? 1 : waves > kMaxWaves ? kMaxWaves : waves;
+    waves = waves > S ? S : waves;
+    constexpr int SW = 4;
+    if (half_out)
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), 0, stream,
+                           w, q, ds, m, k, out);
+    else
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), 0, stream,
+                           w, q, ds, m, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_q6k_gemv(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                           int n, void* out, bool half_out, hipStream_t stream) {
+    switch (n) {
+        case 1: return launch_n<1>(w, m, k, q, ds, out, half_out, stream);
+        case 2: return launch_n<2>(w, m, k, q, ds, out, half_out, stream);
+        case 3: return launch_n<3>(w, m, k, q, ds, out, half_out, stream);
+        case 4: return launch_n<4>(w, m, k, q, ds, out, half_out, stream);
+        case 5: return launch_n<5>(w, m, k, q, ds, out, half_out, stream);
+        case 6: return launch_n<6>(w, m, k, q, ds, out, half_out, stream);
+        case 7: return launch_n<7>(w, m, k, q, ds, out, half_out, stream);
+        case 8: return launch_n<8>(w, m, k, q, ds, out, half_out, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mmq

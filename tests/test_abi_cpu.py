@@ -30,7 +30,7 @@ def lib():
     return binding.load_library()
 
 
-def test_header_declares_the_three_calls():
+def test_header_declares_every_exported_call():
     names = declared_functions()
     assert set(names) == set(binding.EXPORTS), names
 
@@ -66,7 +66,11 @@ def test_quantize_validation(lib, args, want):
     assert lib.q8_quantize_rows(*args, None) == want
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out"])
+MMQ_CALLS = ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
+             "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out"]
+
+
+@pytest.mark.parametrize("fn", MMQ_CALLS)
 @pytest.mark.parametrize("args,want", [
     ((A, 8, 512, A, A, -3, A), SHAPE),
     ((A, -8, 512, A, A, 3, A), SHAPE),
@@ -88,7 +92,8 @@ def test_mmq_validation(lib, fn, args, want):
     assert getattr(lib, fn)(*args, None) == want
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out"])
+@pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
+                                "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out"])
 def test_fold_needs_scales(lib, fn):
     assert getattr(lib, fn)(A, 8, 512, A, 0, 3, A, None) == NULL
     assert getattr(lib, fn)(A, 8, 512, A, MIS, 3, A, None) == ALIGN
@@ -102,6 +107,18 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.mmq_q4k_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4k_q8(A, 8, 512, A, 0, 3, A, None) == DEVICE
+    assert lib.mmq_q6k_q8(A, 8, 512, A, 0, 3, A, None) == DEVICE
+    assert lib.mmq_q6k_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.mmq_q6k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
+
+
+def test_q6k_weight_bytes_limit(lib):
+    # m*(k/256) blocks with 144*blocks < 2^40 <= 210*blocks: an empty q4_K
+    # call passes, the q6_K one is rejected for its larger blocks.
+    m, k = 6_000_000, 1 << 18
+    assert m * (k // 256) * 144 < 1 << 40 <= m * (k // 256) * 210
+    assert lib.mmq_q4k_q8_fp32out(A, m, k, A, A, 0, A, None) == OK
+    assert lib.mmq_q6k_q8_fp32out(A, m, k, A, A, 0, A, None) == OVERFLOW
 
 
 def test_binding_raises_on_error_status(lib):
