@@ -17,10 +17,14 @@
 //     coalesced load), and v_dot4c reads it from lane 4g + i through a
 //     row_newbcast DPP operand.  Lanes 0-3 of a row hold the scale words of
 //     chunks 4h + 0..3, broadcast the same way into v_fmac.
-//   * A wave step covers 16 rows x 4 consecutive super-blocks (runs of 840
-//     contiguous bytes per row).  A workgroup is 16 rows; its waves split the
-//     super-blocks, and the partial sums are added in a fixed order (the four
-//     quarter lanes of a row by a butterfly, then the waves in index order).
+//   * A wave step covers 16 rows x SW consecutive super-blocks.  q6_K blocks
+//     (210 bytes) start only 2-byte aligned, and 16-byte loads at 4-byte
+//     aligned addresses measured slow (the address unit was ~65% busy), so
+//     the step's bytes of each row are first copied into the wave's LDS area
+//     with aligned 16-byte loads, and the block fields are read from LDS.
+//   * A workgroup is 16 rows; its waves split the super-blocks, and the
+//     partial sums are added in a fixed order (the four quarter lanes of a
+//     row by a butterfly, then the waves in index order).
 #include "internal.h"
 #include "q6k_device.h"
 
@@ -79,56 +83,110 @@ __device__ __forceinline__ void fold4(float& acc, float da, const float (&y)[4])
         : "v"(da), "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
 }
 
-// Registers of one wave step: SW super-blocks of the lane's row quarter
-// (three code fields, the scale field and d) and the lane's token dword and
-// scale word of every token.
+// One wave step: SW super-blocks of 16 rows.  The rows' bytes are copied
+// into the wave's LDS area with aligned 16-byte loads (row r's run of SW
+// blocks, from the 16-byte boundary below its first byte, at r * SEG), so
+// that every global load is an aligned, coalesced piece of contiguous rows;
+// the 2-byte-aligned block fields are then read from LDS as aligned dwords
+// and shifted into place (see q6k_device.h).
+template <int SW>
+struct Seg {
+    static constexpr int kChunks = (SW * kQ6kBlockBytes + 14 + 15) / 16;  // per row
+    static constexpr int kBytes = kChunks * 16 + 16;   // row stride in LDS (+16: spreads banks)
+    static constexpr int kLoads = (16 * kChunks + 63) / 64;   // 16-byte pieces per lane
+};
+
+// A 16-byte piece at byte offset a (a % 16 == 0) of the weights, reading
+// nothing at or past byte `total` (the last piece of the matrix may be
+// partial: its bytes past the end read as 0).
+__device__ __forceinline__ uint4 load_piece(const uint8_t* __restrict__ w, int64_t a, int64_t total) {
+    if (a + 16 <= total) return *reinterpret_cast<const uint4*>(w + a);
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (a + 2 * i + 2 <= total)
+            d[i >> 1] |= (uint32_t)*reinterpret_cast<const uint16_t*>(w + a + 2 * i) << (16 * (i & 1));
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// The five LDS dwords covering 16 bytes at LDS byte address `a` (2-aligned).
+__device__ __forceinline__ void lds_run(const uint8_t* base, int a, uint32_t (&v)[5]) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(base + (a & ~3));
+#pragma unroll
+    for (int i = 0; i < 5; ++i) v[i] = p[i];
+}
+
+// Global data of one wave step, as one lane holds it: its 16-byte pieces of
+// the 16 rows' bytes, and its token dword and scale word of every slot.
 template <int N, int SW>
-struct Step {
-    uint32_t ql0[SW][5], ql1[SW][5], qh[SW][5], sc[SW][5];
-    uint32_t dh[SW];
+struct Fetch {
+    uint4 pc[Seg<SW>::kLoads];
     uint32_t tq[N][SW], tw[N][SW];
 };
 
-// Every load is unconditional: slots past the wave's last super-block
-// re-read that block (and are computed with d = 0).
+// Issue the global loads of the step at super-block s (s may lie past the
+// wave's range: then it re-reads the range's last block and is not used).
 template <int N, int SW>
-__device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* __restrict__ w,
-                                          int64_t rowS, const int8_t* __restrict__ q,
-                                          const uint32_t* __restrict__ ds, int K, int C, int s,
-                                          int last, int h, int e, int r) {
+__device__ __forceinline__ void fetch_step(Fetch<N, SW>& f, const uint8_t* __restrict__ w,
+                                           int64_t total, int row0, int M, int S,
+                                           const int8_t* __restrict__ q,
+                                           const uint32_t* __restrict__ ds, int K, int C, int s,
+                                           int last, int lane, int h, int e, int r) {
+    typedef Seg<SW> G;
+    s = min(s, last);
+#pragma unroll
+    for (int k = 0; k < G::kLoads; ++k) {
+        const int i = lane + 64 * k;
+        const int rr = i / G::kChunks, ch = i - rr * G::kChunks;
+        const int64_t a0 = (((int64_t)min(row0 + rr, M - 1) * S + s) * kQ6kBlockBytes) & ~(int64_t)15;
+        f.pc[k] = (i < 16 * G::kChunks) ? load_piece(w, a0 + 16 * ch, total) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
         const int sb = min(s + j, last);
-        const int64_t B = (rowS + sb) * kQ6kBlockBytes;
-        const uint32_t sh = (uint32_t)B & 3u;
-        q6k::load_run(w, B, q6k::ql0_off(h, e), sh, st.ql0[j]);
-        q6k::load_run(w, B, q6k::ql1_off(h, e), sh, st.ql1[j]);
-        q6k::load_run(w, B, q6k::qh_off(h, e), sh, st.qh[j]);
-        q6k::load_run(w, B, 192, sh, st.sc[j], 12);
-        st.dh[j] = *reinterpret_cast<const uint16_t*>(w + B + 208);
         const int64_t toff = (int64_t)sb * 256 + 128 * h + 32 * (r >> 2) + 16 * e + 4 * (r & 3);
         const int64_t woff = (int64_t)sb * 8 + 4 * h + (r & 3);
 #pragma unroll
         for (int t = 0; t < N; ++t) {
-            st.tq[t][j] = q6k::ld32(reinterpret_cast<const uint8_t*>(q) + (int64_t)t * K + toff);
-            st.tw[t][j] = ds[(int64_t)t * C + woff];
+            f.tq[t][j] = q6k::ld32(reinterpret_cast<const uint8_t*>(q) + (int64_t)t * K + toff);
+            f.tw[t][j] = ds[(int64_t)t * C + woff];
         }
     }
 }
 
+// Stage the fetched pieces in the wave's LDS area and compute the step.
 template <int N, int SW>
-__device__ __forceinline__ void compute_step(const Step<N, SW>& st, int64_t rowS, int s, int last,
-                                             int h, int e, float* acc) {
+__device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, uint8_t* __restrict__ lds,
+                                             int64_t rowS, int s, int last, int lane, int h, int e,
+                                             int r, float* acc) {
+    typedef Seg<SW> G;
+#pragma unroll
+    for (int k = 0; k < G::kLoads; ++k) {
+        const int i = lane + 64 * k;
+        const int rr = i / G::kChunks, ch = i - rr * G::kChunks;
+        if (i < 16 * G::kChunks) *reinterpret_cast<uint4*>(lds + rr * G::kBytes + 16 * ch) = f.pc[k];
+    }
+    // LDS accesses of one wave complete in order: the reads below see the
+    // writes above, and the next step's writes come after these reads.
+    const int64_t base0 = ((rowS + s) * kQ6kBlockBytes) & ~(int64_t)15;
+    const uint8_t* row_lds = lds + r * G::kBytes;
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
-        // the block load_step read for this slot
-        const uint32_t sh = (uint32_t)((rowS + min(s + j, last)) * kQ6kBlockBytes) & 3u;
-        uint32_t cw[4][4];
-        q6k::quarter_codes(st.ql0[j], st.ql1[j], st.qh[j], sh, cw);
-        const float d = s + j <= last ? q6k::half_to_float(st.dh[j]) : 0.0f;
+        // byte offset of block s + j in the row's LDS copy; a slot past the
+        // wave's last block reads the last block (and computes with d = 0)
+        const int off = (int)((rowS + min(s + j, last)) * kQ6kBlockBytes - base0);
+        const uint32_t sh = (uint32_t)off & 3u;
+        uint32_t ql0[5], ql1[5], qh[5], sc[5], cw[4][4];
+        lds_run(row_lds, off + q6k::ql0_off(h, e), ql0);
+        lds_run(row_lds, off + q6k::ql1_off(h, e), ql1);
+        lds_run(row_lds, off + q6k::qh_off(h, e), qh);
+        lds_run(row_lds, off + 192, sc);
+        const uint32_t dword = *reinterpret_cast<const uint32_t*>(row_lds + ((off + 208) & ~3));
+        q6k::quarter_codes(ql0, ql1, qh, sh, cw);
+        const float d = s + j <= last ? q6k::half_to_float(dword >> (8 * sh)) : 0.0f;
         // scales of groups 8h + 2g + e: byte 2(g & 1) + e of scale word 2h + (g >> 1)
-        const uint32_t w0 = q6k::run_word(st.sc[j], 0, sh), w1 = q6k::run_word(st.sc[j], 1, sh);
-        const uint32_t w2 = q6k::run_word(st.sc[j], 2, sh), w3 = q6k::run_word(st.sc[j], 3, sh);
+        const uint32_t w0 = q6k::run_word(sc, 0, sh), w1 = q6k::run_word(sc, 1, sh);
+        const uint32_t w2 = q6k::run_word(sc, 2, sh), w3 = q6k::run_word(sc, 3, sh);
         const uint32_t lo = h ? w2 : w0, hi = h ? w3 : w1;
         float dsc[4];
 #pragma unroll
@@ -137,10 +195,10 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int64_t rowS
 #pragma unroll
         for (int t = 0; t < N; ++t) {
             float Df[4], y[4];
-            group_dots(Df, st.tq[t][j], cw);
+            group_dots(Df, f.tq[t][j], cw);
 #pragma unroll
             for (int g = 0; g < 4; ++g) y[g] = dsc[g] * Df[g];
-            fold4(acc[t], q6k::half_to_float(st.tw[t][j]), y);
+            fold4(acc[t], q6k::half_to_float(f.tw[t][j]), y);
         }
     }
 }
@@ -151,6 +209,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint
                                                                       const uint32_t* __restrict__ ds,
                                                                       int M, int K,
                                                                       void* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t seg[];   // W x 16 x Seg<SW>::kBytes
     __shared__ float red[kMaxWaves][N][16];
 
     const int W = blockDim.x >> 6;
@@ -160,18 +219,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint
     const int row0 = blockIdx.x * 16;
     const int S = K >> 8, C = K >> 5;
     const int sb0 = (int)((int64_t)S * wv / W), sb1 = (int)((int64_t)S * (wv + 1) / W);
+    const int64_t total = (int64_t)M * S * kQ6kBlockBytes;
     const int64_t rowS = (int64_t)min(row0 + r, M - 1) * S;
 
     float acc[N];
 #pragma unroll
     for (int t = 0; t < N; ++t) acc[t] = 0.0f;
 
+    // One step at a time: its loads are issued, then it is staged and
+    // computed.  (Fetching the next step during the current one measured no
+    // faster: the wave count per SIMD, not one wave's latency, sets the rate.)
     const int last = sb1 - 1;
+    uint8_t* lds = seg + wv * 16 * Seg<SW>::kBytes;
     for (int s = sb0; s < sb1; s += SW) {
-        Step<N, SW> A;
-        load_step<N, SW>(A, w, rowS, q, ds, K, C, s, last, h, e, r);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_step<N, SW>(A, rowS, s, last, h, e, acc);
+        Fetch<N, SW> f;
+        fetch_step<N, SW>(f, w, total, row0, M, S, q, ds, K, C, s, last, lane, h, e, r);
+        compute_step<N, SW>(f, lds, rowS, s, last, lane, h, e, r, acc);
     }
 
 #pragma unroll
@@ -189,24 +252,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint
     }
 }
 
+template <int N, int SW>
+hipError_t launch_sw(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                     void* out, bool half_out, hipStream_t stream, int waves) {
+    const int rows = (m + 15) / 16;
+    const size_t lds = (size_t)waves * 16 * Seg<SW>::kBytes;
+    if (half_out)
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), lds, stream,
+                           w, q, ds, m, k, out);
+    else
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), lds, stream,
+                           w, q, ds, m, k, out);
+    return hipGetLastError();
+}
+
 template <int N>
 hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                     void* out, bool half_out, hipStream_t stream) {
+    // Measured on the 28672 x 8192 q6_K matrix: 4 waves per row tile, steps
+    // of 2 super-blocks for one token and of 1 for more (whose vector work per
+    // byte is larger): 38 us at 1 token, 55 us at 7.
     const int S = k / 256;
-    const int rows = (m + 15) / 16;
-    // Same split as the q4_K vector-ALU kernel: about 1024 waves in all for
-    // one token, 4 waves per row tile for more.
-    int waves = N == 1 ? 1024 / rows : 4;
-    waves = waves < 1 ? 1 : waves > kMaxWaves ? kMaxWaves : waves;
-    waves = waves > S ? S : waves;
-    constexpr int SW = 4;
-    if (half_out)
-        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), 0, stream,
-                           w, q, ds, m, k, out);
-    else
-        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), 0, stream,
-                           w, q, ds, m, k, out);
-    return hipGetLastError();
+    const int waves = S < kMaxWaves ? S : kMaxWaves;
+    return N == 1 ? launch_sw<N, 2>(w, m, k, q, ds, out, half_out, stream, waves)
+                  : launch_sw<N, 1>(w, m, k, q, ds, out, half_out, stream, waves);
 }
 
 }  // namespace

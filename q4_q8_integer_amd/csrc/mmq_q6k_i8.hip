@@ -19,7 +19,8 @@
 //     and per super-block out += d * acc_b.
 //   * Workgroup tile 128 rows x 128 tokens, 4 waves of 64x64 (2x2 MFMA tiles),
 //     one super-block (256 k) staged per step.  LDS rows are 272 bytes
-//     (256 + 16 pad) for both operands.
+//     (256 + 16 pad) for both operands; with the scales as 16-bit values a
+//     workgroup takes under 80 KB, so two share a CU.
 //
 // Epilogues: kDots (exact int32 group dots[t][o][g], the parity entry), kFp32
 // (float32 out[t][o]), kF16 (the same float32 value stored as binary16).
@@ -39,14 +40,14 @@ constexpr int STRIDE = 272;        // LDS bytes per row of either operand
 enum { kDots = 0, kFp32 = 1, kF16 = 2 };
 
 template <int EPI>
-__global__ __launch_bounds__(NT) void mmq_q6k_i8_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(NT, 2) void mmq_q6k_i8_kernel(const uint8_t* __restrict__ w,
                                                         const int8_t* __restrict__ q,
                                                         const uint32_t* __restrict__ ds,
                                                         int M, int N, int K, int tiles_m,
                                                         void* __restrict__ outp) {
     __shared__ __attribute__((aligned(16))) uint8_t sW[BM * STRIDE];
     __shared__ __attribute__((aligned(16))) uint8_t sX[BN * STRIDE];
-    __shared__ __attribute__((aligned(16))) int sSc[16][BM];     // scale per (group, row)
+    __shared__ __attribute__((aligned(16))) short sSc[16][BM];   // scale per (group, row)
     __shared__ __attribute__((aligned(16))) float sD[BM];        // d per row
     __shared__ __attribute__((aligned(16))) float sDa[8][BN];    // da per (chunk, token)
 
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(NT) void mmq_q6k_i8_kernel(const uint8_t* __restric
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t word = q6k::run_word(sv, j, sh);
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) sSc[4 * j + b][r] = (int)(int8_t)(word >> (8 * b));
+                    for (int b = 0; b < 4; ++b) sSc[4 * j + b][r] = (short)(int8_t)(word >> (8 * b));
                 }
                 sD[r] = q6k::half_to_float(*reinterpret_cast<const uint16_t*>(w + B + 208));
             }
@@ -162,10 +163,12 @@ __global__ __launch_bounds__(NT) void mmq_q6k_i8_kernel(const uint8_t* __restric
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int r = wm * 64 + mt * 32 + 8 * jj + 4 * g;
-                        const int4 a = *reinterpret_cast<const int4*>(&sSc[2 * c][r]);
-                        const int4 b = *reinterpret_cast<const int4*>(&sSc[2 * c + 1][r]);
-                        s0[4 * jj] = a.x; s0[4 * jj + 1] = a.y; s0[4 * jj + 2] = a.z; s0[4 * jj + 3] = a.w;
-                        s1[4 * jj] = b.x; s1[4 * jj + 1] = b.y; s1[4 * jj + 2] = b.z; s1[4 * jj + 3] = b.w;
+                        const uint2 a = *reinterpret_cast<const uint2*>(&sSc[2 * c][r]);
+                        const uint2 b = *reinterpret_cast<const uint2*>(&sSc[2 * c + 1][r]);
+                        s0[4 * jj] = (short)a.x; s0[4 * jj + 1] = (int)a.x >> 16;
+                        s0[4 * jj + 2] = (short)a.y; s0[4 * jj + 3] = (int)a.y >> 16;
+                        s1[4 * jj] = (short)b.x; s1[4 * jj + 1] = (int)b.x >> 16;
+                        s1[4 * jj + 2] = (short)b.y; s1[4 * jj + 3] = (int)b.y >> 16;
                     }
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
