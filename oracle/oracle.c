@@ -36,6 +36,9 @@
  * D[t][o][g] = sum_{i<16} (q - 32)*q8 (exact), output
  * sum_g d*sc[g]*da[t][g/2]*D in float64 in group order (no min term).
  *
+ * Fused SiLU-gate quantize (oracle_q8_quantize_silu_mul): the quantizer applied
+ * to h = float32(g*u / (1 + exp(-g))) evaluated in float64.
+ *
  * Readings taken where the pages are silent: rounding ties go away from zero
  * (C roundf); q is computed from the fp32 da, the rescale uses the binary16
  * da; an all-zero block has da = 0, q = 0, ssum = 0; q is clamped to
@@ -134,6 +137,39 @@ int oracle_q8_quantize(const float *x, int64_t n, int64_t k, int8_t *q, uint32_t
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------- fused SiLU-gate quantize */
+/* The FFN down-projection input h = SiLU(gate) * up, quantized to q8 without
+ * writing h (the pages' later "quantize-transpose prepass" moved activation
+ * quantization into a prepass of its own; fusing the gate into it is this
+ * library's reading).  h is defined as the float32 rounding of the float64
+ * value  g*u / (1 + exp(-g)):  g*u is exact in float64 (two 24-bit
+ * significands), then one IEEE add, one IEEE divide and the round to float32;
+ * only exp() is a library function.  The quantization of h is exactly
+ * oracle_q8_quantize. */
+void oracle_silu_mul(const float *g, const float *u, int64_t count, float *h)
+{
+    for (int64_t i = 0; i < count; i++) {
+        const double gd = (double)g[i];
+        const double s = 1.0 + exp(-gd);
+        h[i] = (float)(gd * (double)u[i] / s);
+    }
+}
+
+int oracle_q8_quantize_silu_mul(const float *g, const float *u, int64_t n, int64_t k,
+                                int8_t *q, uint32_t *ds)
+{
+    if (n < 0 || k < 0 || k % 32)
+        return -1;
+    int rc = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
+    for (int64_t t = 0; t < n; t++) {
+        float row[k > 0 ? k : 1];
+        oracle_silu_mul(g + t * k, u + t * k, k, row);
+        rc |= oracle_q8_quantize(row, 1, k, q + t * k, ds + t * (k / 32));
+    }
+    return rc;
 }
 
 /* ------------------------------------------------------------ q4_K decoding */

@@ -33,6 +33,9 @@ def _declare(lib):
     lib.oracle_q4k_unpack.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]
     lib.oracle_blockdots.argtypes = [c_p, c_i64, c_i64, c_p, c_i64, c_p]
     lib.oracle_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
+    lib.oracle_silu_mul.argtypes = [c_p, c_p, c_i64, c_p]
+    lib.oracle_silu_mul.restype = None
+    lib.oracle_q8_quantize_silu_mul.argtypes = [c_p, c_p, c_i64, c_i64, c_p, c_p]
     lib.oracle_q6k_unpack.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p]
     lib.oracle_q6k_dots.argtypes = [c_p, c_i64, c_i64, c_p, c_i64, c_p]
     lib.oracle_q6k_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
@@ -44,7 +47,7 @@ def _declare(lib):
     lib.oracle_get_threads.restype = ctypes.c_int
     for fn in (lib.oracle_q8_quantize, lib.oracle_q4k_unpack, lib.oracle_blockdots,
                lib.oracle_out_f64, lib.oracle_q6k_unpack, lib.oracle_q6k_dots,
-               lib.oracle_q6k_out_f64):
+               lib.oracle_q6k_out_f64, lib.oracle_q8_quantize_silu_mul):
         fn.restype = ctypes.c_int
     return lib
 
@@ -90,6 +93,29 @@ def quantize(x: np.ndarray, lib=None):
     q = np.empty((n, k), dtype=np.int8)
     ds = np.empty((n, k // 32), dtype=np.uint32)
     _check(lib.oracle_q8_quantize(_ptr(x), n, k, _ptr(q), _ptr(ds)), "quantize")
+    return q, ds
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray, lib=None) -> np.ndarray:
+    """h = float32(g*u / (1 + exp(-g))) evaluated in float64, elementwise."""
+    lib = lib or load()
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    h = np.empty_like(g)
+    lib.oracle_silu_mul(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def quantize_silu_mul(g: np.ndarray, u: np.ndarray, lib=None):
+    """Fused SiLU-gate quantize: (q int8 [n, k], ds uint32 [n, k/32]) of h = SiLU(g)*u."""
+    lib = lib or load()
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    n, k = g.shape
+    q = np.empty((n, k), dtype=np.int8)
+    ds = np.empty((n, k // 32), dtype=np.uint32)
+    _check(lib.oracle_q8_quantize_silu_mul(_ptr(g), _ptr(u), n, k, _ptr(q), _ptr(ds)),
+           "quantize_silu_mul")
     return q, ds
 
 

@@ -445,10 +445,67 @@ def pin_q6k_one_superblock(lib):
     assert oracle.q6k_out_f64(w, 1, 256, q, ds, lib=lib)[0, 0] == out
 
 
+# --------------------------------------------------- fused SiLU-gate quantize
+def _gate_inputs(seed, n, k):
+    rng = np.random.default_rng([950, seed])
+    g = (rng.standard_normal((n, k)) * 3).astype(np.float32)
+    u = rng.standard_normal((n, k)).astype(np.float32)
+    g[0, :64] = np.linspace(-120, 120, 64, dtype=np.float32)   # saturated sigmoid both ways
+    g[0, 64:96] = 0.0
+    u[0, 96:128] = 0.0
+    return g, u
+
+
+def _silu_mul_f64(g, u):
+    gd = g.astype(np.float64)
+    return (gd * u.astype(np.float64) / (1.0 + np.exp(-gd))).astype(np.float32)
+
+
+def pin_silu_mul_float64(lib):
+    """h = float32 of g*u/(1 + exp(-g)) in float64: equal to numpy's float64
+    evaluation (a different exp) on all but a vanishing fraction, and never
+    more than one float32 ulp away."""
+    g, u = _gate_inputs(1, 40, 4096)
+    h = oracle.silu_mul(g, u, lib=lib)
+    ref = _silu_mul_f64(g, u)
+    diff = h != ref
+    assert diff.mean() <= 1e-4, "h differs from the float64 definition at %d places" % diff.sum()
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(h.astype(np.float64) - ref) <= ulp)
+
+
+def pin_silu_mul_closed_forms(lib):
+    """g = 0 gives 0; g >= 40 gives float32(g*u) exactly (exp(-g) vanishes
+    next to 1); g <= -800 gives 0; SiLU(g) - SiLU(-g) = g."""
+    g = np.array([0.0, 40.0, 55.5, 1e4, -800.0, -1e4], dtype=np.float32)
+    u = np.array([3.0, 1.5, -2.25, 7.0, 5.0, -3.0], dtype=np.float32)
+    h = oracle.silu_mul(g, u, lib=lib)
+    assert h[0] == 0.0
+    assert np.array_equal(h[1:4], (g[1:4] * u[1:4]).astype(np.float32))
+    assert h[4] == 0.0 and h[5] == 0.0
+    x = np.linspace(-9, 9, 1001, dtype=np.float32)
+    one = np.ones_like(x)
+    d = oracle.silu_mul(x, one, lib=lib).astype(np.float64) - oracle.silu_mul(-x, one, lib=lib)
+    assert np.all(np.abs(d - x) <= 4 * np.spacing(np.abs(x) + 1).astype(np.float64))
+
+
+def pin_quantize_silu_mul(lib):
+    """The fused quantizer = the (pinned) quantizer applied to the float64
+    definition of h, bit for bit, on rows where numpy's h agrees."""
+    g, u = _gate_inputs(2, 24, 2048)
+    q, ds = oracle.quantize_silu_mul(g, u, lib=lib)
+    ref = _silu_mul_f64(g, u)
+    same = np.all(oracle.silu_mul(g, u, lib=lib) == ref, axis=1)
+    assert same.mean() > 0.9
+    rq, rds = oracle.quantize(ref[same], lib=lib)
+    assert np.array_equal(q[same], rq) and np.array_equal(ds[same], rds)
+
+
 ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundtrip,
             pin_q8_golden, pin_q8_invariants, pin_q8_zero_block, pin_dots_bruteforce,
             pin_dots_closed_forms, pin_out_bruteforce, pin_out_special_cases,
             pin_out_zero_scale_block, pin_one_superblock,
             pin_q6k_golden_block, pin_q6k_roundtrip, pin_q6k_dots_bruteforce,
             pin_q6k_dots_closed_forms, pin_q6k_out_bruteforce, pin_q6k_out_special_cases,
-            pin_q6k_one_superblock]
+            pin_q6k_one_superblock, pin_silu_mul_float64, pin_silu_mul_closed_forms,
+            pin_quantize_silu_mul]

@@ -44,6 +44,10 @@ MUTANTS = [
      "*d = oracle_f16_to_double((uint16_t)(b[0] | (b[1] << 8)));"),
     ("q6_group_skips_last", "for (int i = 0; i < 16; i++)\n                        acc += (q6",
      "for (int i = 0; i < 15; i++)\n                        acc += (q6"),
+    ("silu_without_up", "h[i] = (float)(gd * (double)u[i] / s);", "h[i] = (float)(gd / s);"),
+    ("sigmoid_sign", "const double s = 1.0 + exp(-gd);", "const double s = 1.0 + exp(gd);"),
+    ("silu_in_float32", "const double s = 1.0 + exp(-gd);", "const double s = (float)(1.0f + expf((float)-gd));"),
+    ("quantize_gate_not_h", "rc |= oracle_q8_quantize(row, 1, k,", "rc |= oracle_q8_quantize(g + t * k, 1, k,"),
 ]
 
 
