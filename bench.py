@@ -129,6 +129,103 @@ def cpu_baseline(mats, inputs, budget_s: float = 12.0):
                       "(%.1f s)" % (nt, t)}
 
 
+def run_silu_q8(args):
+    """The fused SiLU-gate quantizer (q8_quantize_silu_mul) on the FFN down
+    projection's input, 2630 x 11008: a step is one fused quantize.  The
+    unfused equivalent (torch's SiLU and product, then q8_quantize_rows) is
+    timed beside it for context."""
+    import torch
+    from q4_q8_integer_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    g, u = synth.ffn_gate_up_outputs()
+    n, k = g.shape
+    sets = []
+    for _ in range(max(1, args.copies)):
+        sets.append((torch.from_numpy(g).to(dev), torch.from_numpy(u).to(dev),
+                     torch.empty((n, k), dtype=torch.int8, device=dev),
+                     torch.empty((n, k // 32), dtype=torch.int32, device=dev)))
+    h = torch.empty((n, k), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        gd, ud, q, ds = sets[i % len(sets)]
+        binding.q8_quantize_silu_mul(gd, ud, n, k, q, ds)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stream = torch.cuda.current_stream()
+    rounds = max(args.steps, 10)
+
+    def event_time(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(50_000_000)
+        e0.record(stream)
+        for i in range(rounds):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / rounds
+
+    fused_ms = event_time(step)
+
+    def unfused(i):
+        gd, ud, q, ds = sets[i % len(sets)]
+        torch.mul(torch.nn.functional.silu(gd), ud, out=h)
+        binding.q8_quantize_rows(h, n, k, q, ds)
+
+    unfused(0)
+    unfused_ms = event_time(unfused)
+
+    alg = 9.125 * n * k     # 4 + 4 B read, 1 + 4/32 B written per element
+    gbs = alg / (fused_ms * 1e-3) / 1e9
+    ms_step = wall * 1e3 / args.steps
+    res = {
+        "metric": "fused SiLU-gate q8 quantize throughput (FFN down input)",
+        "value": round(alg / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64->f32->i8",
+        "data": "synthetic",
+        "config": {"workload": "q8_quantize_silu_mul of SiLU(gate)*up, gate/up fp32 [%dx%d]" % (n, k),
+                   "n": n, "k": k, "copies": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "q8_quantize_silu_mul",
+                     "traffic": measured_traffic("q8_quantize_silu_mul|silu_q8"),
+                     "avg_launch_us": round(fused_ms * 1e3, 2), "launches_timed": rounds,
+                     "alg_bytes_per_step": alg},
+        "unfused_us": round(unfused_ms * 1e3, 2),
+    }
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = 2 * src.numel() * 4
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 8
+        t0 = time.perf_counter()
+        oracle.quantize_silu_mul(g[:rows], u[:rows])
+        t = time.perf_counter() - t0
+        rows = int(min(n, max(rows, rows * 12.0 / max(t, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.quantize_silu_mul(g[:rows], u[:rows])
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(9.125 * rows * k / t / 1e9, 3), "unit": "GB/s",
+                               "cores": oracle.get_threads(), "kind": "oracle",
+                               "sample": "first %d of %d rows (%.1f s)" % (rows, n, t)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +244,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "silu_q8":
+        return run_silu_q8(args)
 
     import torch
     from q4_q8_integer_amd import binding, synth

@@ -77,6 +77,24 @@ int q8_quantize_rows(const float *x, int64_t n, int64_t k, int8_t *q, uint32_t *
                      hipStream_t stream);
 
 /*
+ * q8_quantize_silu_mul - the q8 quantization of an FFN down projection's
+ * input h = SiLU(gate) * up, without writing h.  (The pages' later
+ * "quantize-transpose prepass", named on the r22 page, moved activation
+ * quantization into a pass of its own; fusing the gate product into that
+ * pass is this library's reading.)
+ *
+ *   gate, up : float [n][k] each, row-major, k % 32 == 0 (the gate and up
+ *              projections' outputs).
+ *   q, ds    : as for q8_quantize_rows, of
+ *              h = float32( g*u / (1 + exp(-g)) ) evaluated in float64
+ *              (g*u exact, IEEE add and divide, one rounding to float32).
+ * The result equals q8_quantize_rows applied to that h.  Errors and empty
+ * calls as for q8_quantize_rows.
+ */
+int q8_quantize_silu_mul(const float *gate, const float *up, int64_t n, int64_t k, int8_t *q,
+                         uint32_t *ds, hipStream_t stream);
+
+/*
  * mmq_q4k_q8 - exact per-block integer dot products (the int32 result of the
  * 32-deep integer contraction, before the two-term rescale; r31 page, section 1).
  *

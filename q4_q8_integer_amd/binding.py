@@ -14,7 +14,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
-EXPORTS = ("q8_quantize_rows", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
+EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
            "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_status_string")
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
               "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out")
@@ -41,6 +41,8 @@ def load_library(path: str = LIB_PATH):
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.q8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_rows.restype = ctypes.c_int
+    lib.q8_quantize_silu_mul.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.q8_quantize_silu_mul.restype = ctypes.c_int
     for name in _MMQ_CALLS:
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
@@ -81,6 +83,12 @@ def q8_quantize_rows(x, n, k, q, ds):
         _ptr(x), n, k, _ptr(q), _ptr(ds), _stream()))
 
 
+def q8_quantize_silu_mul(gate, up, n, k, q, ds):
+    """Enqueue the fused SiLU-gate quantizer on preallocated outputs."""
+    _check("q8_quantize_silu_mul", load_library().q8_quantize_silu_mul(
+        _ptr(gate), _ptr(up), n, k, _ptr(q), _ptr(ds), _stream()))
+
+
 def mmq_q4k_q8(w, m, k, q, ds, n, dots):
     _check("mmq_q4k_q8", load_library().mmq_q4k_q8(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
@@ -119,6 +127,19 @@ def quantize(x: torch.Tensor):
     q = torch.empty((n, k), dtype=torch.int8, device=x.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
     q8_quantize_rows(x, n, k, q, ds)
+    return q, ds
+
+
+def quantize_silu_mul(gate: torch.Tensor, up: torch.Tensor):
+    """q8 of SiLU(gate) * up: (q int8 [n, k], ds int32 [n, k/32])."""
+    _need(gate, torch.float32, "gate")
+    _need(up, torch.float32, "up")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    n, k = gate.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=gate.device)
+    ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=gate.device)
+    q8_quantize_silu_mul(gate, up, n, k, q, ds)
     return q, ds
 
 

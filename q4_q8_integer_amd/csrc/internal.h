@@ -13,6 +13,10 @@ constexpr int kBlockBytes = 144;
 hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
                               hipStream_t stream);
 
+// q8 quantize of h = float32(g*u / (1 + exp(-g))) (float64 evaluation).
+hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,
+                                       uint32_t* ds, hipStream_t stream);
+
 // Exact int32 block dots, dots[t][o][c].
 hipError_t launch_mmq_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,
                            int32_t* dots, hipStream_t stream);

@@ -152,6 +152,18 @@ int q8_quantize_rows(const float* x, int64_t n, int64_t k, int8_t* q, uint32_t* 
     return hip_status(mmq::launch_q8_quantize(x, n * (k / 32), q, ds, stream));
 }
 
+int q8_quantize_silu_mul(const float* gate, const float* up, int64_t n, int64_t k, int8_t* q,
+                         uint32_t* ds, hipStream_t stream) {
+    if (n < 0 || k <= 0 || (k & 31) != 0) return MMQ_ERR_SHAPE;
+    if (n > kMaxDim || k > kMaxK || n * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (n == 0) return MMQ_OK;
+    if (!gate || !up || !q || !ds) return MMQ_ERR_NULL;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(q) || !aligned16(ds)) return MMQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != MMQ_OK) return dev;
+    return hip_status(mmq::launch_q8_quantize_silu_mul(gate, up, n * (k / 32), q, ds, stream));
+}
+
 int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
                int64_t n, int32_t* dots, hipStream_t stream) {
     (void)ds;  // not read: the block dots do not depend on the scales

@@ -12,6 +12,10 @@
 // 512 contiguous bytes of q; the quantizer is HBM-bound (4 B read + 1.125 B
 // written per element).
 //
+// The same kernel quantizes h = SiLU(gate) * up without writing h (the fused
+// input of an FFN's down projection): the block's values are computed from
+// the two inputs as they are loaded.
+//
 // Numerics: x/da is the IEEE fp32 division (hipcc's default correctly
 // rounded divide; never built with fast-math), roundf rounds ties away from
 // zero, and v_cvt_f16_f32 rounds to nearest even keeping subnormals.
@@ -38,8 +42,46 @@ __device__ __forceinline__ int quad_sum(int v) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void q8_quantize_kernel(const float* __restrict__ x,
-                                                          int64_t nblocks,
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The 8 values of lane `part` of block `blk`: the activations themselves.
+struct PlainSrc {
+    const float* x;
+    __device__ __forceinline__ void load(int64_t blk, int part, float (&v)[8]) const {
+        const v4f* src = reinterpret_cast<const v4f*>(x + blk * 32 + part * 8);
+        const v4f lo = __builtin_nontemporal_load(src);      // read once: do not keep in cache
+        const v4f hi = __builtin_nontemporal_load(src + 1);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+};
+
+// h = SiLU(g) * u of the FFN's gate and up outputs, as the float32 rounding
+// of the float64 value g*u / (1 + exp(-g)): g*u is exact in float64, then an
+// IEEE add, an IEEE divide and the round to float32 (one function, exp, is
+// the device library's), so h is the correctly rounded value but for a
+// float64 ulp of exp.
+struct SiluMulSrc {
+    const float* g;
+    const float* u;
+    __device__ __forceinline__ void load(int64_t blk, int part, float (&v)[8]) const {
+        const v4f* gs = reinterpret_cast<const v4f*>(g + blk * 32 + part * 8);
+        const v4f* us = reinterpret_cast<const v4f*>(u + blk * 32 + part * 8);
+        const v4f g0 = __builtin_nontemporal_load(gs), g1 = __builtin_nontemporal_load(gs + 1);
+        const v4f u0 = __builtin_nontemporal_load(us), u1 = __builtin_nontemporal_load(us + 1);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double gd = (double)gv[i];
+            const double den = 1.0 + exp(-gd);
+            v[i] = (float)(gd * (double)uv[i] / den);
+        }
+    }
+};
+
+template <class Src>
+__global__ __launch_bounds__(256) void q8_quantize_kernel(Src src, int64_t nblocks,
                                                           int8_t* __restrict__ q,
                                                           uint32_t* __restrict__ ds) {
     const int64_t lane_id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -47,11 +89,8 @@ __global__ __launch_bounds__(256) void q8_quantize_kernel(const float* __restric
     if (blk >= nblocks) return;
     const int part = threadIdx.x & 3;
 
-    typedef float v4f __attribute__((ext_vector_type(4)));
-    const v4f* src = reinterpret_cast<const v4f*>(x + blk * 32 + part * 8);
-    const v4f lo = __builtin_nontemporal_load(src);      // read once: do not keep in cache
-    const v4f hi = __builtin_nontemporal_load(src + 1);
-    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    float v[8];
+    src.load(blk, part, v);
 
     float amax = 0.0f;
 #pragma unroll
@@ -80,14 +119,24 @@ __global__ __launch_bounds__(256) void q8_quantize_kernel(const float* __restric
     if (part == 0) ds[blk] = word;
 }
 
+template <class Src>
+hipError_t launch(Src src, int64_t nblocks, int8_t* q, uint32_t* ds, hipStream_t stream) {
+    const int64_t lanes = nblocks * 4;
+    const unsigned grid = (unsigned)((lanes + 255) / 256);
+    hipLaunchKernelGGL((q8_quantize_kernel<Src>), dim3(grid), dim3(256), 0, stream, src, nblocks, q, ds);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
                               hipStream_t stream) {
-    const int64_t lanes = nblocks * 4;
-    const unsigned grid = (unsigned)((lanes + 255) / 256);
-    void* args[] = {(void*)&x, (void*)&nblocks, (void*)&q, (void*)&ds};
-    return hipLaunchKernel((const void*)q8_quantize_kernel, dim3(grid), dim3(256), args, 0, stream);
+    return launch(PlainSrc{x}, nblocks, q, ds, stream);
+}
+
+hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,
+                                       uint32_t* ds, hipStream_t stream) {
+    return launch(SiluMulSrc{g, u}, nblocks, q, ds, stream);
 }
 
 }  // namespace mmq

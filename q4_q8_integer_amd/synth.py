@@ -236,6 +236,17 @@ def ffn_inputs(which: str, n: int | None = None):
     raise ValueError(which)
 
 
+def ffn_gate_up_outputs(n: int | None = None):
+    """The FFN's gate and up projection outputs [n x 11008] (the fused
+    SiLU-gate quantizer's inputs): gate ~ 2 N(0,1) (so the SiLU sees both its
+    linear and its saturated range), up ~ N(0,1), float32, streams (2, 5) and
+    (2, 6)."""
+    n = FFN["n"] if n is None else n
+    g = (rng_for(2, 5).standard_normal((n, FFN["d_ff"]), dtype=np.float32) * np.float32(2.0))
+    u = rng_for(2, 6).standard_normal((n, FFN["d_ff"]), dtype=np.float32)
+    return g, u
+
+
 def layer_weights(name: str) -> Q4KFields:
     """One projection of the full 7B layer set (tensor ids 0..6 in LAYER_MATS order)."""
     for tid, (nm, m, k) in enumerate(LAYER_MATS):

@@ -64,6 +64,14 @@ def test_status_strings(lib):
 ])
 def test_quantize_validation(lib, args, want):
     assert lib.q8_quantize_rows(*args, None) == want
+    # the fused SiLU-gate quantizer checks the same, with `up` beside `gate`
+    x, n, k, q, ds = args
+    assert lib.q8_quantize_silu_mul(x, A, n, k, q, ds, None) == want
+
+
+def test_silu_quantize_checks_up(lib):
+    assert lib.q8_quantize_silu_mul(A, 0, 4, 64, A, A, None) == NULL
+    assert lib.q8_quantize_silu_mul(A, MIS, 4, 64, A, A, None) == ALIGN
 
 
 MMQ_CALLS = ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
@@ -104,6 +112,7 @@ def test_valid_arguments_without_device_report_device_error(lib):
     # Arguments pass validation, so the next step is the device check, which
     # fails here before anything could be launched on the fake pointers.
     assert lib.q8_quantize_rows(A, 4, 64, A, A, None) == DEVICE
+    assert lib.q8_quantize_silu_mul(A, A, 4, 64, A, A, None) == DEVICE
     assert lib.mmq_q4k_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4k_q8(A, 8, 512, A, 0, 3, A, None) == DEVICE
