@@ -255,6 +255,46 @@ int oracle_blockdots(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,
     return 0;
 }
 
+/* ------------------------------------------------------- load-time repack */
+/* q4_K weights re-laid out for the few-token path (the pages' "load-time B
+ * pre-expansion" and scale "predecode" rounds name the step, not a format;
+ * this layout is the library's): rows in tiles of 16, one 2368-byte record
+ * per (tile, super-block), records in tile-major order.  Record:
+ *   [0, 64)      dword r:          d | dmin << 16 (binary16 bits) of row r
+ *   [64, 320)    dword 16p + r:    sc[2p] | sc[2p+1] << 8 | m[2p] << 16 | m[2p+1] << 24
+ *   [320, 2368)  bytes 320 + 512p + 256h + 16r + i:  qs byte 32p + 16h + i of row r
+ * for pair p < 4, half h < 2, row r < 16, i < 16.  Rows past m are zero
+ * (d = dmin = 0: they contribute nothing).  wr holds ceil(m/16)*(k/256)*2368
+ * bytes. */
+int oracle_q4k_repack(const uint8_t *w, int64_t m, int64_t k, uint8_t *wr)
+{
+    if (m < 0 || k < 0 || k % 256)
+        return -1;
+    const int64_t S = k / 256, tiles = (m + 15) / 16;
+    memset(wr, 0, (size_t)(tiles * S * 2368));
+    for (int64_t o = 0; o < m; o++) {
+        const int64_t t = o / 16, r = o % 16;
+        for (int64_t b = 0; b < S; b++) {
+            const uint8_t *blk = w + (o * S + b) * 144;
+            uint8_t *rec = wr + (t * S + b) * 2368;
+            double dd, dm;
+            int sc[8], mn[8], q4[256];
+            decode_block(blk, &dd, &dm, sc, mn, q4);
+            memcpy(rec + 4 * r, blk, 4);   /* d, dmin as stored */
+            for (int p = 0; p < 4; p++) {
+                uint8_t *sw = rec + 64 + 4 * (16 * p + r);
+                sw[0] = (uint8_t)sc[2 * p];
+                sw[1] = (uint8_t)sc[2 * p + 1];
+                sw[2] = (uint8_t)mn[2 * p];
+                sw[3] = (uint8_t)mn[2 * p + 1];
+                for (int h = 0; h < 2; h++)
+                    memcpy(rec + 320 + 512 * p + 256 * h + 16 * r, blk + 16 + 32 * p + 16 * h, 16);
+            }
+        }
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------------- output */
 /* out[t][o] in float64, chunk order, from the two-term fold. */
 int oracle_out_f64(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,

@@ -33,6 +33,8 @@ def _declare(lib):
     lib.oracle_q4k_unpack.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]
     lib.oracle_blockdots.argtypes = [c_p, c_i64, c_i64, c_p, c_i64, c_p]
     lib.oracle_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
+    lib.oracle_q4k_repack.argtypes = [c_p, c_i64, c_i64, c_p]
+    lib.oracle_q4k_repack.restype = ctypes.c_int
     lib.oracle_silu_mul.argtypes = [c_p, c_p, c_i64, c_p]
     lib.oracle_silu_mul.restype = None
     lib.oracle_q8_quantize_silu_mul.argtypes = [c_p, c_p, c_i64, c_i64, c_p, c_p]
@@ -155,6 +157,15 @@ def out_f64(w: np.ndarray, m: int, k: int, q: np.ndarray, ds: np.ndarray,
     out = np.empty((n, m), dtype=np.float64)
     _check(lib.oracle_out_f64(_ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out)), "out_f64")
     return out
+
+
+def q4k_repack(w: np.ndarray, m: int, k: int, lib=None) -> np.ndarray:
+    """The few-token record layout of a q4_K matrix: uint8 [ceil(m/16)*(k/256)*2368]."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    wr = np.empty(((m + 15) // 16) * (k // 256) * 2368, dtype=np.uint8)
+    _check(lib.oracle_q4k_repack(_ptr(w), m, k, _ptr(wr)), "q4k_repack")
+    return wr
 
 
 def q6k_unpack(w: np.ndarray, m: int, k: int, lib=None):

@@ -501,6 +501,45 @@ def pin_quantize_silu_mul(lib):
     assert np.array_equal(q[same], rq) and np.array_equal(ds[same], rds)
 
 
+# -------------------------------------------------------- load-time repack
+def expected_repack(f: synth.Q4KFields) -> np.ndarray:
+    """The record layout built with numpy from the generator's unpacked fields
+    (never from the oracle's decoder or the packer's scale packing)."""
+    m, k = f.q.shape
+    S, T = k // 256, (m + 15) // 16
+    rec = np.zeros((T, S, 2368), dtype=np.uint8)
+    mp = T * 16
+    d = np.zeros((mp, S), dtype=np.uint16)
+    dm = np.zeros((mp, S), dtype=np.uint16)
+    d[:m] = f.d.view(np.uint16)
+    dm[:m] = f.dmin.view(np.uint16)
+    hdr = (d.astype(np.uint32) | (dm.astype(np.uint32) << 16)).reshape(T, 16, S).transpose(0, 2, 1)
+    rec[:, :, 0:64] = hdr.copy().view(np.uint8).reshape(T, S, 64)
+    sc = np.zeros((mp, S, 8), dtype=np.uint8)
+    mn = np.zeros((mp, S, 8), dtype=np.uint8)
+    sc[:m] = f.sc.reshape(m, S, 8)
+    mn[:m] = f.mn.reshape(m, S, 8)
+    sw = np.stack([sc[:, :, 0::2], sc[:, :, 1::2], mn[:, :, 0::2], mn[:, :, 1::2]], axis=-1)  # [row, S, p, 4]
+    sw = sw.reshape(T, 16, S, 4, 4).transpose(0, 2, 3, 1, 4)                                 # [T, S, p, r, 4]
+    rec[:, :, 64:320] = sw.reshape(T, S, 256)
+    q = np.zeros((mp, k), dtype=np.uint8)
+    q[:m] = f.q
+    q = q.reshape(T, 16, S, 4, 2, 32)                  # [T, r, S, pair p, chunk in pair, i]
+    qs = q[:, :, :, :, 0, :] | (q[:, :, :, :, 1, :] << 4)   # qs byte 32p + i: [T, r, S, p, 32]
+    qs = qs.reshape(T, 16, S, 4, 2, 16).transpose(0, 2, 3, 4, 1, 5)   # [T, S, p, h, r, 16]
+    rec[:, :, 320:] = qs.reshape(T, S, 2048)
+    return rec.reshape(-1)
+
+
+def pin_q4k_repack(lib):
+    """The oracle's repack equals the record layout built from the fields,
+    on row counts that fill the last 16-row tile and ones that do not."""
+    for seed, (m, k) in enumerate([(16, 256), (5, 512), (33, 768), (48, 256)]):
+        f = synth.random_fields(70 + seed, m, k)
+        got = oracle.q4k_repack(synth.pack_q4k(f), m, k, lib=lib)
+        assert np.array_equal(got, expected_repack(f)), "repack differs (m=%d k=%d)" % (m, k)
+
+
 ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundtrip,
             pin_q8_golden, pin_q8_invariants, pin_q8_zero_block, pin_dots_bruteforce,
             pin_dots_closed_forms, pin_out_bruteforce, pin_out_special_cases,
@@ -508,4 +547,4 @@ ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundt
             pin_q6k_golden_block, pin_q6k_roundtrip, pin_q6k_dots_bruteforce,
             pin_q6k_dots_closed_forms, pin_q6k_out_bruteforce, pin_q6k_out_special_cases,
             pin_q6k_one_superblock, pin_silu_mul_float64, pin_silu_mul_closed_forms,
-            pin_quantize_silu_mul]
+            pin_quantize_silu_mul, pin_q4k_repack]

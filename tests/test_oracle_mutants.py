@@ -47,6 +47,10 @@ MUTANTS = [
     ("silu_without_up", "h[i] = (float)(gd * (double)u[i] / s);", "h[i] = (float)(gd / s);"),
     ("sigmoid_sign", "const double s = 1.0 + exp(-gd);", "const double s = 1.0 + exp(gd);"),
     ("silu_in_float32", "const double s = 1.0 + exp(-gd);", "const double s = (float)(1.0f + expf((float)-gd));"),
+    ("repack_scales_swapped", "sw[2] = (uint8_t)mn[2 * p];\n                sw[3] = (uint8_t)mn[2 * p + 1];",
+     "sw[2] = (uint8_t)mn[2 * p + 1];\n                sw[3] = (uint8_t)mn[2 * p];"),
+    ("repack_halves_swapped", "memcpy(rec + 320 + 512 * p + 256 * h + 16 * r, blk + 16 + 32 * p + 16 * h, 16);",
+     "memcpy(rec + 320 + 512 * p + 256 * (1 - h) + 16 * r, blk + 16 + 32 * p + 16 * h, 16);"),
     ("quantize_gate_not_h", "rc |= oracle_q8_quantize(row, 1, k,", "rc |= oracle_q8_quantize(g + t * k, 1, k,"),
 ]
 
