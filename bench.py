@@ -65,6 +65,11 @@ def build_workload(name: str):
         return ({"workload": "weight-bound q6_K W[%dx%d] at N=%d (10%% of scale groups sc=0)"
                              % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
                 {"x": synth.q6k_activation("wide_in", n)}, [("wide_in", f, "x")])
+    if name.startswith("r_wide_in") or name.startswith("r_wide_out"):
+        desc, inputs, mats = build_workload(name[2:])
+        desc = dict(desc, repacked=True,
+                    workload=desc["workload"] + ", weights repacked at load time (q4k_repack)")
+        return desc, inputs, mats
     if name.startswith("wide_in") or name.startswith("wide_out"):
         wname, n = name.rsplit("_n", 1)
         n = int(n)
@@ -261,6 +266,8 @@ def main():
         xs = {s: torch.from_numpy(x).to(dev) for s, x in inputs.items()}
         ws = [(lbl, torch.from_numpy(weight_format(f)[0](f)).to(dev), f.m, f.k, src)
               for lbl, f, src in mats]
+        if desc.get("repacked"):   # load-time step, outside the timed region
+            ws = [(lbl, binding.repack(w, m, k), m, k, src) for lbl, w, m, k, src in ws]
         qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
                   torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
               for s, x in xs.items()}
@@ -273,12 +280,18 @@ def main():
     n_tok = max(x.shape[0] for x in inputs.values())
     mmq_ops = sum(2.0 * inputs[src].shape[0] * f.m * f.k for _, f, src in mats)
     out_bytes = 2.0 if args.f16_out else 4.0
-    mmq_alg_bytes = sum(weight_format(f)[1] * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
+    wbytes = (lambda f: 2368.0 / 4096.0) if desc.get("repacked") else (lambda f: weight_format(f)[1])
+    mmq_alg_bytes = sum(wbytes(f) * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
                         + out_bytes * inputs[src].shape[0] * f.m for _, f, src in mats)
     suffix = "_f16out" if args.f16_out else "_fp32out"
     names = sorted({weight_format(f)[2] + suffix for _, f, _ in mats})
+    if desc.get("repacked"):
+        if args.f16_out:
+            raise SystemExit("the repacked layout has a float32 entry point only")
+        names = ["mmq_q4kr_q8_fp32out"]
     mmq_name = "+".join(names)
-    calls = [getattr(binding, weight_format(f)[2] + suffix) for _, f, _ in mats]
+    calls = [getattr(binding, names[0] if desc.get("repacked") else weight_format(f)[2] + suffix)
+             for _, f, _ in mats]
 
     def step(i):
         xs, ws, qs, outs = sets[i % len(sets)]

@@ -188,6 +188,36 @@ int mmq_q6k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
 int mmq_q6k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
                       const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
 
+/*
+ * q4k_repack - load-time re-layout of q4_K weights for the few-token path.
+ * (The pages name a "load-time B pre-expansion" round and a scale
+ * "predecode" round, r18 and r35 in the r17 and r31 pages' notes; the
+ * layout is this library's.)
+ *
+ *   w  : q4_K super-blocks of W [m][k] (as for mmq_q4k_q8), k % 256 == 0.
+ *   wr : ceil(m/16) * (k/256) * 2368 bytes (out), 16-byte aligned.  Rows in
+ *        tiles of 16, one 2368-byte record per (tile, super-block), records
+ *        tile-major.  Record: [0, 64) dword r = d | dmin << 16 of row r;
+ *        [64, 320) dword 16p + r = sc[2p] | sc[2p+1] << 8 | m[2p] << 16 |
+ *        m[2p+1] << 24 (the 6-bit fields as bytes); [320, 2368) the 16 bytes
+ *        at 320 + 512p + 256h + 16r are qs bytes 32p + 16h .. +15 of row r
+ *        (p < 4, h < 2, r < 16).  Rows past m are zero.
+ * Pure byte work: the same values, 148 bytes per row and super-block
+ * against 144.  Errors as for mmq_q4k_q8 (m == 0 is an empty call).
+ */
+int q4k_repack(const void *w, int64_t m, int64_t k, void *wr, hipStream_t stream);
+
+/*
+ * mmq_q4kr_q8_fp32out - mmq_q4k_q8_fp32out on repacked weights (wr from
+ * q4k_repack of the same m, k).  For n <= 8 it runs the vector-ALU dot4
+ * kernel with the same arithmetic, in the same order, as
+ * mmq_q4k_q8_fp32out's kernel for that n, so the two results are equal bit
+ * for bit; more tokens run as slices of 8, each reading the weights again.
+ * Other arguments, errors and empty calls as for mmq_q4k_q8_fp32out.
+ */
+int mmq_q4kr_q8_fp32out(const void *wr, int64_t m, int64_t k, const int8_t *q,
+                        const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);
 

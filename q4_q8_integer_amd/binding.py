@@ -15,9 +15,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-           "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_status_string")
+           "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "q4k_repack",
+           "mmq_q4kr_q8_fp32out", "mmq_status_string")
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out")
+              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out")
 _lib = None
 
 
@@ -43,6 +44,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_quantize_rows.restype = ctypes.c_int
     lib.q8_quantize_silu_mul.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_silu_mul.restype = ctypes.c_int
+    lib.q4k_repack.argtypes = [vp, i64, i64, vp, vp]
+    lib.q4k_repack.restype = ctypes.c_int
     for name in _MMQ_CALLS:
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
@@ -102,6 +105,15 @@ def mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out):
 def mmq_q4k_q8_f16out(w, m, k, q, ds, n, out):
     _check("mmq_q4k_q8_f16out", load_library().mmq_q4k_q8_f16out(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
+
+
+def q4k_repack(w, m, k, wr):
+    _check("q4k_repack", load_library().q4k_repack(_ptr(w), m, k, _ptr(wr), _stream()))
+
+
+def mmq_q4kr_q8_fp32out(wr, m, k, q, ds, n, out):
+    _check("mmq_q4kr_q8_fp32out", load_library().mmq_q4kr_q8_fp32out(
+        _ptr(wr), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q6k_q8(w, m, k, q, ds, n, dots):
@@ -216,4 +228,31 @@ def q6k_fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor,
     else:
         _need(out, torch.float16, "out")
     mmq_q6k_q8_f16out(w, m, k, q, ds, n, out)
+    return out
+
+
+def repack_bytes(m: int, k: int) -> int:
+    """Size of q4k_repack's output for an m x k matrix."""
+    return (m + 15) // 16 * (k // 256) * 2368
+
+
+def repack(w: torch.Tensor, m: int, k: int):
+    """Load-time repack of q4_K weights: uint8 tensor of repack_bytes(m, k)."""
+    _need(w, torch.uint8, "w")
+    wr = torch.empty(repack_bytes(m, k), dtype=torch.uint8, device=w.device)
+    q4k_repack(w, m, k, wr)
+    return wr
+
+
+def fp32_repacked(wr: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """mmq_q4k_q8_fp32out on repacked weights: float32 [n, m]."""
+    _need(wr, torch.uint8, "wr")
+    _need(q, torch.int8, "q")
+    _need(ds, torch.int32, "ds")
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, torch.float32, "out")
+    mmq_q4kr_q8_fp32out(wr, m, k, q, ds, n, out)
     return out

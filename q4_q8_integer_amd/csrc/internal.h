@@ -9,6 +9,8 @@ namespace mmq {
 
 // Bytes of one q4_K super-block (256 weights).
 constexpr int kBlockBytes = 144;
+// Bytes of one record (16 rows x one super-block) of the repacked q4_K layout.
+constexpr int kRepackRecordBytes = 2368;
 
 hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
                               hipStream_t stream);
@@ -71,6 +73,13 @@ hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
                                 const uint32_t* ds, int n, void* out, bool half_out,
                                 hipStream_t stream);
 constexpr int kGemvMaxN = 8;
+
+// Load-time repack of q4_K into 16-row records (repack.hip), and the dot4
+// kernel on that layout (1 <= n <= kGemvMaxN; w is the repacked buffer).
+hipError_t launch_q4k_repack(const uint8_t* w, int m, int k, uint8_t* wr, hipStream_t stream);
+hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
+                                         const uint32_t* ds, int n, void* out, bool half_out,
+                                         hipStream_t stream);
 
 // Two-term fold, out[t][o], for n <= kPairMaxN tokens: one int8 MFMA per
 // chunk pair, 8 tokens x 16 rows, weights streamed once.

@@ -212,6 +212,44 @@ int mmq_q6k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
     return q6k_fold_entry(w, m, k, q, ds, n, out, true, stream);
 }
 
+int q4k_repack(const void* w, int64_t m, int64_t k, void* wr, hipStream_t stream) {
+    if (m < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
+    if (m > kMaxDim || k > kMaxK) return MMQ_ERR_OVERFLOW;
+    if (m * (k / 256) * 144 >= kMaxElems || (m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems)
+        return MMQ_ERR_OVERFLOW;
+    if (m == 0) return MMQ_OK;
+    if (!w || !wr) return MMQ_ERR_NULL;
+    if (!aligned16(w) || !aligned16(wr)) return MMQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != MMQ_OK) return dev;
+    return hip_status(mmq::launch_q4k_repack(static_cast<const uint8_t*>(w), (int)m, (int)k,
+                                             static_cast<uint8_t*>(wr), stream));
+}
+
+int mmq_q4kr_q8_fp32out(const void* wr, int64_t m, int64_t k, const int8_t* q,
+                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(wr, m, k, q, n, out, &empty);
+    if (rc != MMQ_OK || empty) return rc;
+    if ((m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    // Up to 8 tokens per launch; more tokens run as slices of 8 (each reads
+    // the weights again: this layout serves the few-token path).  Slice
+    // starts stay 16-byte aligned: 8 rows of q, ds and out are 8k, k/4 and
+    // 32m bytes.
+    for (int64_t t0 = 0; t0 < n; t0 += mmq::kGemvMaxN) {
+        const int nn = (int)(n - t0 < mmq::kGemvMaxN ? n - t0 : mmq::kGemvMaxN);
+        rc = hip_status(mmq::launch_mmq_fp32_gemv_repacked(
+            static_cast<const uint8_t*>(wr), (int)m, (int)k, q + t0 * k, ds + t0 * (k / 32), nn,
+            out + t0 * m, false, stream));
+        if (rc != MMQ_OK) return rc;
+    }
+    return MMQ_OK;
+}
+
 const char* mmq_status_string(int status) {
     switch (status) {
         case MMQ_OK: return "MMQ_OK";

@@ -173,24 +173,33 @@ __device__ __forceinline__ void fold_two_tokens(float& acca, float& accb, float 
 // One super-block J of the step for every token.  A slot past the wave's
 // last super-block (live false) runs with d = dmin = 0 and adds exactly 0:
 // no branch, so the compiler keeps all of the step's loads ahead of the math.
-template <int N, int J>
+template <int N, int J, bool R>
 __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb, int p, bool live,
                                         const v4u* tq, const float* tda, const float* tdass,
                                         float* acc) {
     const float d = live ? half_lo(h[0]) : 0.0f, dmin = live ? half_lo(h[0] >> 16) : 0.0f;
+    uint32_t sc0, sc1, m0, m1;
+    if constexpr (R) {
+        // repacked layout: the four scales as bytes of one dword
+        sc0 = h[1] & 0xFF;
+        sc1 = (h[1] >> 8) & 0xFF;
+        m0 = (h[1] >> 16) & 0xFF;
+        m1 = h[1] >> 24;
+    } else {
     // 6-bit (sc, m) of chunks 2p and 2p+1 (GGUF k-quant scale packing).
     // Chunks 0-3: low 6 bits of scale bytes j (sc) and j+4 (m).  Chunks 4-7:
     // a nibble of byte j+4 (low: sc, high: m) topped with the 2 high bits of
     // byte j-4 (sc) or j (m).  Both cases as a 4-bit field plus a 2-bit
     // field, so no lane branches.
-    const bool lo4 = p < 2;
-    const int sh = 16 * (p & 1);
-    const uint32_t xs = lo4 ? h[1] : h[3], xm = lo4 ? h[2] : h[3];
-    const int oh = lo4 ? 4 : 6, om = lo4 ? 0 : 4;
-    const uint32_t sc0 = __builtin_amdgcn_ubfe(xs, sh, 4) | (__builtin_amdgcn_ubfe(h[1], sh + oh, 2) << 4);
-    const uint32_t sc1 = __builtin_amdgcn_ubfe(xs, sh + 8, 4) | (__builtin_amdgcn_ubfe(h[1], sh + 8 + oh, 2) << 4);
-    const uint32_t m0 = __builtin_amdgcn_ubfe(xm, sh + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + oh, 2) << 4);
-    const uint32_t m1 = __builtin_amdgcn_ubfe(xm, sh + 8 + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + 8 + oh, 2) << 4);
+        const bool lo4 = p < 2;
+        const int sh = 16 * (p & 1);
+        const uint32_t xs = lo4 ? h[1] : h[3], xm = lo4 ? h[2] : h[3];
+        const int oh = lo4 ? 4 : 6, om = lo4 ? 0 : 4;
+        sc0 = __builtin_amdgcn_ubfe(xs, sh, 4) | (__builtin_amdgcn_ubfe(h[1], sh + oh, 2) << 4);
+        sc1 = __builtin_amdgcn_ubfe(xs, sh + 8, 4) | (__builtin_amdgcn_ubfe(h[1], sh + 8 + oh, 2) << 4);
+        m0 = __builtin_amdgcn_ubfe(xm, sh + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + oh, 2) << 4);
+        m1 = __builtin_amdgcn_ubfe(xm, sh + 8 + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + 8 + oh, 2) << 4);
+    }
     const float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1;
     const float dmm0 = -(dmin * (float)m0), dmm1 = -(dmin * (float)m1);
     int lo[8], hi[8];
@@ -226,8 +235,9 @@ struct Step {
 
 // Issue the loads of the step starting at super-block s.  Every load is
 // unconditional: slots past the wave's last super-block re-read that block
-// (and are computed with live = false).
-template <int N, int SW>
+// (and are computed with live = false).  wrow is the lane's row (GGUF
+// layout) or the workgroup's 16-row tile of records (repacked layout, R).
+template <int N, int SW, bool R>
 __device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
                                           const int8_t* __restrict__ q,
                                           const uint32_t* __restrict__ ds, int K, int C, int s,
@@ -243,14 +253,22 @@ __device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
     for (int t = 0; t < N; ++t) st.tw[t] = ds[(int64_t)t * C + woff];
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
-        const uint8_t* b = wrow + (int64_t)min(s + j, last) * kBlockBytes;
-        st.hdr[j] = ld16(b);
-        st.qa[j] = ld16(b + 16 + 32 * p);
-        st.qb[j] = ld16(b + 32 + 32 * p);
+        if constexpr (R) {
+            const uint8_t* b = wrow + (int64_t)min(s + j, last) * kRepackRecordBytes;
+            st.hdr[j] = v4u{*reinterpret_cast<const uint32_t*>(b + 4 * r),
+                            *reinterpret_cast<const uint32_t*>(b + 64 + 4 * (16 * p + r)), 0u, 0u};
+            st.qa[j] = ld16(b + 320 + 512 * p + 16 * r);
+            st.qb[j] = ld16(b + 320 + 512 * p + 256 + 16 * r);
+        } else {
+            const uint8_t* b = wrow + (int64_t)min(s + j, last) * kBlockBytes;
+            st.hdr[j] = ld16(b);
+            st.qa[j] = ld16(b + 16 + 32 * p);
+            st.qb[j] = ld16(b + 32 + 32 * p);
+        }
     }
 }
 
-template <int N, int SW>
+template <int N, int SW, bool R>
 __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int p, float* acc) {
     float tda[N], tdass[N];
 #pragma unroll
@@ -258,13 +276,13 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int 
         tda[t] = half_lo(st.tw[t]);
         tdass[t] = tda[t] * (float)(int16_t)(uint16_t)(st.tw[t] >> 16);
     }
-    gemv_sb<N, 0>(st.hdr[0], st.qa[0], st.qb[0], p, ns > 0, st.tq, tda, tdass, acc);
-    if constexpr (SW > 1) gemv_sb<N, 1>(st.hdr[1], st.qa[1], st.qb[1], p, ns > 1, st.tq, tda, tdass, acc);
-    if constexpr (SW > 2) gemv_sb<N, 2>(st.hdr[2], st.qa[2], st.qb[2], p, ns > 2, st.tq, tda, tdass, acc);
-    if constexpr (SW > 3) gemv_sb<N, 3>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
+    gemv_sb<N, 0, R>(st.hdr[0], st.qa[0], st.qb[0], p, ns > 0, st.tq, tda, tdass, acc);
+    if constexpr (SW > 1) gemv_sb<N, 1, R>(st.hdr[1], st.qa[1], st.qb[1], p, ns > 1, st.tq, tda, tdass, acc);
+    if constexpr (SW > 2) gemv_sb<N, 2, R>(st.hdr[2], st.qa[2], st.qb[2], p, ns > 2, st.tq, tda, tdass, acc);
+    if constexpr (SW > 3) gemv_sb<N, 3, R>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
 }
 
-template <int N, int SW, bool H>
+template <int N, int SW, bool H, bool R>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
                                                                   const int8_t* __restrict__ q,
                                                                   const uint32_t* __restrict__ ds,
@@ -279,7 +297,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     const int row0 = blockIdx.x * 16;
     const int S = K >> 8, C = K >> 5;
     const int sb0 = (int)((int64_t)S * wv / W), sb1 = (int)((int64_t)S * (wv + 1) / W);
-    const uint8_t* wrow = w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
+    const uint8_t* wrow = R ? w + (int64_t)blockIdx.x * S * kRepackRecordBytes
+                            : w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
 
     float acc[N];
 #pragma unroll
@@ -292,9 +311,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     const int last = sb1 - 1;
     for (int s = sb0; s < sb1; s += SW) {
         Step<N, SW> A;
-        load_step<N, SW>(A, wrow, q, ds, K, C, s, last, p, r);
+        load_step<N, SW, R>(A, wrow, q, ds, K, C, s, last, p, r);
         __builtin_amdgcn_sched_barrier(0);
-        compute_step<N, SW>(A, sb1 - s, p, acc);
+        compute_step<N, SW, R>(A, sb1 - s, p, acc);
     }
 
     // the four chunk-pair lanes of a row (every lane ends with the same
@@ -314,7 +333,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     }
 }
 
-template <int N>
+template <int N, bool R>
 hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                     void* out, bool half_out, hipStream_t stream) {
     const int S = k / 256;
@@ -329,12 +348,28 @@ hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint3
     waves = waves > S ? S : waves;
     constexpr int SW = 4;
     if (half_out)
-        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), 0, stream,
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, true, R>), dim3(rows), dim3(64 * waves), 0, stream,
                            w, q, ds, m, k, out);
     else
-        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), 0, stream,
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, false, R>), dim3(rows), dim3(64 * waves), 0, stream,
                            w, q, ds, m, k, out);
     return hipGetLastError();
+}
+
+template <bool R>
+hipError_t launch_any(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
+                      void* out, bool half_out, hipStream_t stream) {
+    switch (n) {
+        case 1: return launch_n<1, R>(w, m, k, q, ds, out, half_out, stream);
+        case 2: return launch_n<2, R>(w, m, k, q, ds, out, half_out, stream);
+        case 3: return launch_n<3, R>(w, m, k, q, ds, out, half_out, stream);
+        case 4: return launch_n<4, R>(w, m, k, q, ds, out, half_out, stream);
+        case 5: return launch_n<5, R>(w, m, k, q, ds, out, half_out, stream);
+        case 6: return launch_n<6, R>(w, m, k, q, ds, out, half_out, stream);
+        case 7: return launch_n<7, R>(w, m, k, q, ds, out, half_out, stream);
+        case 8: return launch_n<8, R>(w, m, k, q, ds, out, half_out, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -342,17 +377,13 @@ hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint3
 hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
                                 const uint32_t* ds, int n, void* out, bool half_out,
                                 hipStream_t stream) {
-    switch (n) {
-        case 1: return launch_n<1>(w, m, k, q, ds, out, half_out, stream);
-        case 2: return launch_n<2>(w, m, k, q, ds, out, half_out, stream);
-        case 3: return launch_n<3>(w, m, k, q, ds, out, half_out, stream);
-        case 4: return launch_n<4>(w, m, k, q, ds, out, half_out, stream);
-        case 5: return launch_n<5>(w, m, k, q, ds, out, half_out, stream);
-        case 6: return launch_n<6>(w, m, k, q, ds, out, half_out, stream);
-        case 7: return launch_n<7>(w, m, k, q, ds, out, half_out, stream);
-        case 8: return launch_n<8>(w, m, k, q, ds, out, half_out, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_any<false>(w, m, k, q, ds, n, out, half_out, stream);
+}
+
+hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
+                                         const uint32_t* ds, int n, void* out, bool half_out,
+                                         hipStream_t stream) {
+    return launch_any<true>(wr, m, k, q, ds, n, out, half_out, stream);
 }
 
 }  // namespace mmq

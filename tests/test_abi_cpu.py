@@ -75,7 +75,7 @@ def test_silu_quantize_checks_up(lib):
 
 
 MMQ_CALLS = ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-             "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out"]
+             "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out"]
 
 
 @pytest.mark.parametrize("fn", MMQ_CALLS)
@@ -101,7 +101,7 @@ def test_mmq_validation(lib, fn, args, want):
 
 
 @pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-                                "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out"])
+                                "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out"])
 def test_fold_needs_scales(lib, fn):
     assert getattr(lib, fn)(A, 8, 512, A, 0, 3, A, None) == NULL
     assert getattr(lib, fn)(A, 8, 512, A, MIS, 3, A, None) == ALIGN
@@ -119,6 +119,24 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.mmq_q6k_q8(A, 8, 512, A, 0, 3, A, None) == DEVICE
     assert lib.mmq_q6k_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q6k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.q4k_repack(A, 8, 512, A, None) == DEVICE
+    assert lib.mmq_q4kr_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+
+
+@pytest.mark.parametrize("args,want", [
+    ((A, -1, 512, A), SHAPE),
+    ((A, 8, 0, A), SHAPE),
+    ((A, 8, 288, A), SHAPE),
+    ((A, 8, 1 << 25, A), OVERFLOW),
+    ((A, 1 << 31, 512, A), OVERFLOW),
+    ((0, 8, 512, A), NULL),
+    ((A, 8, 512, 0), NULL),
+    ((MIS, 8, 512, A), ALIGN),
+    ((A, 8, 512, MIS), ALIGN),
+    ((0, 0, 512, 0), OK),
+])
+def test_repack_validation(lib, args, want):
+    assert lib.q4k_repack(*args, None) == want
 
 
 def test_q6k_weight_bytes_limit(lib):

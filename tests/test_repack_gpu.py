@@ -1,0 +1,61 @@
+"""The load-time repack (q4k_repack) and the MMQ on repacked weights
+(mmq_q4kr_q8_fp32out) on the GPU: repacked bytes equal the oracle's bit for
+bit; for n <= 8 the result equals mmq_q4k_q8_fp32out's bit for bit (same
+kernel arithmetic on the other layout), and meets the float32 bar against the
+oracle; above 8 tokens (slices of 8) it meets the bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import check_fp32, gpu_quantize, note, to_dev
+from q4_q8_integer_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("m,k", [(1, 256), (16, 512), (33, 768), (200, 2304), (257, 11008)])
+def test_repack_bytes_match_oracle(m, k):
+    note("repack m=%d k=%d" % (m, k))
+    f = synth.random_fields(600 + m, m, k)
+    w = synth.pack_q4k(f)
+    wr = binding.repack(to_dev(w), m, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(wr.cpu().numpy(), oracle.q4k_repack(w, m, k))
+
+
+@pytest.mark.parametrize("n,m,k", [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (5, 129, 4352),
+                                   (7, 131, 2304), (8, 256, 11008), (9, 40, 768), (20, 100, 1024)])
+def test_repacked_mmq(n, m, k):
+    note("repacked mmq n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(610 + n, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(610 + n, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    wd = to_dev(w)
+    q, ds = gpu_quantize(x)
+    wr = binding.repack(wd, m, k)
+    got = binding.fp32_repacked(wr, m, k, q, ds)
+    base = binding.fp32(wd, m, k, q, ds)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    if n <= 8:
+        assert np.array_equal(got.view(np.uint32), base.cpu().numpy().view(np.uint32))
+    rq, rds = oracle.quantize(x)
+    check_fp32(got, oracle.out_f64(w, m, k, rq, rds), "repacked")
+
+
+@pytest.mark.parametrize("n", [1, 7])
+def test_repacked_wide_in_full(n):
+    f = synth.weight_bound_weights("wide_in")
+    x = synth.weight_bound_activation("wide_in", n)
+    m, k = f.q.shape
+    note("repacked wide_in full n=%d" % n)
+    w = synth.pack_q4k(f)
+    wd = to_dev(w)
+    q, ds = binding.quantize(to_dev(x))
+    wr = binding.repack(wd, m, k)
+    got = binding.fp32_repacked(wr, m, k, q, ds)
+    base = binding.fp32(wd, m, k, q, ds)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), base.cpu().numpy().view(np.uint32))
+    assert np.array_equal(wr.cpu().numpy()[:4 * 2368 * 32], oracle.q4k_repack(w[:64], 64, k))
