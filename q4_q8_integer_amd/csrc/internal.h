@@ -100,6 +100,11 @@ hipError_t launch_q6k_dots(const uint8_t* w, int m, int k, const int8_t* q, int 
 hipError_t launch_q6k_i8(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                          int n, void* out, bool half_out, hipStream_t stream);
 
+// out[t][o] for any n: binary16 MFMA on the split exact operands sc*nibble/64
+// and sc*(hi2 - 2)/4 (one FMA per output and chunk).
+hipError_t launch_q6k_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
+                          void* out, bool half_out, hipStream_t stream);
+
 // out[t][o] for 1 <= n <= kQ6kGemvMaxN: 4-way int8 dots on the vector ALU.
 hipError_t launch_q6k_gemv(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                            int n, void* out, bool half_out, hipStream_t stream);

@@ -112,14 +112,20 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
 }
 
 // q6_K kernel behind the fold entry points: the vector-ALU dot4 kernel for
-// n <= 8, the int8-MFMA tile kernel above.  MMQ_Q6K_KERNEL=i8 forces the
-// tile kernel (for comparisons and tests).
-bool q6k_forced_i8() {
-    static const bool f = [] {
+// n <= 8, the binary16-MFMA kernel above.  MMQ_Q6K_KERNEL=i8|f16|gemv forces
+// one (for comparisons and tests; "gemv" only where n <= 8).
+enum class Q6kKernel { Auto, I8, F16, Gemv };
+
+Q6kKernel forced_q6k_kernel() {
+    static const Q6kKernel k = [] {
         const char* v = std::getenv("MMQ_Q6K_KERNEL");
-        return v && std::strcmp(v, "i8") == 0;
+        if (!v) return Q6kKernel::Auto;
+        if (std::strcmp(v, "i8") == 0) return Q6kKernel::I8;
+        if (std::strcmp(v, "f16") == 0) return Q6kKernel::F16;
+        if (std::strcmp(v, "gemv") == 0) return Q6kKernel::Gemv;
+        return Q6kKernel::Auto;
     }();
-    return f;
+    return k;
 }
 
 int q6k_fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
@@ -131,7 +137,11 @@ int q6k_fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const u
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    auto launch = n <= mmq::kQ6kGemvMaxN && !q6k_forced_i8() ? mmq::launch_q6k_gemv : mmq::launch_q6k_i8;
+    const Q6kKernel f = forced_q6k_kernel();
+    auto launch = n <= mmq::kQ6kGemvMaxN ? mmq::launch_q6k_gemv : mmq::launch_q6k_f16;
+    if (f == Q6kKernel::I8) launch = mmq::launch_q6k_i8;
+    if (f == Q6kKernel::F16) launch = mmq::launch_q6k_f16;
+    if (f == Q6kKernel::Gemv && n <= mmq::kQ6kGemvMaxN) launch = mmq::launch_q6k_gemv;
     return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
                              half_out, stream));
 }

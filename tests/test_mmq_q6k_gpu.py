@@ -2,8 +2,9 @@
 against the oracle: bit-exact group dots, the float32 bar, binary16 output
 equal to the rounded float32 output bit for bit, ragged shapes (odd
 super-block counts put blocks at both 2- and 4-byte alignments), both
-kernels (the dot4 kernel by default up to 8 tokens, the int8-MFMA tile kernel
-above that and, forced in a child process, on few tokens), the hand-worked
+kernels (the dot4 kernel by default up to 8 tokens, the binary16-MFMA kernel
+above that, the int8-MFMA tile kernel behind the dots entry; each also forced
+outside its range in a child process), the hand-worked
 super-block, full-size workloads, and metamorphic properties."""
 import os
 import subprocess
@@ -108,8 +109,9 @@ def test_q6k_wide_in_full(n):
 
 
 def test_q6k_qproj_full_sampled():
-    """W[4096 x 4096] q6_K at 2630 tokens (the tile kernel): sampled tokens x
-    all rows in float32, exact group dots for sampled tokens x a row window."""
+    """W[4096 x 4096] q6_K at 2630 tokens (the binary16-MFMA kernel): sampled
+    tokens x all rows in float32, exact group dots (the tile kernel) for
+    sampled tokens x a row window."""
     f = synth.q6k_weights("qproj")
     m, k = f.q.shape
     n = 2630
@@ -158,10 +160,19 @@ print("ok")
 """
 
 
-def test_q6k_forced_tile_kernel_on_few_tokens():
-    shapes = [(1, 1, 256), (3, 33, 768), (5, 131, 2304), (8, 200, 1280)]
-    env = dict(os.environ, MMQ_Q6K_KERNEL="i8")
-    code = CHILD % {"root": ROOT, "tests": os.path.join(ROOT, "tests"), "shapes": repr(shapes)}
+FORCED = {
+    "i8": [(1, 1, 256), (3, 33, 768), (5, 131, 2304), (8, 200, 1280), (40, 96, 512), (130, 129, 768)],
+    "f16": [(1, 1, 256), (3, 33, 768), (8, 200, 1280), (9, 17, 512), (64, 127, 256), (200, 300, 1280)],
+    "gemv": [(1, 40, 512), (4, 16, 256), (8, 129, 2304)],
+}
+
+
+@pytest.mark.parametrize("kernel", sorted(FORCED))
+def test_q6k_forced_kernel(kernel):
+    """Every q6_K fold kernel meets the bar outside its default range
+    (MMQ_Q6K_KERNEL is read once per process, so each runs in a child)."""
+    env = dict(os.environ, MMQ_Q6K_KERNEL=kernel)
+    code = CHILD % {"root": ROOT, "tests": os.path.join(ROOT, "tests"), "shapes": repr(FORCED[kernel])}
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        timeout=300)
     print(r.stdout, r.stderr[-2000:])
