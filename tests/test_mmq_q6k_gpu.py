@@ -177,3 +177,57 @@ def test_q6k_forced_kernel(kernel):
                        timeout=300)
     print(r.stdout, r.stderr[-2000:])
     assert r.returncode == 0 and r.stdout.strip().endswith("ok")
+
+
+# ------------------------------------------------------------- metamorphic
+@pytest.mark.parametrize("n", [5, 70])
+def test_q6k_outputs_fully_written_and_guard_bands_untouched(n):
+    """NaN-poisoned outputs are fully overwritten (both fold kernels, and the
+    dots kernel) and the bytes on either side are untouched."""
+    m, k = 100, 512
+    note("q6k guard bands n=%d" % n)
+    f = synth.random_q6k_fields(820 + n, m, k)
+    x = synth.random_activations(820 + n, n, k)
+    w = synth.pack_q6k(f)
+    wg = to_dev(w)
+    q, ds = gpu_quantize(x)
+    pad = 64
+    buf = torch.full((n * m + 2 * pad,), float("nan"), dtype=torch.float32, device=q.device)
+    buf[:pad] = 12345.0
+    buf[-pad:] = -6789.0
+    binding.mmq_q6k_q8_fp32out(wg, m, k, q, ds, n, buf[pad:pad + n * m])
+    dbuf = torch.full((n * m * (k // 16) + 2 * pad,), -77, dtype=torch.int32, device=q.device)
+    binding.mmq_q6k_q8(wg, m, k, q, ds, n, dbuf[pad:pad + n * m * (k // 16)])
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert not np.isnan(h[pad:-pad]).any()
+    assert (h[:pad] == 12345.0).all() and (h[-pad:] == -6789.0).all()
+    hd = dbuf.cpu().numpy()
+    assert (hd[:pad] == -77).all() and (hd[-pad:] == -77).all()
+    rq, _ = oracle.quantize(x)
+    assert np.array_equal(hd[pad:-pad].reshape(n, m, k // 16), oracle.q6k_dots(w, m, k, rq))
+
+
+def test_q6k_token_slice_bitwise():
+    """Above 8 tokens, a token's output row does not depend on the other
+    tokens of the call (same kernel, same summation order)."""
+    m, k = 150, 1024
+    f = synth.random_q6k_fields(830, m, k)
+    x = synth.random_activations(830, 200, k)
+    wg = to_dev(synth.pack_q6k(f))
+    q, ds = gpu_quantize(x)
+    a = binding.q6k_fp32(wg, m, k, q, ds)
+    s = binding.q6k_fp32(wg, m, k, q[37:151].contiguous(), ds[37:151].contiguous())
+    d1 = binding.q6k_dots(wg, m, k, q)
+    d2 = binding.q6k_dots(wg, m, k, q[37:151].contiguous())
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy()[37:151].view(np.uint32), s.cpu().numpy().view(np.uint32))
+    assert np.array_equal(d1.cpu().numpy()[37:151], d2.cpu().numpy())
+
+
+def test_q6k_empty_calls_touch_nothing():
+    q = torch.zeros((0, 256), dtype=torch.int8, device="cuda:0")
+    ds = torch.zeros((0, 8), dtype=torch.int32, device="cuda:0")
+    w = torch.zeros((4, 210), dtype=torch.uint8, device="cuda:0")
+    assert binding.q6k_fp32(w, 4, 256, q, ds).shape == (0, 4)
+    assert binding.q6k_dots(w, 4, 256, q).shape == (0, 4, 16)

@@ -62,3 +62,22 @@ def test_silu_quantize_equals_plain_quantize_of_h():
 def test_silu_quantize_ffn_down_full_size():
     g, u = synth.ffn_gate_up_outputs()
     _check(g, u, "FFN down input 2630x11008")
+
+
+def test_silu_quantize_guard_bands_and_empty():
+    n, k = 9, 320
+    g, u = _inputs(13, n, k)
+    pad = 64
+    qbuf = torch.full((n * k + 2 * pad,), 99, dtype=torch.int8, device="cuda:0")
+    dbuf = torch.full((n * k // 32 + 2 * pad,), -5, dtype=torch.int32, device="cuda:0")
+    binding.q8_quantize_silu_mul(to_dev(g), to_dev(u), n, k, qbuf[pad:pad + n * k], dbuf[pad:pad + n * k // 32])
+    torch.cuda.synchronize()
+    hq, hd = qbuf.cpu().numpy(), dbuf.cpu().numpy()
+    assert (hq[:pad] == 99).all() and (hq[-pad:] == 99).all()
+    assert (hd[:pad] == -5).all() and (hd[-pad:] == -5).all()
+    rq, rds = oracle.quantize_silu_mul(g, u)
+    assert np.array_equal(hq[pad:-pad].reshape(n, k), rq)
+    assert np.array_equal(hd[pad:-pad].view(np.uint32).reshape(n, k // 32), rds)
+    z = torch.zeros((0, 64), device="cuda:0")
+    q0, ds0 = binding.quantize_silu_mul(z, z)
+    assert q0.shape == (0, 64) and ds0.shape == (0, 2)

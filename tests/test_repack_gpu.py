@@ -59,3 +59,19 @@ def test_repacked_wide_in_full(n):
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy().view(np.uint32), base.cpu().numpy().view(np.uint32))
     assert np.array_equal(wr.cpu().numpy()[:4 * 2368 * 32], oracle.q4k_repack(w[:64], 64, k))
+
+
+def test_repack_guard_bands_and_empty():
+    m, k = 21, 512
+    f = synth.random_fields(620, m, k)
+    w = synth.pack_q4k(f)
+    size = binding.repack_bytes(m, k)
+    pad = 64
+    buf = torch.full((size + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    binding.q4k_repack(to_dev(w), m, k, buf[pad:pad + size])
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert (h[:pad] == 0xA5).all() and (h[-pad:] == 0xA5).all()
+    assert np.array_equal(h[pad:-pad], oracle.q4k_repack(w, m, k))
+    empty = torch.zeros(0, dtype=torch.uint8, device="cuda:0")
+    binding.q4k_repack(empty, 0, k, empty)
