@@ -69,7 +69,7 @@ struct SmallLds {
     };
 };
 
-template <int T, int RB, bool H>
+template <int T, int RB, bool PF, bool H>
 __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict__ w,
                                                        const int8_t* __restrict__ q,
                                                        const uint32_t* __restrict__ ds,
@@ -108,33 +108,42 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
             accb[rb][tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         }
 
-    for (int sb = sb0; sb < sb1; ++sb) {
+    // Global data of one super-block step, as this lane loads it.  Two sets
+    // alternate: the loads of step sb+1 are in flight while sb is computed.
+    struct Fetch {
         uint4 hdr[RB];
         uint2 qs[RB][4];
+        uint4 tq[T][4];
+        uint32_t word[T][2];
+    };
+    auto fetch = [&](Fetch& f, int sb) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const uint8_t* b = blk[rb] + (int64_t)sb * kBlockBytes;
-            hdr[rb] = *reinterpret_cast<const uint4*>(b);
+            f.hdr[rb] = *reinterpret_cast<const uint4*>(b);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) qs[rb][p] = *reinterpret_cast<const uint2*>(b + 16 + 32 * p + 8 * kg);
+            for (int p = 0; p < 4; ++p) f.qs[rb][p] = *reinterpret_cast<const uint2*>(b + 16 + 32 * p + 8 * kg);
         }
-        uint4 tq[T][4];
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.tq[tt][j] = *reinterpret_cast<const uint4*>(qpiece[tt][j] + sb * 256);
+            const int tok = min(16 * tt + r, N - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) f.word[tt][h] = ds[(int64_t)tok * C + sb * 8 + kg + 4 * h];
+        }
+    };
+    auto compute = [&](const Fetch& f) {
+        // scale words of this super-block: lane handles (token 16tt + r, chunks kg and kg + 4)
 #pragma unroll
         for (int tt = 0; tt < T; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tq[tt][j] = *reinterpret_cast<const uint4*>(qpiece[tt][j] + sb * 256);
-        // scale words of this super-block: lane handles (token 16tt + r, chunks kg and kg + 4)
-#pragma unroll
-        for (int tt = 0; tt < T; ++tt) {
-            const int tok = min(16 * tt + r, N - 1);
-#pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint32_t word = ds[(int64_t)tok * C + sb * 8 + kg + 4 * h];
+                const uint32_t word = f.word[tt][h];
                 const float da = half_bits_to_float(word);
                 L.m.da[wv][kg + 4 * h][16 * tt + r] = da;
                 L.m.dass[wv][kg + 4 * h][16 * tt + r] = da * (float)(int16_t)(uint16_t)(word >> 16);
             }
-        }
         // The LDS areas are wave-private: LDS accesses of one wave complete in
         // order, so each write below is seen by the reads after it, and a tile's
         // reads finish before the next tile overwrites the area.
@@ -145,16 +154,16 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 int sc, mn;
-                scale_min(hdr[rb].y, hdr[rb].z, hdr[rb].w, c, sc, mn);
+                scale_min(f.hdr[rb].y, f.hdr[rb].z, f.hdr[rb].w, c, sc, mn);
                 scf[rb][c] = (float)sc;
-                const uint2 x = qs[rb][c >> 1];
+                const uint2 x = f.qs[rb][c >> 1];
                 bw[rb][c] = (c & 1) ? (int64_t)(((uint64_t)((x.y >> 4) & 0x0F0F0F0Fu) << 32) | ((x.x >> 4) & 0x0F0F0F0Fu))
                                     : (int64_t)(((uint64_t)(x.y & 0x0F0F0F0Fu) << 32) | (x.x & 0x0F0F0F0Fu));
             }
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) L.m.tok[wv][4 * j + (lane >> 4)][lane & 15] = tq[tt][j];
+            for (int j = 0; j < 4; ++j) L.m.tok[wv][4 * j + (lane >> 4)][lane & 15] = f.tq[tt][j];
             const uint8_t* arow = reinterpret_cast<const uint8_t*>(L.m.tok[wv][r]) + 8 * kg;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -173,24 +182,44 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float dmin = half_bits_to_float(hdr[rb].x >> 16);
+            const float dmin = half_bits_to_float(f.hdr[rb].x >> 16);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 int sc, mn;
-                scale_min(hdr[rb].y, hdr[rb].z, hdr[rb].w, 4 * j + kg, sc, mn);
+                scale_min(f.hdr[rb].y, f.hdr[rb].z, f.hdr[rb].w, 4 * j + kg, sc, mn);
                 const float bneg = -(dmin * (float)mn);
 #pragma unroll
                 for (int tt = 0; tt < T; ++tt)
                     acc[rb][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(L.m.dass[wv][4 * j + kg][16 * tt + r], bneg,
                                                                        acc[rb][tt], 0, 0, 0);
             }
-            const float d = half_bits_to_float(hdr[rb].x);
+            const float d = half_bits_to_float(f.hdr[rb].x);
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[rb][tt][i] = fmaf(d, accb[rb][tt][i], acc[rb][tt][i]);
                 accb[rb][tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
             }
+        }
+    };
+
+    if constexpr (PF) {
+        // Every fetch is unconditional (a fetch past the last step re-reads it).
+        Fetch fa, fb;
+        if (sb0 < sb1) fetch(fa, sb0);
+        for (int sb = sb0; sb < sb1; sb += 2) {
+            fetch(fb, min(sb + 1, sb1 - 1));
+            compute(fa);
+            if (sb + 1 >= sb1) break;
+            fetch(fa, min(sb + 2, sb1 - 1));
+            compute(fb);
+        }
+    } else {
+        // one step at a time: the step's loads are all issued before its math
+        for (int sb = sb0; sb < sb1; ++sb) {
+            Fetch f;
+            fetch(f, sb);
+            compute(f);
         }
     }
 
@@ -217,12 +246,13 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
     }
 }
 
-template <int T>
+template <int T, bool PF>
 hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
                     void* out, bool half_out, hipStream_t stream) {
     constexpr int RB = 2;
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k, (void*)&out};
-    const void* f = half_out ? (const void*)mmq_small_kernel<T, RB, true> : (const void*)mmq_small_kernel<T, RB, false>;
+    const void* f = half_out ? (const void*)mmq_small_kernel<T, RB, PF, true>
+                             : (const void*)mmq_small_kernel<T, RB, PF, false>;
     return hipLaunchKernel(f, dim3((unsigned)((m + 16 * RB - 1) / (16 * RB))), dim3(NT), args, 0, stream);
 }
 
@@ -230,10 +260,17 @@ hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint3
 
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                                  int n, void* out, bool half_out, hipStream_t stream) {
-    if (n <= 16) return launch_t<1>(w, m, k, q, ds, n, out, half_out, stream);
-    if (n <= 32) return launch_t<2>(w, m, k, q, ds, n, out, half_out, stream);
-    if (n <= 48) return launch_t<3>(w, m, k, q, ds, n, out, half_out, stream);
-    return launch_t<4>(w, m, k, q, ds, n, out, half_out, stream);
+    // Prefetching the next super-block into a second register set pays when
+    // each wave has many steps (8192 x 28672: 14 per wave, 16 tokens 67 ->
+    // 56 us) and costs occupancy when it has few (28672 x 8192: 4 per wave,
+    // 63 -> 73 us); with 3-4 token tiles the second set does not fit.
+    const bool pf = (k / 256) / WAVES >= 8;
+    if (n <= 16) return pf ? launch_t<1, true>(w, m, k, q, ds, n, out, half_out, stream)
+                           : launch_t<1, false>(w, m, k, q, ds, n, out, half_out, stream);
+    if (n <= 32) return pf ? launch_t<2, true>(w, m, k, q, ds, n, out, half_out, stream)
+                           : launch_t<2, false>(w, m, k, q, ds, n, out, half_out, stream);
+    if (n <= 48) return launch_t<3, false>(w, m, k, q, ds, n, out, half_out, stream);
+    return launch_t<4, false>(w, m, k, q, ds, n, out, half_out, stream);
 }
 
 }  // namespace mmq
