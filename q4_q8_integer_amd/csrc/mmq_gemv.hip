@@ -23,6 +23,15 @@
 //     576 contiguous bytes): reading q4_K in runs of several blocks per row
 //     keeps HBM close to its streaming rate, where one block from each of
 //     many rows does not.
+//   * Up to 6 tokens the weights go through LDS: per step the wave copies
+//     its 16 runs with buffer loads that write LDS directly (consecutive
+//     16-byte pieces, so each load instruction covers about one contiguous
+//     KiB and no registers hold the copy), then each lane reads its three
+//     16-byte fields from there.  Loading the fields straight into registers
+//     costs 64 lanes x 3 scattered 16-byte reads per block column, which
+//     keeps the address units, not HBM, busy; it is kept for 6-8 tokens,
+//     where the vector work is the bound.  With >= 4 steps per wave, a
+//     second LDS area takes the next step's copy while a step computes.
 //   * A workgroup is 16 rows; its waves split the super-blocks, and the
 //     partial sums are added in a fixed order (a butterfly over the four
 //     chunk-pair lanes of a row, then the waves in index order): results do
@@ -36,6 +45,18 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWaves = 4;   // waves per workgroup (split of the super-blocks)
+
+// Weight layouts the kernel reads: GGUF q4_K rows loaded straight into
+// registers, the repacked 16-row records, or GGUF rows staged through LDS
+// (one area per wave, or two with the next step's copy in flight).
+enum { kDirect = 0, kRepacked = 1, kStaged = 2, kStagedPf = 3 };
+constexpr bool staged_layout(int L) { return L == kStaged || L == kStagedPf; }
+constexpr int kStagedRow = 4 * kBlockBytes + 16;   // LDS bytes per row of a 4-block step
+constexpr int kStagedArea = 16 * kStagedRow;        // LDS bytes of one step's copy
+// s_waitcnt operand: at most n vector-memory operations outstanding, the
+// other counters untouched (vmcnt bits 3:0 and 15:14)
+constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kBufferFlags = 0x00020000;            // word 3 of a raw buffer resource on gfx950
 
 __device__ __forceinline__ float half_lo(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
@@ -173,13 +194,13 @@ __device__ __forceinline__ void fold_two_tokens(float& acca, float& accb, float 
 // One super-block J of the step for every token.  A slot past the wave's
 // last super-block (live false) runs with d = dmin = 0 and adds exactly 0:
 // no branch, so the compiler keeps all of the step's loads ahead of the math.
-template <int N, int J, bool R>
+template <int N, int J, int L>
 __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb, int p, bool live,
                                         const v4u* tq, const float* tda, const float* tdass,
                                         float* acc) {
     const float d = live ? half_lo(h[0]) : 0.0f, dmin = live ? half_lo(h[0] >> 16) : 0.0f;
     uint32_t sc0, sc1, m0, m1;
-    if constexpr (R) {
+    if constexpr (L == kRepacked) {
         // repacked layout: the four scales as bytes of one dword
         sc0 = h[1] & 0xFF;
         sc1 = (h[1] >> 8) & 0xFF;
@@ -236,8 +257,10 @@ struct Step {
 // Issue the loads of the step starting at super-block s.  Every load is
 // unconditional: slots past the wave's last super-block re-read that block
 // (and are computed with live = false).  wrow is the lane's row (GGUF
-// layout) or the workgroup's 16-row tile of records (repacked layout, R).
-template <int N, int SW, bool R>
+// layout) or the workgroup's 16-row tile of records (repacked layout).  The
+// staged layout loads only the activations here (its weights go through
+// stage_issue / stage_read).
+template <int N, int SW, int L>
 __device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
                                           const int8_t* __restrict__ q,
                                           const uint32_t* __restrict__ ds, int K, int C, int s,
@@ -251,9 +274,10 @@ __device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
     const int64_t woff = (int64_t)min(s + ((r >> 1) & 3), last) * 8 + 2 * p + (r & 1);
 #pragma unroll
     for (int t = 0; t < N; ++t) st.tw[t] = ds[(int64_t)t * C + woff];
+    if constexpr (staged_layout(L)) return;   // fields come from the wave's LDS area
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
-        if constexpr (R) {
+        if constexpr (L == kRepacked) {
             const uint8_t* b = wrow + (int64_t)min(s + j, last) * kRepackRecordBytes;
             st.hdr[j] = v4u{*reinterpret_cast<const uint32_t*>(b + 4 * r),
                             *reinterpret_cast<const uint32_t*>(b + 64 + 4 * (16 * p + r)), 0u, 0u};
@@ -268,7 +292,45 @@ __device__ __forceinline__ void load_step(Step<N, SW>& st, const uint8_t* wrow,
     }
 }
 
-template <int N, int SW, bool R>
+// Staged GGUF layout.  The wave copies the 16 runs of 4 blocks of a step
+// into one of its two LDS areas with consecutive 16-byte pieces (one load
+// instruction reads about one contiguous KiB and writes it to LDS without
+// passing through registers), so the next step's copy is in flight while
+// this step computes.  Slot i of an area (16 bytes at 16*i) holds piece
+// i % 37 of row i / 37 of the tile; piece 36 is padding, which makes the row
+// stride 592 bytes and the 16-row reads of stage_read free of bank
+// conflicts.  wt spans the tile's rows: pieces past the end of a row (a
+// wave's last step may run over it) read the next row, past the tile they
+// read zeros; either way they are never used.
+constexpr int kStagedSlots = 16 * kStagedRow / 16;
+constexpr int kStagedLoads = (kStagedSlots + 63) / 64;   // load instructions per step
+
+__device__ __forceinline__ void stage_issue(__amdgpu_buffer_rsrc_t wt, int S, int s, int lane,
+                                            uint8_t* area) {
+#pragma unroll
+    for (int c = 0; c < kStagedLoads; ++c) {
+        const int i = lane + 64 * c;
+        const int rr = i / (kStagedRow / 16), ch = min(i - rr * (kStagedRow / 16), 4 * 9 - 1);
+        const uint32_t off = (uint32_t)(rr * S + s + ch / 9) * kBlockBytes + 16 * (ch % 9);
+        if (i < kStagedSlots)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wt, (__attribute__((address_space(3))) void*)(area + 1024 * c),
+                                                     16, off, 0, 0, 0);
+    }
+}
+
+template <int N, int SW>
+__device__ __forceinline__ void stage_read(Step<N, SW>& st, const uint8_t* area, int p, int r) {
+    static_assert(SW == 4, "staged rows hold four blocks");
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+        const uint8_t* b = area + r * kStagedRow + j * kBlockBytes;
+        st.hdr[j] = *reinterpret_cast<const v4u*>(b);
+        st.qa[j] = *reinterpret_cast<const v4u*>(b + 16 + 32 * p);
+        st.qb[j] = *reinterpret_cast<const v4u*>(b + 32 + 32 * p);
+    }
+}
+
+template <int N, int SW, int L>
 __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int p, float* acc) {
     float tda[N], tdass[N];
 #pragma unroll
@@ -276,19 +338,20 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int 
         tda[t] = half_lo(st.tw[t]);
         tdass[t] = tda[t] * (float)(int16_t)(uint16_t)(st.tw[t] >> 16);
     }
-    gemv_sb<N, 0, R>(st.hdr[0], st.qa[0], st.qb[0], p, ns > 0, st.tq, tda, tdass, acc);
-    if constexpr (SW > 1) gemv_sb<N, 1, R>(st.hdr[1], st.qa[1], st.qb[1], p, ns > 1, st.tq, tda, tdass, acc);
-    if constexpr (SW > 2) gemv_sb<N, 2, R>(st.hdr[2], st.qa[2], st.qb[2], p, ns > 2, st.tq, tda, tdass, acc);
-    if constexpr (SW > 3) gemv_sb<N, 3, R>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
+    gemv_sb<N, 0, L>(st.hdr[0], st.qa[0], st.qb[0], p, ns > 0, st.tq, tda, tdass, acc);
+    if constexpr (SW > 1) gemv_sb<N, 1, L>(st.hdr[1], st.qa[1], st.qb[1], p, ns > 1, st.tq, tda, tdass, acc);
+    if constexpr (SW > 2) gemv_sb<N, 2, L>(st.hdr[2], st.qa[2], st.qb[2], p, ns > 2, st.tq, tda, tdass, acc);
+    if constexpr (SW > 3) gemv_sb<N, 3, L>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
 }
 
-template <int N, int SW, bool H, bool R>
+template <int N, int SW, bool H, int L>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
                                                                   const int8_t* __restrict__ q,
                                                                   const uint32_t* __restrict__ ds,
                                                                   int M, int K,
                                                                   void* __restrict__ out) {
     __shared__ float red[kMaxWaves][N][16];
+    extern __shared__ __attribute__((aligned(16))) uint8_t staged[];   // W x 2 areas (staged layout)
 
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -297,8 +360,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     const int row0 = blockIdx.x * 16;
     const int S = K >> 8, C = K >> 5;
     const int sb0 = (int)((int64_t)S * wv / W), sb1 = (int)((int64_t)S * (wv + 1) / W);
-    const uint8_t* wrow = R ? w + (int64_t)blockIdx.x * S * kRepackRecordBytes
-                            : w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
+    const uint8_t* wrow = L == kRepacked ? w + (int64_t)blockIdx.x * S * kRepackRecordBytes
+                                         : w + (int64_t)min(row0 + r, M - 1) * S * kBlockBytes;
+    uint8_t* lds = staged + wv * (L == kStagedPf ? 2 : 1) * kStagedArea;
+    const __amdgpu_buffer_rsrc_t wt =   // the tile's GGUF rows (used by the staged layout)
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * S * kBlockBytes), 0,
+                                          min(16, M - row0) * S * kBlockBytes, kBufferFlags);
 
     float acc[N];
 #pragma unroll
@@ -309,11 +376,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     // slower: it halves the waves a CU holds, and a wave's own latency is not
     // what limits the stream.)
     const int last = sb1 - 1;
-    for (int s = sb0; s < sb1; s += SW) {
-        Step<N, SW> A;
-        load_step<N, SW, R>(A, wrow, q, ds, K, C, s, last, p, r);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_step<N, SW, R>(A, sb1 - s, p, acc);
+    if constexpr (L == kStaged) {
+        for (int s = sb0; s < sb1; s += SW) {
+            Step<N, SW> A;
+            load_step<N, SW, L>(A, wrow, q, ds, K, C, s, last, p, r);
+            stage_issue(wt, S, s, lane, lds);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
+            __builtin_amdgcn_sched_barrier(0);
+            stage_read(A, lds, p, r);
+            compute_step<N, SW, L>(A, sb1 - s, p, acc);
+        }
+    } else if constexpr (L == kStagedPf) {
+        // The next step's weights (into the other LDS area) and activations
+        // (into registers) are in flight while a step computes; one wait for
+        // everything at the top of the step.
+        Step<N, SW> nx;
+        if (sb0 < sb1) {
+            load_step<N, SW, L>(nx, wrow, q, ds, K, C, sb0, last, p, r);
+            stage_issue(wt, S, sb0, lane, lds);
+        }
+        for (int s = sb0, b = 0; s < sb1; s += SW, b ^= 1) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
+            __builtin_amdgcn_sched_barrier(0);
+            Step<N, SW> A;
+#pragma unroll
+            for (int t = 0; t < N; ++t) {
+                A.tq[t] = nx.tq[t];
+                A.tw[t] = nx.tw[t];
+            }
+            if (s + SW < sb1) {
+                load_step<N, SW, L>(nx, wrow, q, ds, K, C, s + SW, last, p, r);
+                stage_issue(wt, S, s + SW, lane, lds + (b ^ 1) * kStagedArea);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            stage_read(A, lds + b * kStagedArea, p, r);
+            compute_step<N, SW, L>(A, sb1 - s, p, acc);
+        }
+    } else {
+        for (int s = sb0; s < sb1; s += SW) {
+            Step<N, SW> A;
+            load_step<N, SW, L>(A, wrow, q, ds, K, C, s, last, p, r);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step<N, SW, L>(A, sb1 - s, p, acc);
+        }
     }
 
     // the four chunk-pair lanes of a row (every lane ends with the same
@@ -333,41 +438,54 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t*
     }
 }
 
-template <int N, bool R>
+template <int N, int L>
 hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                     void* out, bool half_out, hipStream_t stream) {
     const int S = k / 256;
     const int rows = (m + 15) / 16;
-    // The super-blocks of a row are split over the waves of a workgroup.
-    // Measured on the 28672 x 8192 and 8192 x 28672 matrices: one token
-    // streams best with about 1024 waves in all (long runs per wave), two or
-    // more tokens, whose vector work per byte is larger, with 4 waves per row
-    // tile.
-    int waves = N == 1 ? 1024 / rows : 4;
-    waves = waves < 1 ? 1 : waves > 4 ? 4 : waves;
-    waves = waves > S ? S : waves;
+    // The super-blocks of a row are split over the 4 waves of a workgroup
+    // (fewer when a row has fewer super-blocks).  Every layout splits the
+    // same way, so every layout sums in the same order.
+    int waves = S < 4 ? S : 4;
     constexpr int SW = 4;
+    const size_t lds = L == kStaged ? (size_t)waves * kStagedArea
+                       : L == kStagedPf ? (size_t)waves * 2 * kStagedArea : 0;
     if (half_out)
-        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, true, R>), dim3(rows), dim3(64 * waves), 0, stream,
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, true, L>), dim3(rows), dim3(64 * waves), lds, stream,
                            w, q, ds, m, k, out);
     else
-        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, false, R>), dim3(rows), dim3(64 * waves), 0, stream,
+        hipLaunchKernelGGL((mmq_gemv_kernel<N, SW, false, L>), dim3(rows), dim3(64 * waves), lds, stream,
                            w, q, ds, m, k, out);
     return hipGetLastError();
 }
 
-template <bool R>
+// Token counts each layout is launched for (the staged layouts up to 6
+// tokens, the register-loaded GGUF layout from 6): the others are not
+// instantiated.
+template <int L>
+constexpr bool serves(int n) {
+    return staged_layout(L) ? n <= 6 : L == kDirect ? n >= 6 : true;
+}
+
+template <int L, int N>
+hipError_t launch_if(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, void* out,
+                     bool half_out, hipStream_t stream) {
+    if constexpr (serves<L>(N)) return launch_n<N, L>(w, m, k, q, ds, out, half_out, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int L>
 hipError_t launch_any(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
                       void* out, bool half_out, hipStream_t stream) {
     switch (n) {
-        case 1: return launch_n<1, R>(w, m, k, q, ds, out, half_out, stream);
-        case 2: return launch_n<2, R>(w, m, k, q, ds, out, half_out, stream);
-        case 3: return launch_n<3, R>(w, m, k, q, ds, out, half_out, stream);
-        case 4: return launch_n<4, R>(w, m, k, q, ds, out, half_out, stream);
-        case 5: return launch_n<5, R>(w, m, k, q, ds, out, half_out, stream);
-        case 6: return launch_n<6, R>(w, m, k, q, ds, out, half_out, stream);
-        case 7: return launch_n<7, R>(w, m, k, q, ds, out, half_out, stream);
-        case 8: return launch_n<8, R>(w, m, k, q, ds, out, half_out, stream);
+        case 1: return launch_if<L, 1>(w, m, k, q, ds, out, half_out, stream);
+        case 2: return launch_if<L, 2>(w, m, k, q, ds, out, half_out, stream);
+        case 3: return launch_if<L, 3>(w, m, k, q, ds, out, half_out, stream);
+        case 4: return launch_if<L, 4>(w, m, k, q, ds, out, half_out, stream);
+        case 5: return launch_if<L, 5>(w, m, k, q, ds, out, half_out, stream);
+        case 6: return launch_if<L, 6>(w, m, k, q, ds, out, half_out, stream);
+        case 7: return launch_if<L, 7>(w, m, k, q, ds, out, half_out, stream);
+        case 8: return launch_if<L, 8>(w, m, k, q, ds, out, half_out, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -377,13 +495,21 @@ hipError_t launch_any(const uint8_t* w, int m, int k, const int8_t* q, const uin
 hipError_t launch_mmq_fp32_gemv(const uint8_t* w, int m, int k, const int8_t* q,
                                 const uint32_t* ds, int n, void* out, bool half_out,
                                 hipStream_t stream) {
-    return launch_any<false>(w, m, k, q, ds, n, out, half_out, stream);
+    // Staging through LDS pays while the stream, not the vector work, is the
+    // bound; the next step's copy in flight pays when a wave has at least 4
+    // steps (4 waves of 4-block steps: 64 super-blocks per row).  Measured
+    // on the 28672 x 8192 and 8192 x 28672 matrices, 1-8 tokens.
+    const bool pf = k / 256 >= 64;
+    if (n <= 5 || (n == 6 && pf))
+        return pf ? launch_any<kStagedPf>(w, m, k, q, ds, n, out, half_out, stream)
+                  : launch_any<kStaged>(w, m, k, q, ds, n, out, half_out, stream);
+    return launch_any<kDirect>(w, m, k, q, ds, n, out, half_out, stream);
 }
 
 hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
                                          const uint32_t* ds, int n, void* out, bool half_out,
                                          hipStream_t stream) {
-    return launch_any<true>(wr, m, k, q, ds, n, out, half_out, stream);
+    return launch_any<kRepacked>(wr, m, k, q, ds, n, out, half_out, stream);
 }
 
 }  // namespace mmq

@@ -56,6 +56,32 @@ def test_ragged_shapes(n, m, k):
     run_case(f, x, "ragged")
 
 
+@pytest.mark.parametrize("k", [2304, 16640])
+@pytest.mark.parametrize("n", range(1, 9))
+def test_few_token_weight_layouts(n, k):
+    """Every token count of the dot4 kernel on both sides of its layout
+    choices: 9 super-blocks per row (weights staged through one LDS area up
+    to 5 tokens, loaded into registers from 6) and 65 (staged with the next
+    step in flight up to 6 tokens: 4 waves of 16-17 super-blocks, so each
+    wave's last step runs past its range and the last row's past the
+    matrix).  40 rows leave a half tile.  The result also equals the
+    repacked-layout path bit for bit (same summation order)."""
+    m = 40
+    note("few-token layouts n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(700 + 10 * n + k % 7, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(700 + 10 * n + k % 7, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    wd = to_dev(w)
+    q, ds = gpu_quantize(x)
+    got = binding.fp32(wd, m, k, q, ds)
+    rep = binding.fp32_repacked(binding.repack(wd, m, k), m, k, q, ds)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), rep.cpu().numpy().view(np.uint32))
+    rq, rds = oracle.quantize(x)
+    check_fp32(got, oracle.out_f64(w, m, k, rq, rds), "few-token layouts")
+
+
 def test_hand_worked_superblock():
     f, x, dots, ssum, out = pins.golden_one_superblock()
     wg = to_dev(synth.pack_q4k(f))
