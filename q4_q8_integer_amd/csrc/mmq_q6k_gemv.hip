@@ -21,7 +21,10 @@
 //     (210 bytes) start only 2-byte aligned, and 16-byte loads at 4-byte
 //     aligned addresses measured slow (the address unit was ~65% busy), so
 //     the step's bytes of each row are first copied into the wave's LDS area
-//     with aligned 16-byte loads, and the block fields are read from LDS.
+//     with aligned 16-byte buffer loads that write LDS directly, and the
+//     block fields are read from LDS.  With enough steps per wave a second
+//     area takes the next step's copy while a step computes (it costs no
+//     registers).
 //   * A workgroup is 16 rows; its waves split the super-blocks, and the
 //     partial sums are added in a fixed order (the four quarter lanes of a
 //     row by a butterfly, then the waves in index order).
@@ -84,23 +87,30 @@ __device__ __forceinline__ void fold4(float& acc, float da, const float (&y)[4])
 }
 
 // One wave step: SW super-blocks of 16 rows.  The rows' bytes are copied
-// into the wave's LDS area with aligned 16-byte loads (row r's run of SW
-// blocks, from the 16-byte boundary below its first byte, at r * SEG), so
-// that every global load is an aligned, coalesced piece of contiguous rows;
-// the 2-byte-aligned block fields are then read from LDS as aligned dwords
+// into the wave's LDS area by buffer loads that write LDS directly (no
+// registers hold the copy): row r's run of SW blocks, from the 16-byte
+// boundary below its first byte, in aligned 16-byte pieces.  Slot i of the
+// area (16 bytes at 16*i) holds piece i % kSlots of row i / kSlots; the last
+// slot of a row is padding, which spreads the 16 rows' reads over the banks.
+// The 2-byte-aligned block fields are then read from LDS as aligned dwords
 // and shifted into place (see q6k_device.h).
 template <int SW>
 struct Seg {
-    static constexpr int kChunks = (SW * kQ6kBlockBytes + 14 + 15) / 16;  // per row
-    static constexpr int kBytes = kChunks * 16 + 16;   // row stride in LDS (+16: spreads banks)
-    static constexpr int kLoads = (16 * kChunks + 63) / 64;   // 16-byte pieces per lane
+    static constexpr int kChunks = (SW * kQ6kBlockBytes + 14 + 15) / 16;  // pieces per row
+    static constexpr int kSlots = kChunks + 1;
+    static constexpr int kBytes = 16 * kSlots;                           // row stride in LDS
+    static constexpr int kArea = 16 * kBytes;
+    static constexpr int kLoads = (16 * kSlots + 63) / 64;               // load instructions per step
 };
 
+constexpr int kBufferFlags = 0x00020000;   // word 3 of a raw buffer resource on gfx950
+// s_waitcnt operand: no vector-memory operation outstanding, the other
+// counters untouched
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // A 16-byte piece at byte offset a (a % 16 == 0) of the weights, reading
-// nothing at or past byte `total` (the last piece of the matrix may be
-// partial: its bytes past the end read as 0).
+// nothing at or past byte `total` (its bytes past the end read as 0).
 __device__ __forceinline__ uint4 load_piece(const uint8_t* __restrict__ w, int64_t a, int64_t total) {
-    if (a + 16 <= total) return *reinterpret_cast<const uint4*>(w + a);
     uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -116,31 +126,60 @@ __device__ __forceinline__ void lds_run(const uint8_t* base, int a, uint32_t (&v
     for (int i = 0; i < 5; ++i) v[i] = p[i];
 }
 
-// Global data of one wave step, as one lane holds it: its 16-byte pieces of
-// the 16 rows' bytes, and its token dword and scale word of every slot.
+// The weights of a workgroup's tile of rows: a buffer resource over its
+// whole 16-byte pieces, and the partial piece at its end (the tile's bytes
+// need not end on a 16-byte boundary), which a buffer load would read as
+// zeros and stage_patch copies in with 2-byte loads.
+struct Tile {
+    __amdgpu_buffer_rsrc_t rs;
+    const uint8_t* base;
+    int end;     // the tile's bytes
+    int rows;    // rows in the tile
+};
+
+// Issue the copy of the step at super-block s into `area`.  Pieces past a
+// row's end (a wave's last step may run over it) read the next row, past
+// the resource they read zeros; neither is used.
+template <int SW>
+__device__ __forceinline__ void stage_issue(const Tile& tl, int S, int s, int lane, uint8_t* area) {
+    typedef Seg<SW> G;
+#pragma unroll
+    for (int c = 0; c < G::kLoads; ++c) {
+        const int i = lane + 64 * c;
+        const int rr = i / G::kSlots, ch = min(i - rr * G::kSlots, G::kChunks - 1);
+        const int off = (((rr * S + s) * kQ6kBlockBytes) & ~15) + 16 * ch;
+        if (i < 16 * G::kSlots)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(tl.rs, (__attribute__((address_space(3))) void*)(area + 1024 * c),
+                                                     16, off, 0, 0, 0);
+    }
+}
+
+// After the copy of step s has landed: the tile's partial last piece, if
+// this step's run of the tile's last row covers it.
+template <int SW>
+__device__ __forceinline__ void stage_patch(const Tile& tl, int S, int s, int lane, uint8_t* area) {
+    typedef Seg<SW> G;
+    const int end16 = tl.end & ~15;
+    if (end16 == tl.end) return;
+    const int rr = tl.rows - 1;
+    const int ch = (end16 - (((rr * S + s) * kQ6kBlockBytes) & ~15)) >> 4;
+    if (lane == 0 && ch >= 0 && ch < G::kChunks)
+        *reinterpret_cast<uint4*>(area + rr * G::kBytes + 16 * ch) = load_piece(tl.base, end16, tl.end);
+}
+
+// The activations of one wave step, as one lane holds them: its token dword
+// and scale word of every slot.
 template <int N, int SW>
 struct Fetch {
-    uint4 pc[Seg<SW>::kLoads];
     uint32_t tq[N][SW], tw[N][SW];
 };
 
-// Issue the global loads of the step at super-block s (s may lie past the
-// wave's range: then it re-reads the range's last block and is not used).
+// Issue the activation loads of the step at super-block s (slots past the
+// wave's range re-read its last block and are not used).
 template <int N, int SW>
-__device__ __forceinline__ void fetch_step(Fetch<N, SW>& f, const uint8_t* __restrict__ w,
-                                           int64_t total, int row0, int M, int S,
-                                           const int8_t* __restrict__ q,
+__device__ __forceinline__ void fetch_step(Fetch<N, SW>& f, const int8_t* __restrict__ q,
                                            const uint32_t* __restrict__ ds, int K, int C, int s,
-                                           int last, int lane, int h, int e, int r) {
-    typedef Seg<SW> G;
-    s = min(s, last);
-#pragma unroll
-    for (int k = 0; k < G::kLoads; ++k) {
-        const int i = lane + 64 * k;
-        const int rr = i / G::kChunks, ch = i - rr * G::kChunks;
-        const int64_t a0 = (((int64_t)min(row0 + rr, M - 1) * S + s) * kQ6kBlockBytes) & ~(int64_t)15;
-        f.pc[k] = (i < 16 * G::kChunks) ? load_piece(w, a0 + 16 * ch, total) : make_uint4(0, 0, 0, 0);
-    }
+                                           int last, int h, int e, int r) {
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
         const int sb = min(s + j, last);
@@ -154,20 +193,14 @@ __device__ __forceinline__ void fetch_step(Fetch<N, SW>& f, const uint8_t* __res
     }
 }
 
-// Stage the fetched pieces in the wave's LDS area and compute the step.
+// Compute the step at super-block s from the wave's LDS copy.  rowS = the
+// lane's row times S (any row past the matrix reads a zero copy and is not
+// stored).
 template <int N, int SW>
-__device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, uint8_t* __restrict__ lds,
-                                             int64_t rowS, int s, int last, int lane, int h, int e,
-                                             int r, float* acc) {
+__device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, const uint8_t* __restrict__ lds,
+                                             int64_t rowS, int s, int last, int h, int e, int r,
+                                             float* acc) {
     typedef Seg<SW> G;
-#pragma unroll
-    for (int k = 0; k < G::kLoads; ++k) {
-        const int i = lane + 64 * k;
-        const int rr = i / G::kChunks, ch = i - rr * G::kChunks;
-        if (i < 16 * G::kChunks) *reinterpret_cast<uint4*>(lds + rr * G::kBytes + 16 * ch) = f.pc[k];
-    }
-    // LDS accesses of one wave complete in order: the reads below see the
-    // writes above, and the next step's writes come after these reads.
     const int64_t base0 = ((rowS + s) * kQ6kBlockBytes) & ~(int64_t)15;
     const uint8_t* row_lds = lds + r * G::kBytes;
 #pragma unroll
@@ -203,13 +236,15 @@ __device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, uint8_t* __r
     }
 }
 
-template <int N, int SW, bool H>
+// PF: two LDS areas per wave, the next step's copy (and activation loads)
+// in flight while a step computes.
+template <int N, int SW, bool PF, bool H>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint8_t* __restrict__ w,
                                                                       const int8_t* __restrict__ q,
                                                                       const uint32_t* __restrict__ ds,
                                                                       int M, int K,
                                                                       void* __restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t seg[];   // W x 16 x Seg<SW>::kBytes
+    extern __shared__ __attribute__((aligned(16))) uint8_t seg[];   // W x (PF ? 2 : 1) x Seg<SW>::kArea
     __shared__ float red[kMaxWaves][N][16];
 
     const int W = blockDim.x >> 6;
@@ -219,22 +254,52 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint
     const int row0 = blockIdx.x * 16;
     const int S = K >> 8, C = K >> 5;
     const int sb0 = (int)((int64_t)S * wv / W), sb1 = (int)((int64_t)S * (wv + 1) / W);
-    const int64_t total = (int64_t)M * S * kQ6kBlockBytes;
-    const int64_t rowS = (int64_t)min(row0 + r, M - 1) * S;
+    const int64_t rowS = (int64_t)(row0 + r) * S;
+
+    Tile tl;
+    tl.rows = min(16, M - row0);
+    tl.end = tl.rows * S * kQ6kBlockBytes;
+    tl.base = w + (int64_t)row0 * S * kQ6kBlockBytes;
+    tl.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tl.base), 0, tl.end & ~15, kBufferFlags);
 
     float acc[N];
 #pragma unroll
     for (int t = 0; t < N; ++t) acc[t] = 0.0f;
 
-    // One step at a time: its loads are issued, then it is staged and
-    // computed.  (Fetching the next step during the current one measured no
-    // faster: the wave count per SIMD, not one wave's latency, sets the rate.)
     const int last = sb1 - 1;
-    uint8_t* lds = seg + wv * 16 * Seg<SW>::kBytes;
-    for (int s = sb0; s < sb1; s += SW) {
-        Fetch<N, SW> f;
-        fetch_step<N, SW>(f, w, total, row0, M, S, q, ds, K, C, s, last, lane, h, e, r);
-        compute_step<N, SW>(f, lds, rowS, s, last, lane, h, e, r, acc);
+    constexpr int kAreas = PF ? 2 : 1;
+    uint8_t* lds = seg + wv * kAreas * Seg<SW>::kArea;
+    if constexpr (PF) {
+        Fetch<N, SW> nx;
+        if (sb0 < sb1) {
+            fetch_step<N, SW>(nx, q, ds, K, C, sb0, last, h, e, r);
+            stage_issue<SW>(tl, S, sb0, lane, lds);
+        }
+        for (int s = sb0, b = 0; s < sb1; s += SW, b ^= 1) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __builtin_amdgcn_sched_barrier(0);
+            uint8_t* cur = lds + b * Seg<SW>::kArea;
+            stage_patch<SW>(tl, S, s, lane, cur);
+            Fetch<N, SW> f = nx;
+            if (s + SW < sb1) {
+                fetch_step<N, SW>(nx, q, ds, K, C, s + SW, last, h, e, r);
+                stage_issue<SW>(tl, S, s + SW, lane, lds + (b ^ 1) * Seg<SW>::kArea);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step<N, SW>(f, cur, rowS, s, last, h, e, r, acc);
+        }
+    } else {
+        // LDS accesses of one wave complete in order: a step's reads finish
+        // before the next step's copy is issued (its math needs them).
+        for (int s = sb0; s < sb1; s += SW) {
+            Fetch<N, SW> f;
+            fetch_step<N, SW>(f, q, ds, K, C, s, last, h, e, r);
+            stage_issue<SW>(tl, S, s, lane, lds);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_patch<SW>(tl, S, s, lane, lds);
+            compute_step<N, SW>(f, lds, rowS, s, last, h, e, r, acc);
+        }
     }
 
 #pragma unroll
@@ -252,16 +317,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_q6k_gemv_kernel(const uint
     }
 }
 
-template <int N, int SW>
+template <int N, int SW, bool PF>
 hipError_t launch_sw(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                      void* out, bool half_out, hipStream_t stream, int waves) {
     const int rows = (m + 15) / 16;
-    const size_t lds = (size_t)waves * 16 * Seg<SW>::kBytes;
+    const size_t lds = (size_t)waves * (PF ? 2 : 1) * Seg<SW>::kArea;
     if (half_out)
-        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, true>), dim3(rows), dim3(64 * waves), lds, stream,
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, PF, true>), dim3(rows), dim3(64 * waves), lds, stream,
                            w, q, ds, m, k, out);
     else
-        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, false>), dim3(rows), dim3(64 * waves), lds, stream,
+        hipLaunchKernelGGL((mmq_q6k_gemv_kernel<N, SW, PF, false>), dim3(rows), dim3(64 * waves), lds, stream,
                            w, q, ds, m, k, out);
     return hipGetLastError();
 }
@@ -269,13 +334,20 @@ hipError_t launch_sw(const uint8_t* w, int m, int k, const int8_t* q, const uint
 template <int N>
 hipError_t launch_n(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                     void* out, bool half_out, hipStream_t stream) {
-    // Measured on the 28672 x 8192 q6_K matrix: 4 waves per row tile, steps
-    // of 2 super-blocks for one token and of 1 for more (whose vector work per
-    // byte is larger): 38 us at 1 token, 55 us at 7.
-    const int S = k / 256;
-    const int waves = S < kMaxWaves ? S : kMaxWaves;
-    return N == 1 ? launch_sw<N, 2>(w, m, k, q, ds, out, half_out, stream, waves)
-                  : launch_sw<N, 1>(w, m, k, q, ds, out, half_out, stream, waves);
+    // Measured on the 28672 x 8192 q6_K matrix (1-7 tokens, steps of 1, 2
+    // and 4 super-blocks, 1-4 waves, with and without the next step in
+    // flight): one token streams best in steps of 2 with about 1024 waves in
+    // all, more tokens (more vector work per byte) in steps of 1 with 4 waves
+    // per row tile; the second LDS area pays up to 4 tokens once a wave has
+    // at least 8 steps.
+    const int S = k / 256, rows = (m + 15) / 16;
+    int waves = N == 1 ? 1024 / rows : kMaxWaves;
+    waves = waves < 1 ? 1 : waves > kMaxWaves ? kMaxWaves : waves;
+    waves = waves > S ? S : waves;
+    constexpr int SW = N == 1 ? 2 : 1;
+    if constexpr (N <= 4)
+        if (S / (waves * SW) >= 8) return launch_sw<N, SW, true>(w, m, k, q, ds, out, half_out, stream, waves);
+    return launch_sw<N, SW, false>(w, m, k, q, ds, out, half_out, stream, waves);
 }
 
 }  // namespace

@@ -56,6 +56,19 @@ def test_q6k_ragged_shapes(n, m, k):
     run_case(f, x, "ragged")
 
 
+@pytest.mark.parametrize("k", [2304, 16640])
+@pytest.mark.parametrize("n", range(1, 9))
+def test_q6k_few_token_layouts(n, k):
+    """Every token count of the dot4 kernel with and without the second LDS
+    area: 9 super-blocks per row (one area) and 65 (the next step's copy in
+    flight up to 4 tokens; each wave's last step runs past its range).  37
+    rows leave a 5-row tile whose bytes end inside a 16-byte piece."""
+    m = 37
+    f = synth.random_q6k_fields(740 + 10 * n + k % 7, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(740 + 10 * n + k % 7, n, k, "outliers")
+    run_case(f, x, "few-token layouts", dots=False)
+
+
 def test_q6k_hand_worked_superblock():
     f, x, dots, out = pins.golden_q6k_one_superblock()
     wg = to_dev(synth.pack_q6k(f))
