@@ -25,6 +25,15 @@
 //     (halving the token bytes fetched per weight byte; measured: 8192 x
 //     28672 at 33 tokens 129 -> 120 us, 28672 x 8192 140 -> 139 us).
 //   * After the main loop the staging LDS is reused for the partial sums.
+//   * Up to 16 tokens (one tile) a second kernel, mmq_few_kernel, makes the
+//     same contraction from copies that bypass registers: each wave copies
+//     its weight rows and token tile per super-block into its own LDS area
+//     with buffer loads that write LDS directly (the scattered 8-byte
+//     weight loads above kept the address unit busy), in workgroups of 4
+//     waves, with the next step's copies in flight where a wave has enough
+//     steps (measured 28672 x 8192 / 8192 x 28672 at 16 tokens 58 / 55 ->
+//     49 / 50 us).  With 2-4 tiles its per-wave token copies cost more LDS
+//     than they save, so this kernel keeps 17-64 tokens.
 #include "internal.h"
 
 namespace mmq {
@@ -256,6 +265,257 @@ hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint3
     return hipLaunchKernel(f, dim3((unsigned)((m + 16 * RB - 1) / (16 * RB))), dim3(NT), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Up to 16 tokens: the copies bypass registers.  A workgroup is 16 rows and
+// 4 waves that split the super-blocks; per super-block a wave copies its 16
+// weight rows and the 16-token tile into its own LDS area with buffer loads
+// that write LDS directly, then runs the same MFMA and fold as above from
+// there.  The weight rows are read as 144-byte runs per row and step, but
+// with no register cost a second area can take the next step's copies while
+// a step computes.
+constexpr int kFewWaves = 4;
+constexpr int kFewNT = 64 * kFewWaves;
+constexpr int kBufferFlags = 0x00020000;   // word 3 of a raw buffer resource on gfx950
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0), other counters untouched
+
+// Copies are made by buffer loads that write LDS directly: lane i of a load
+// instruction writes 16 bytes at 16*i from its base, so every instruction
+// fills 64 consecutive 16-byte slots.  Every instruction is issued with all
+// lanes active (a load under a lane mask is not kept in place by the
+// compiler relative to the loads after it), so areas are whole instructions.
+//
+// A wave's copy of one super-block of its 16 weight rows: slot i holds
+// piece i % 11 of row i / 11 (pieces 9 and 10, and rows 16+, padding), so
+// rows sit 176 bytes apart and the 16 rows' reads of one field hit distinct
+// banks; 3 instructions.
+constexpr int kWSlots = 11;
+constexpr int kWLoads = 3;
+constexpr int kWBytes = 1024 * kWLoads;
+// A wave's copy of one super-block of a 16-token tile: slot 16t + s holds
+// piece s ^ t of token t (an XOR swizzle instead of padding, so the 16
+// tokens' reads of one piece hit distinct banks); 4 instructions.
+constexpr int kTLoads = 4;
+constexpr int kTBytes = 1024 * kTLoads;
+
+// A wave's LDS: the copies (two sets with PF, the next step's in flight
+// while a step computes) and the decoded activation scales of the step.
+template <int T, bool PF>
+struct alignas(16) FewWaveLds {
+    uint8_t w[PF ? 2 : 1][kWBytes];
+    uint8_t tok[PF ? 2 : 1][T][kTBytes];
+    float da[8][16 * T];     // [chunk][token]
+    float dass[8][16 * T];   // da*ssum, [chunk][token]
+};
+
+// LDS of a workgroup: the waves' areas, reused after the main loop for the
+// partial sums of the 4 waves (reduced in a fixed order).
+template <int T, bool PF>
+struct FewLds {
+    union {
+        FewWaveLds<T, PF> wave[kFewWaves];
+        v4f red[kFewWaves][T][64];
+    };
+};
+
+// Buffer resources over the tile's weight rows and all token rows.
+struct Sources {
+    __amdgpu_buffer_rsrc_t w, q;
+};
+
+// Issue the copies of super-block sb into a wave's set: the weights to
+// wdst, token tile tt to tdst + tt * kTBytes.
+template <int T>
+__device__ __forceinline__ void issue_copies(uint8_t* wdst, uint8_t* tdst, const Sources& src,
+                                             const int* woff, const int* toff, int sb) {
+#pragma unroll
+    for (int c = 0; c < kWLoads; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.w, (__attribute__((address_space(3))) void*)(wdst + 1024 * c),
+                                                 16, woff[c] + sb * kBlockBytes, 0, 0, 0);
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int c = 0; c < kTLoads; ++c)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                src.q, (__attribute__((address_space(3))) void*)(tdst + tt * kTBytes + 1024 * c), 16,
+                toff[tt * kTLoads + c] + sb * 256, 0, 0, 0);
+}
+
+template <int T, bool PF, bool H>
+__global__ __launch_bounds__(kFewNT) void mmq_few_kernel(const uint8_t* __restrict__ w,
+                                                       const int8_t* __restrict__ q,
+                                                       const uint32_t* __restrict__ ds,
+                                                       int M, int N, int K,
+                                                       void* __restrict__ out) {
+    __shared__ FewLds<T, PF> L;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int r = lane & 15, kg = lane >> 4;
+    const int row0 = blockIdx.x * 16;
+    const int S = K >> 8, C = K >> 5;
+    const int sb0 = (int)((int64_t)S * wv / kFewWaves), sb1 = (int)((int64_t)S * (wv + 1) / kFewWaves);
+    FewWaveLds<T, PF>& my = L.wave[wv];
+
+    // The tile's weight rows (rows past m, and the padding rows, read as
+    // zeros; the former are never stored) and all n token rows, as buffer
+    // resources; each lane's copy offsets without the super-block term
+    // (padded tokens repeat the last real one and are never stored).
+    Sources src;
+    src.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * S * kBlockBytes), 0,
+                                              min(16, M - row0) * S * kBlockBytes, kBufferFlags);
+    src.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q), 0, N * K, kBufferFlags);
+    int woff[kWLoads], toff[T * kTLoads];
+#pragma unroll
+    for (int c = 0; c < kWLoads; ++c) {
+        const int i = lane + 64 * c, rr = i / kWSlots, ch = min(i - rr * kWSlots, 8);
+        woff[c] = rr * S * kBlockBytes + 16 * ch;   // rr = 16 (the last 16 slots): past the tile
+    }
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int c = 0; c < kTLoads; ++c) {
+            const int tk = 4 * c + (lane >> 4), ch = (lane & 15) ^ tk;
+            toff[tt * kTLoads + c] = min(16 * tt + tk, N - 1) * K + 16 * ch;
+        }
+    // scale words of a step: lane handles (token 16tt + r, chunks kg and kg + 4)
+    auto words = [&](uint32_t (&wd)[T][2], int sb) {
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            const int tok = min(16 * tt + r, N - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) wd[tt][h] = ds[(int64_t)tok * C + sb * 8 + kg + 4 * h];
+        }
+    };
+
+    v4f acc[T], accb[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+        acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        accb[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // One super-block from the copies in set b.  LDS accesses of one wave
+    // complete in order: the table writes are seen by the reads after them,
+    // and a step's reads finish before later writes to the same bytes.
+    auto compute = [&](const uint32_t (&wd)[T][2], int b) {
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float da = half_bits_to_float(wd[tt][h]);
+                my.da[kg + 4 * h][16 * tt + r] = da;
+                my.dass[kg + 4 * h][16 * tt + r] = da * (float)(int16_t)(uint16_t)(wd[tt][h] >> 16);
+            }
+        const uint8_t* wrow = my.w[b] + r * (16 * kWSlots);
+        const uint4 hdr = *reinterpret_cast<const uint4*>(wrow);
+        int64_t bw[8];
+        float scf[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            int sc, mn;
+            scale_min(hdr.y, hdr.z, hdr.w, c, sc, mn);
+            scf[c] = (float)sc;
+            const uint2 x = *reinterpret_cast<const uint2*>(wrow + 16 + 32 * (c >> 1) + 8 * kg);
+            bw[c] = (c & 1) ? (int64_t)(((uint64_t)((x.y >> 4) & 0x0F0F0F0Fu) << 32) | ((x.x >> 4) & 0x0F0F0F0Fu))
+                            : (int64_t)(((uint64_t)(x.y & 0x0F0F0F0Fu) << 32) | (x.x & 0x0F0F0F0Fu));
+        }
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            // token r's bytes 32c + 8kg: piece 2c + (kg >> 1), swizzled
+            const uint8_t* arow = my.tok[b][tt] + 256 * r + 8 * (kg & 1);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int64_t a = *reinterpret_cast<const int64_t*>(arow + 16 * ((2 * c + (kg >> 1)) ^ r));
+                const float4 da4 = *reinterpret_cast<const float4*>(&my.da[c][16 * tt + 4 * kg]);
+                const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
+                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[c], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i] * scf[c], (float)D[i], accb[tt][i]);
+            }
+        }
+        // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
+        const float dmin = half_bits_to_float(hdr.x >> 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int sc, mn;
+            scale_min(hdr.y, hdr.z, hdr.w, 4 * j + kg, sc, mn);
+            const float bneg = -(dmin * (float)mn);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt)
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(my.dass[4 * j + kg][16 * tt + r], bneg, acc[tt], 0, 0, 0);
+        }
+        const float d = half_bits_to_float(hdr.x);
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][i] = fmaf(d, accb[tt][i], acc[tt][i]);
+            accb[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+
+    if constexpr (PF) {
+        uint32_t nx[T][2];
+        if (sb0 < sb1) {
+            words(nx, sb0);
+            issue_copies<T>(my.w[0], my.tok[0][0], src, woff, toff, sb0);
+        }
+        for (int sb = sb0, b = 0; sb < sb1; ++sb, b ^= 1) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t wd[T][2];
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt) {
+                wd[tt][0] = nx[tt][0];
+                wd[tt][1] = nx[tt][1];
+            }
+            if (sb + 1 < sb1) {
+                words(nx, sb + 1);
+                issue_copies<T>(my.w[b ^ 1], my.tok[b ^ 1][0], src, woff, toff, sb + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wd, b);
+        }
+    } else {
+        for (int sb = sb0; sb < sb1; ++sb) {
+            uint32_t wd[T][2];
+            words(wd, sb);
+            issue_copies<T>(my.w[0], my.tok[0][0], src, woff, toff, sb);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wd, 0);
+        }
+    }
+
+    __syncthreads();  // every wave is done with the areas the sums reuse
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) L.red[wv][tt][lane] = acc[tt];
+    __syncthreads();
+    // 64*T output values of 4 floats; the 4 waves share them, each summing
+    // the 4 partials in wave order.
+    for (int e = threadIdx.x; e < 64 * T; e += kFewNT) {
+        const int l = e & 63, tt = e >> 6;
+        v4f sum = L.red[0][tt][l];
+#pragma unroll
+        for (int v = 1; v < kFewWaves; ++v) sum += L.red[v][tt][l];
+        const int row = row0 + (l & 15);
+        if (row >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * tt + 4 * (l >> 4) + i;
+            if (tok < N) store_out<H>(out, (int64_t)tok * M + row, sum[i]);
+        }
+    }
+}
+
+template <int T, bool PF>
+hipError_t launch_few(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
+                    void* out, bool half_out, hipStream_t stream) {
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k, (void*)&out};
+    const void* f = half_out ? (const void*)mmq_few_kernel<T, PF, true>
+                             : (const void*)mmq_few_kernel<T, PF, false>;
+    return hipLaunchKernel(f, dim3((unsigned)((m + 15) / 16)), dim3(kFewNT), args, 0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
@@ -264,9 +524,13 @@ hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q
     // each wave has many steps (8192 x 28672: 14 per wave, 16 tokens 67 ->
     // 56 us) and costs occupancy when it has few (28672 x 8192: 4 per wave,
     // 63 -> 73 us); with 3-4 token tiles the second set does not fit.
+    if (n <= 16) {
+        // the second copy area pays from 16 super-blocks per wave (8192 x
+        // 28672: 28 per wave, 52 -> 50 us; 28672 x 8192: 8 per wave, 49 -> 59 us)
+        return (k / 256) / kFewWaves >= 16 ? launch_few<1, true>(w, m, k, q, ds, n, out, half_out, stream)
+                                           : launch_few<1, false>(w, m, k, q, ds, n, out, half_out, stream);
+    }
     const bool pf = (k / 256) / WAVES >= 8;
-    if (n <= 16) return pf ? launch_t<1, true>(w, m, k, q, ds, n, out, half_out, stream)
-                           : launch_t<1, false>(w, m, k, q, ds, n, out, half_out, stream);
     if (n <= 32) return pf ? launch_t<2, true>(w, m, k, q, ds, n, out, half_out, stream)
                            : launch_t<2, false>(w, m, k, q, ds, n, out, half_out, stream);
     if (n <= 48) return launch_t<3, false>(w, m, k, q, ds, n, out, half_out, stream);

@@ -82,6 +82,17 @@ def test_few_token_weight_layouts(n, k):
     check_fp32(got, oracle.out_f64(w, m, k, rq, rds), "few-token layouts")
 
 
+@pytest.mark.parametrize("k", [2304, 16640])
+@pytest.mark.parametrize("n", [9, 13, 16])
+def test_one_tile_mfma_kernel(n, k):
+    """9-16 tokens (one 16-token tile of the few-token MFMA path) with 9
+    super-blocks per row (one copy area per wave) and 65 (the next step's
+    copies in flight; 16-17 per wave); 37 rows leave a 5-row tile."""
+    f = synth.random_fields(760 + n + k % 7, 37, k, sc_zero_frac=0.1)
+    x = synth.random_activations(760 + n + k % 7, n, k, "outliers")
+    run_case(f, x, "one-tile MFMA")
+
+
 def test_hand_worked_superblock():
     f, x, dots, ssum, out = pins.golden_one_superblock()
     wg = to_dev(synth.pack_q4k(f))
