@@ -174,18 +174,45 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
 #pragma unroll
             for (int j = 0; j < 4; ++j) L.m.tok[wv][4 * j + (lane >> 4)][lane & 15] = f.tq[tt][j];
             const uint8_t* arow = reinterpret_cast<const uint8_t*>(L.m.tok[wv][r]) + 8 * kg;
+            // Software-pipelined over the chunks: the operand reads of chunk
+            // c + 1 and the MFMAs of chunk c are issued before the fold of
+            // chunk c - 1, so neither the LDS nor the matrix-core latency sits
+            // between dependent instructions.
+            int64_t an = *reinterpret_cast<const int64_t*>(arow);
+            float4 dn = *reinterpret_cast<const float4*>(&L.m.da[wv][0][16 * tt + 4 * kg]);
+            v4i Dp[RB];
+            float4 dp;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const int64_t a = *reinterpret_cast<const int64_t*>(arow + 32 * c);
-                const float4 da4 = *reinterpret_cast<const float4*>(&L.m.da[wv][c][16 * tt + 4 * kg]);
-                const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
+                const int64_t a = an;
+                const float4 da4 = dn;
+                if (c < 7) {
+                    an = *reinterpret_cast<const int64_t*>(arow + 32 * (c + 1));
+                    dn = *reinterpret_cast<const float4*>(&L.m.da[wv][c + 1][16 * tt + 4 * kg]);
+                }
+                v4i Dc[RB];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[rb][c], v4i{0, 0, 0, 0}, 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb)
+                    Dc[rb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[rb][c], v4i{0, 0, 0, 0}, 0, 0, 0);
+                if (c > 0) {
+                    const float dav[4] = {dp.x, dp.y, dp.z, dp.w};
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            accb[rb][tt][i] = fmaf(dav[i] * scf[rb][c - 1], (float)Dp[rb][i], accb[rb][tt][i]);
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) Dp[rb] = Dc[rb];
+                dp = da4;
+            }
+            {
+                const float dav[4] = {dp.x, dp.y, dp.z, dp.w};
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        accb[rb][tt][i] = fmaf(dav[i] * scf[rb][c], (float)D[i], accb[rb][tt][i]);
-                }
+                        accb[rb][tt][i] = fmaf(dav[i] * scf[rb][7], (float)Dp[rb][i], accb[rb][tt][i]);
             }
         }
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
@@ -423,14 +450,32 @@ __global__ __launch_bounds__(kFewNT) void mmq_few_kernel(const uint8_t* __restri
         for (int tt = 0; tt < T; ++tt) {
             // token r's bytes 32c + 8kg: piece 2c + (kg >> 1), swizzled
             const uint8_t* arow = my.tok[b][tt] + 256 * r + 8 * (kg & 1);
+            // software-pipelined over the chunks as in mmq_small_kernel
+            int64_t an = *reinterpret_cast<const int64_t*>(arow + 16 * ((kg >> 1) ^ r));
+            float4 dn = *reinterpret_cast<const float4*>(&my.da[0][16 * tt + 4 * kg]);
+            v4i Dp;
+            float4 dp;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const int64_t a = *reinterpret_cast<const int64_t*>(arow + 16 * ((2 * c + (kg >> 1)) ^ r));
-                const float4 da4 = *reinterpret_cast<const float4*>(&my.da[c][16 * tt + 4 * kg]);
-                const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
-                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[c], v4i{0, 0, 0, 0}, 0, 0, 0);
+                const int64_t a = an;
+                const float4 da4 = dn;
+                if (c < 7) {
+                    an = *reinterpret_cast<const int64_t*>(arow + 16 * ((2 * (c + 1) + (kg >> 1)) ^ r));
+                    dn = *reinterpret_cast<const float4*>(&my.da[c + 1][16 * tt + 4 * kg]);
+                }
+                const v4i Dc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw[c], v4i{0, 0, 0, 0}, 0, 0, 0);
+                if (c > 0) {
+                    const float dav[4] = {dp.x, dp.y, dp.z, dp.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i] * scf[c], (float)D[i], accb[tt][i]);
+                    for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i] * scf[c - 1], (float)Dp[i], accb[tt][i]);
+                }
+                Dp = Dc;
+                dp = da4;
+            }
+            {
+                const float dav[4] = {dp.x, dp.y, dp.z, dp.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accb[tt][i] = fmaf(dav[i] * scf[7], (float)Dp[i], accb[tt][i]);
             }
         }
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
