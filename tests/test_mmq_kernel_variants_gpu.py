@@ -1,8 +1,9 @@
 """Every float32 kernel meets the same bar on shapes outside its default
 range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
-binary16-MFMA kernel, default above 64 tokens and from 33 where the matrix
+binary16-MFMA kernel, default above 64 tokens and from 49 where the matrix
 gives it enough tiles, here also on few tokens), small (the few-token
-int8-MFMA kernel, default from 9 tokens, here also on fewer), pair (the
+int8-MFMA kernels, one-tile up to 16 tokens and multi-tile above, default
+from 9 tokens, here also on fewer), pair (the
 chunk-pair int8-MFMA kernel, kept for comparison) and gemv (the vector-ALU
 dot4 kernel, default up to 8 tokens).  Each forced kernel's binary16 output
 must equal its float32 output rounded to nearest-even, bit for bit.  The
