@@ -19,9 +19,10 @@
 // (int multiply by sc, convert, FMA) against one here; the vector ALU, not the
 // matrix core, is what bounds this operation on gfx950.
 //
-// Tiling: workgroup 128 rows x 128 tokens; 4 consumer waves of 64x64 (2x2
-// tiles of 32x32) and 4 producer waves; k is staged 128 at a time (half a
-// super-block, 4 chunks) in two alternating LDS stages (~141 KB, one
+// Tiling: workgroup 128 rows x 128 tokens (x 64 tokens where 128-token
+// tiles would leave CUs idle); 8 consumer waves of 64 rows x 32 tokens (32 x
+// 32 with 64-token tiles) and 8 producer waves; k is staged 128 at a time
+// (half a super-block, 4 chunks) in two alternating LDS stages (~141 KB, one
 // workgroup per CU).  Producers convert each weight and each activation once
 // per workgroup into binary16 operand slots laid out
 // [chunk][k-half][lane-half][row or token][8 halves], so that the 32 lanes of
@@ -145,12 +146,15 @@ struct Src {
     int word[SPC];           // scale-word offsets
 };
 
+// TB: tokens of the workgroup tile (BN, or BN / 2 where full tiles would
+// leave CUs idle); the LDS stage keeps its BN-token size.
+template <int TB>
 __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                          const int8_t* __restrict__ q,
                                          const uint32_t* __restrict__ ds, int pt, int row0,
                                          int tok0, int M, int N, int K) {
     const int S = K >> 8, C = K >> 5;
-    const int rows = min(BM, M - row0), toks = min(BN, N - tok0);
+    const int rows = min(BM, M - row0), toks = min(TB, N - tok0);
     const int row_bytes = S * kBlockBytes;
     p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * row_bytes), 0,
                                             rows * row_bytes, kBufferFlags);
@@ -167,7 +171,7 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
         p.wq[rr] = p.wh[rr] + 16 + 32 * pl + 16 * gg;
     }
 #pragma unroll
-    for (int rr = 0; rr < APC; ++rr) {
+    for (int rr = 0; rr < TB * 8 / PT; ++rr) {
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
@@ -175,12 +179,15 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     }
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr) {
-        const int i = pt + rr * PT;
-        const int tok = i & (BN - 1), cl = i >> 7;
+        // with TB < BN only the first TB * 4 producer threads hold a word
+        // (the others re-read the last one and store nothing)
+        const int i = TB == BN ? pt + rr * PT : min(pt + rr * PT, TB * 4 - 1);
+        const int tok = i % TB, cl = i / TB;
         p.word[rr] = (min(tok, toks - 1) * C + cl) * 4;
     }
 }
 
+template <int TB>
 __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     const int boff = (st >> 1) * kBlockBytes, qoff = boff + (st & 1) * 64;
@@ -190,13 +197,14 @@ __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
         r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
     }
 #pragma unroll
-    for (int rr = 0; rr < APC; ++rr)
+    for (int rr = 0; rr < TB * 8 / PT; ++rr)
         r.y[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y[rr], 128 * st, 0));
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr)
         r.word[rr] = __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word[rr], 16 * st, 0);
 }
 
+template <int TB>
 __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
     const int hs = st & 1;
 #pragma unroll
@@ -234,7 +242,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         }
     }
 #pragma unroll
-    for (int rr = 0; rr < APC; ++rr) {
+    for (int rr = 0; rr < TB * 8 / PT; ++rr) {
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
@@ -250,10 +258,12 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr) {
         const int i = pt + rr * PT;
-        const int tok = i & (BN - 1), cl = i >> 7;
+        const int tok = i % TB, cl = i / TB;
         const float da = half_bits_to_float(r.word[rr]);
-        sg.Da[cl][tok] = da;
-        sg.Dass[cl][tok] = da * (float)(int16_t)(uint16_t)(r.word[rr] >> 16);  // exact
+        if (TB == BN || i < TB * 4) {
+            sg.Da[cl][tok] = da;
+            sg.Dass[cl][tok] = da * (float)(int16_t)(uint16_t)(r.word[rr] >> 16);  // exact
+        }
     }
 }
 
@@ -262,7 +272,9 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
 // chunk multiplies instead of accumulating), HS = 1 ends it with the d fold.
 // Per chunk all eight MFMAs are issued before any of the epilogue, so each
 // tile's FMAs find their MFMA results done instead of waiting on them.
-template <int HS>
+// RT: 32-row tiles per wave (2 with 128-token tiles, 1 with 64: the 8
+// waves then cover 4 x 32 rows x 2 x 32 tokens); r0 = the wave's first row.
+template <int HS, int RT>
 __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, int g, int l32,
                                               v16f (&acc)[2][NTW], v16f (&accb)[2][NTW]) {
 #pragma unroll
@@ -277,25 +289,25 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
             da[nt] = sg.Da[cl][t];
         }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int rr = wm * 64 + rt * 32 + l32;
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rr = wm * 32 * RT + rt * 32 + l32;
             a0[rt] = __builtin_bit_cast(v8h, sg.A[cl][0][g][rr]);
             a1[rt] = __builtin_bit_cast(v8h, sg.A[cl][1][g][rr]);
         }
         v16f pr[2][NTW];
         const v16f zero = {};
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
                 pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[rt], b0[nt], zero, 0, 0, 0);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
                 pr[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[rt], b1[nt], pr[rt][nt], 0, 0, 0);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 if (HS == 0 && cl == 0)
@@ -311,11 +323,11 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
     for (int cp = 0; cp < CS / 2; ++cp) {
         float ca[2], cb[NTW];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 64 + rt * 32 + l32];
+        for (int rt = 0; rt < RT; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 32 * RT + rt * 32 + l32];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 32 * NTW + nt * 32 + l32];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
                 acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
@@ -323,10 +335,10 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
     // end of a super-block: out += d * acc_b
     if (HS == 1) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float4 d4 = *reinterpret_cast<const float4*>(&sg.D[wm * 64 + rt * 32 + 8 * jj + 4 * g]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sg.D[wm * 32 * RT + rt * 32 + 8 * jj + 4 * g]);
                 const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -342,7 +354,7 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 // binary16 operand slots).  Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
-template <bool H>
+template <int TB, bool H>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 
     const int tid = threadIdx.x;
     const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
-    const int row0 = bm * BM, tok0 = bn * BN;
+    const int row0 = bm * BM, tok0 = bn * TB;
     const int stages = K >> 7;
 
     if (tid >= CT) {
@@ -362,19 +374,19 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
         // wait on them).
         const int pt = tid - CT;
         Src src;
-        init_src(src, w, q, ds, pt, row0, tok0, M, N, K);
+        init_src<TB>(src, w, q, ds, pt, row0, tok0, M, N, K);
         Raw ra, rb;
-        load_stage(ra, src, 0);
+        load_stage<TB>(ra, src, 0);
         // k is a multiple of 256, so the stage count is even and the loop
         // runs whole (even, odd) pairs.  Every load is unconditional (the
         // last prefetch re-reads the final stage), which lets the compiler
         // wait only for the older register set.
         for (int it = 0; it < stages; it += 2) {
-            load_stage(rb, src, it + 1);
-            convert_stage(ra, stage[0], pt, it);
+            load_stage<TB>(rb, src, it + 1);
+            convert_stage<TB>(ra, stage[0], pt, it);
             __syncthreads();
-            load_stage(ra, src, min(it + 2, stages - 1));
-            convert_stage(rb, stage[1], pt, it + 1);
+            load_stage<TB>(ra, src, min(it + 2, stages - 1));
+            convert_stage<TB>(rb, stage[1], pt, it + 1);
             __syncthreads();
         }
         __syncthreads();  // the consumers' last stage
@@ -383,7 +395,9 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 
     // ----------------------------------------------------------- consumer
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    constexpr int RT = TB / 64;                 // 32-row tiles per wave
+    constexpr int RW = 128 / (32 * RT);         // waves along the rows
+    const int wm = wave % RW, wn = wave / RW;
     const int g = lane >> 5, l32 = lane & 31;
 
     v16f acc[2][NTW], accb[2][NTW];
@@ -398,22 +412,22 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
     // even stages, stage[1] odd ones.  The barriers pair with the producers'.
     __syncthreads();
     for (int st = 0; st < stages; st += 2) {
-        consume_stage<0>(stage[0], wm, wn, g, l32, acc, accb);
+        consume_stage<0, RT>(stage[0], wm, wn, g, l32, acc, accb);
         __syncthreads();
-        consume_stage<1>(stage[1], wm, wn, g, l32, acc, accb);
+        consume_stage<1, RT>(stage[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
     }
 
     const bool vec = (M & 3) == 0;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int tok = tok0 + wn * 32 * NTW + nt * 32 + l32;
             if (tok >= N) continue;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int o = row0 + wm * 64 + rt * 32 + 8 * jj + 4 * g;
+                const int o = row0 + wm * 32 * RT + rt * 32 + 8 * jj + 4 * g;
                 const int64_t idx = (int64_t)tok * M + o;
                 if (vec && o + 3 < M) {
                     store_out4<H>(out, idx, acc[rt][nt][4 * jj], acc[rt][nt][4 * jj + 1],
@@ -432,10 +446,19 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                                int n, void* out, bool half_out, hipStream_t stream) {
     int tiles_m = (m + BM - 1) / BM;
-    const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    // Tiles of 128 tokens, or of 64 where 128-token tiles would not give
+    // every CU one: the 7B layer set at 512 tokens 99 -> 88 us per
+    // projection (its 4096-row projections have 128 tiles of 128 tokens);
+    // with enough tiles the halved tiles lose (2630-token FFN 565 -> 690 us:
+    // each converts the whole weight tile for half the tokens).
+    const int64_t full = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    const bool half_tiles = full < 256;
+    const int tb = half_tiles ? BN / 2 : BN;
+    const int64_t tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_out ? (const void*)mmq_f16_kernel<true> : (const void*)mmq_f16_kernel<false>;
+    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true> : (const void*)mmq_f16_kernel<BN / 2, false>)
+                               : (half_out ? (const void*)mmq_f16_kernel<BN, true> : (const void*)mmq_f16_kernel<BN, false>);
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 
