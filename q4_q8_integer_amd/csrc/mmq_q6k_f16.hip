@@ -157,7 +157,7 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * rbytes), 0,
                                             p.extent, kBufferFlags);
     p.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q + (int64_t)tok0 * K), 0,
-                                            toks * K, kBufferFlags);
+                                            (int)((uint32_t)toks * (uint32_t)K), kBufferFlags);   // up to 2^31 bytes
     p.ds = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ds + (int64_t)tok0 * C), 0,
                                              toks * C * 4, kBufferFlags);
     // q8 piece pt: token pt & 127, 16-byte piece pt >> 7 of the stage's 64 bytes
