@@ -65,8 +65,10 @@ def build_workload(name: str):
         return ({"workload": "weight-bound q6_K W[%dx%d] at N=%d (10%% of scale groups sc=0)"
                              % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
                 {"x": synth.q6k_activation("wide_in", n)}, [("wide_in", f, "x")])
-    if name.startswith("r_wide_in") or name.startswith("r_wide_out"):
+    if name.startswith("r_"):
         desc, inputs, mats = build_workload(name[2:])
+        if any(not isinstance(f, synth.Q4KFields) for _, f, _ in mats):
+            raise SystemExit("the repacked layout is for q4_K weights")
         desc = dict(desc, repacked=True,
                     workload=desc["workload"] + ", weights repacked at load time (q4k_repack)")
         return desc, inputs, mats

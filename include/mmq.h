@@ -189,7 +189,8 @@ int mmq_q6k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
                       const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
 
 /*
- * q4k_repack - load-time re-layout of q4_K weights for the few-token path.
+ * q4k_repack - load-time re-layout of q4_K weights (read by the few-token
+ * dot4 kernel and the binary16-MFMA prefill kernel).
  * (The pages name a "load-time B pre-expansion" round and a scale
  * "predecode" round, r18 and r35 in the r17 and r31 pages' notes; the
  * layout is this library's.)
@@ -212,8 +213,13 @@ int q4k_repack(const void *w, int64_t m, int64_t k, void *wr, hipStream_t stream
  * q4k_repack of the same m, k).  For n <= 8 it runs the vector-ALU dot4
  * kernel with the same arithmetic, in the same order, as
  * mmq_q4k_q8_fp32out's kernel for that n, so the two results are equal bit
- * for bit; more tokens run as slices of 8, each reading the weights again.
- * Other arguments, errors and empty calls as for mmq_q4k_q8_fp32out.
+ * for bit.  Above 16 tokens, where the tiles fill the CUs (at least 160
+ * tiles of 128 rows x 128 tokens) or n > 40, it runs the binary16-MFMA
+ * kernel on the records, again with mmq_q4k_q8_fp32out's arithmetic and
+ * order for that kernel (equal bit for bit where mmq_q4k_q8_fp32out takes it,
+ * n > 64).  Other token counts run as slices of 8 tokens, each reading the
+ * weights again.  Other arguments, errors and empty calls as for
+ * mmq_q4k_q8_fp32out.
  */
 int mmq_q4kr_q8_fp32out(const void *wr, int64_t m, int64_t k, const int8_t *q,
                         const uint32_t *ds, int64_t n, float *out, hipStream_t stream);

@@ -61,6 +61,11 @@ hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
                                const uint32_t* ds, int n, void* out, bool half_out,
                                hipStream_t stream);
 
+// The binary16-MFMA kernel on q4k_repack records (same arithmetic and order
+// as launch_mmq_fp32_f16, so the same float32 result bit for bit).
+hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
+                                        const uint32_t* ds, int n, float* out, hipStream_t stream);
+
 // Two-term fold, out[t][o], for n <= 64 tokens: weight-streaming int8-MFMA
 // kernel (8 waves per 16 rows, each over a slice of k).
 hipError_t launch_mmq_fp32_small(const uint8_t* w, int m, int k, const int8_t* q,

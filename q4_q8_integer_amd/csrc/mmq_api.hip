@@ -256,6 +256,15 @@ int mmq_q4kr_q8_fp32out(const void* wr, int64_t m, int64_t k, const int8_t* q,
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
+    // Above 16 tokens the binary16-MFMA kernel on the records, where it has
+    // tiles enough for the CUs (>= 160 of 128 x 128) or the slices would be
+    // many (> 40 tokens).  Measured per call: 28672 x 8192 (224 tiles) at 9 /
+    // 16 / 24 tokens 60 / 76 / 121 us in slices against 75 us; 8192 x 28672
+    // (64 tiles) at 33 / 48 tokens 197 / 273 us in slices against 221 us.
+    const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    if (n > 16 && (f16_tiles >= 160 || n > 40))
+        return hip_status(mmq::launch_mmq_fp32_f16_repacked(static_cast<const uint8_t*>(wr), (int)m, (int)k,
+                                                            q, ds, (int)n, out, stream));
     // Up to 8 tokens per launch; more tokens run as slices of 8 (each reads
     // the weights again: this layout serves the few-token path).  Slice
     // starts stay 16-byte aligned: 8 rows of q, ds and out are 8k, k/4 and

@@ -28,6 +28,12 @@
 // [chunk][k-half][lane-half][row or token][8 halves], so that the 32 lanes of
 // a half-wave read 32 consecutive 16-byte slots (conflict-free) and each
 // staging store is a run of consecutive slots.
+//
+// The same kernel reads q4k_repack records (REP): per stage and piece the
+// producers load the row's d | dmin dword and its chunk pair's scale dword
+// (sc and m as bytes) in place of the 16-byte block header, and skip the
+// 6-bit scale decode; everything after the scales is the same arithmetic, so
+// the two layouts give the same result bit for bit.
 #include "internal.h"
 
 namespace mmq {
@@ -128,7 +134,8 @@ struct Stage {
 
 // Raw global data of one stage, as one producer thread loads it.
 struct Raw {
-    uint4 hdr[WPC], qs[WPC]; // weight pieces: block header + 16 nibble bytes
+    uint4 hdr[WPC], qs[WPC]; // weight pieces: block header + 16 nibble bytes (repacked
+                             // records: hdr.x = d | dmin << 16, hdr.y = the scale dword)
     uint4 y[APC];            // activation pieces of 16 q8 bytes
     uint32_t word[SPC];      // activation scale words
 };
@@ -141,14 +148,17 @@ struct Raw {
 // zeros instead of faulting.
 struct Src {
     __amdgpu_buffer_rsrc_t w, q, ds;
-    int wh[WPC], wq[WPC];    // weight piece offsets: block header, nibbles
+    int wh[WPC], wq[WPC];    // weight piece offsets: block header (repacked: d | dmin), nibbles
+    int wsc[WPC];            // repacked records: scale dword
     int y[APC];              // q8 piece offsets
     int word[SPC];           // scale-word offsets
 };
 
 // TB: tokens of the workgroup tile (BN, or BN / 2 where full tiles would
 // leave CUs idle); the LDS stage keeps its BN-token size.
-template <int TB>
+// REP: w holds q4k_repack records (16-row tiles, one 2368-byte record per
+// tile and super-block) instead of q4_K rows.
+template <int TB, bool REP>
 __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                          const int8_t* __restrict__ q,
                                          const uint32_t* __restrict__ ds, int pt, int row0,
@@ -156,8 +166,14 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     const int S = K >> 8, C = K >> 5;
     const int rows = min(BM, M - row0), toks = min(TB, N - tok0);
     const int row_bytes = S * kBlockBytes;
-    p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * row_bytes), 0,
-                                            rows * row_bytes, kBufferFlags);
+    // repacked: the workgroup's 16-row tiles (up to 8), S records each
+    const int tile_bytes = S * kRepackRecordBytes, ntile = (rows + 15) >> 4;
+    if (REP)
+        p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)(row0 >> 4) * tile_bytes), 0,
+                                                ntile * tile_bytes, kBufferFlags);
+    else
+        p.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + (int64_t)row0 * row_bytes), 0,
+                                                rows * row_bytes, kBufferFlags);
     p.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q + (int64_t)tok0 * K), 0,
                                             (int)((uint32_t)toks * (uint32_t)K), kBufferFlags);   // up to 2^31 bytes
     p.ds = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ds + (int64_t)tok0 * C), 0,
@@ -167,8 +183,17 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
         const int i = pt + rr * PT;
         const int row = (i & 15) | ((i >> 6) << 4);
         const int j = (i >> 4) & 3, pl = j >> 1, gg = j & 1;
-        p.wh[rr] = min(row, rows - 1) * row_bytes;
-        p.wq[rr] = p.wh[rr] + 16 + 32 * pl + 16 * gg;
+        if (REP) {
+            // record: [0,64) d | dmin dword r; [64,320) scale dword 16p + r;
+            // [320,2368) qs bytes 32p + 16h .. +15 of row r at 320 + 512p + 256h + 16r
+            const int base = min(row >> 4, ntile - 1) * tile_bytes, r = row & 15;
+            p.wh[rr] = base + 4 * r;
+            p.wsc[rr] = base + 64 + 64 * pl + 4 * r;
+            p.wq[rr] = base + 320 + 512 * pl + 256 * gg + 16 * r;
+        } else {
+            p.wh[rr] = min(row, rows - 1) * row_bytes;
+            p.wq[rr] = p.wh[rr] + 16 + 32 * pl + 16 * gg;
+        }
     }
 #pragma unroll
     for (int rr = 0; rr < TB * 8 / PT; ++rr) {
@@ -187,14 +212,25 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     }
 }
 
-template <int TB>
+template <int TB, bool REP>
 __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    const int boff = (st >> 1) * kBlockBytes, qoff = boff + (st & 1) * 64;
+    if (REP) {
+        // stage st: record st / 2, chunk pairs 2 (st & 1) and 2 (st & 1) + 1
+        const int roff = (st >> 1) * kRepackRecordBytes, hs = st & 1;
 #pragma unroll
-    for (int rr = 0; rr < WPC; ++rr) {
-        r.hdr[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wh[rr], boff, 0));
-        r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
+        for (int rr = 0; rr < WPC; ++rr) {
+            r.hdr[rr].x = __builtin_amdgcn_raw_buffer_load_b32(p.w, p.wh[rr], roff, 0);
+            r.hdr[rr].y = __builtin_amdgcn_raw_buffer_load_b32(p.w, p.wsc[rr], roff + 128 * hs, 0);
+            r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], roff + 1024 * hs, 0));
+        }
+    } else {
+        const int boff = (st >> 1) * kBlockBytes, qoff = boff + (st & 1) * 64;
+#pragma unroll
+        for (int rr = 0; rr < WPC; ++rr) {
+            r.hdr[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wh[rr], boff, 0));
+            r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
+        }
     }
 #pragma unroll
     for (int rr = 0; rr < TB * 8 / PT; ++rr)
@@ -204,7 +240,7 @@ __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
         r.word[rr] = __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word[rr], 16 * st, 0);
 }
 
-template <int TB>
+template <int TB, bool REP>
 __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
     const int hs = st & 1;
 #pragma unroll
@@ -215,8 +251,14 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         const uint4 hdr = r.hdr[rr], qs = r.qs[rr];
         const int c0 = 2 * (2 * hs + pl);
         int sclo, schi, mn;
-        scale_min(hdr.y, hdr.z, hdr.w, c0, sclo, mn);
-        scale_min(hdr.y, hdr.z, hdr.w, c0 + 1, schi, mn);
+        if (REP) {
+            // the scale dword of chunk pair c0/2: sc[c0] | sc[c0+1] << 8 | m[c0] << 16 | m[c0+1] << 24
+            sclo = hdr.y & 0xFF;
+            schi = (hdr.y >> 8) & 0xFF;
+        } else {
+            scale_min(hdr.y, hdr.z, hdr.w, c0, sclo, mn);
+            scale_min(hdr.y, hdr.z, hdr.w, c0 + 1, schi, mn);
+        }
         const uint32_t sl2 = f16x2_splat((float)sclo), nl2 = f16x2_splat(-1024.0f * sclo);
         const uint32_t sh2 = f16x2_splat(0.0625f * schi), nh2 = f16x2_splat(-64.0f * schi);
         uint32_t lo[8], hi[8];
@@ -236,7 +278,10 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
             const float d = half_bits_to_float(hdr.x);
             const float dmin = half_bits_to_float(hdr.x >> 16);
             int sc, m;
-            scale_min(hdr.y, hdr.z, hdr.w, 4 * hs + j, sc, m);
+            if (REP)
+                m = (hdr.y >> (16 + 8 * gg)) & 0xFF;   // chunk 4 hs + j = c0 + gg
+            else
+                scale_min(hdr.y, hdr.z, hdr.w, 4 * hs + j, sc, m);
             sg.D[row] = d;
             sg.CA[j][row] = -(dmin * (float)m);
         }
@@ -354,7 +399,7 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 // binary16 operand slots).  Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
-template <int TB, bool H>
+template <int TB, bool H, bool REP>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
@@ -374,19 +419,19 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
         // wait on them).
         const int pt = tid - CT;
         Src src;
-        init_src<TB>(src, w, q, ds, pt, row0, tok0, M, N, K);
+        init_src<TB, REP>(src, w, q, ds, pt, row0, tok0, M, N, K);
         Raw ra, rb;
-        load_stage<TB>(ra, src, 0);
+        load_stage<TB, REP>(ra, src, 0);
         // k is a multiple of 256, so the stage count is even and the loop
         // runs whole (even, odd) pairs.  Every load is unconditional (the
         // last prefetch re-reads the final stage), which lets the compiler
         // wait only for the older register set.
         for (int it = 0; it < stages; it += 2) {
-            load_stage<TB>(rb, src, it + 1);
-            convert_stage<TB>(ra, stage[0], pt, it);
+            load_stage<TB, REP>(rb, src, it + 1);
+            convert_stage<TB, REP>(ra, stage[0], pt, it);
             __syncthreads();
-            load_stage<TB>(ra, src, min(it + 2, stages - 1));
-            convert_stage<TB>(rb, stage[1], pt, it + 1);
+            load_stage<TB, REP>(ra, src, min(it + 2, stages - 1));
+            convert_stage<TB, REP>(rb, stage[1], pt, it + 1);
             __syncthreads();
         }
         __syncthreads();  // the consumers' last stage
@@ -443,22 +488,42 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 
 }  // namespace
 
+// Token-tile width and tile count of a launch: tiles of 128 tokens, or of 64
+// where 128-token tiles would not give every CU one (the 7B layer set at 512
+// tokens 99 -> 88 us per projection: its 4096-row projections have 128 tiles
+// of 128 tokens); with enough tiles the halved tiles lose (2630-token FFN
+// 565 -> 690 us: each converts the whole weight tile for half the tokens).
+static void tile_shape(int m, int n, int& tiles_m, bool& half_tiles, int64_t& tiles) {
+    tiles_m = (m + BM - 1) / BM;
+    const int64_t full = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    half_tiles = full < 256;
+    const int tb = half_tiles ? BN / 2 : BN;
+    tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
+}
+
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                                int n, void* out, bool half_out, hipStream_t stream) {
-    int tiles_m = (m + BM - 1) / BM;
-    // Tiles of 128 tokens, or of 64 where 128-token tiles would not give
-    // every CU one: the 7B layer set at 512 tokens 99 -> 88 us per
-    // projection (its 4096-row projections have 128 tiles of 128 tokens);
-    // with enough tiles the halved tiles lose (2630-token FFN 565 -> 690 us:
-    // each converts the whole weight tile for half the tokens).
-    const int64_t full = (int64_t)tiles_m * ((n + BN - 1) / BN);
-    const bool half_tiles = full < 256;
-    const int tb = half_tiles ? BN / 2 : BN;
-    const int64_t tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
+    int tiles_m;
+    bool half_tiles;
+    int64_t tiles;
+    tile_shape(m, n, tiles_m, half_tiles, tiles);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true> : (const void*)mmq_f16_kernel<BN / 2, false>)
-                               : (half_out ? (const void*)mmq_f16_kernel<BN, true> : (const void*)mmq_f16_kernel<BN, false>);
+    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true, false> : (const void*)mmq_f16_kernel<BN / 2, false, false>)
+                               : (half_out ? (const void*)mmq_f16_kernel<BN, true, false> : (const void*)mmq_f16_kernel<BN, false, false>);
+    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+}
+
+hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
+                                        const uint32_t* ds, int n, float* out, hipStream_t stream) {
+    int tiles_m;
+    bool half_tiles;
+    int64_t tiles;
+    tile_shape(m, n, tiles_m, half_tiles, tiles);
+    void* args[] = {(void*)&wr, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
+                    (void*)&tiles_m, (void*)&out};
+    const void* f = half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true>
+                               : (const void*)mmq_f16_kernel<BN, false, true>;
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 

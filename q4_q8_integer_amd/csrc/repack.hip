@@ -1,4 +1,5 @@
-// repack.hip - load-time re-layout of q4_K weights for the few-token path.
+// repack.hip - load-time re-layout of q4_K weights (few-token dot4 kernel,
+// and the binary16-MFMA prefill kernel's producers).
 //
 // The pages name a "load-time B pre-expansion" round and a later scale
 // "predecode" round (the r17 page's and the r31 page's neighbours), not a
@@ -9,8 +10,9 @@
 //   [320, 2368)  16 bytes at 320 + 512p + 256h + 16r: qs bytes 32p + 16h .. +15 of row r
 // Rows past m are zero.  A wave of the dot4 kernel then reads a step as one
 // contiguous run, with every lane's data at a fixed offset, and takes its
-// 6-bit scales as bytes (no bit-field decode).  148 bytes per row and
-// super-block against 144.
+// 6-bit scales as bytes (no bit-field decode); the binary16 kernel's
+// producers likewise read a chunk pair's (sc, m) as one dword.  148 bytes per
+// row and super-block against 144.
 #include "internal.h"
 
 namespace mmq {
