@@ -295,6 +295,39 @@ int oracle_q4k_repack(const uint8_t *w, int64_t m, int64_t k, uint8_t *wr)
     return 0;
 }
 
+/* ------------------------------------------------------ q8 operand tiles */
+/* The q8 codes laid out as binary16 matrix-core operands (the pages name a
+ * later "quantize-transpose prepass" that changed the activation side's
+ * layout at its root, r22 page, section 5; no layout is printed, this one is
+ * the library's: the binary16 matmul kernel's LDS operand order).  Tokens in tiles of 128 and k in stages of 128: one block of
+ * 16 x 128 slots of 8 binary16 values (32768 bytes) per (tile T, stage s),
+ * blocks tile-major.  Slot ((c * 2 + h) * 2 + g) * 128 + tt of block (T, s)
+ * holds the codes of token 128 T + tt at k = 128 s + 32 c + 16 g + 8 h + e for
+ * e = 0, 2, 1, 3, 4, 6, 5, 7 (in that order); each code is exact in binary16.
+ * Tokens past n hold zeros. */
+int oracle_q8_tiles(const int8_t *q8, int64_t n, int64_t k, uint16_t *qt)
+{
+    static const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    if (n < 0 || k < 0 || k % 128)
+        return -1;
+    const int64_t tiles = (n + 127) / 128, stages = k / 128;
+    for (int64_t T = 0; T < tiles; T++)
+        for (int64_t s = 0; s < stages; s++)
+            for (int c = 0; c < 4; c++)
+                for (int h = 0; h < 2; h++)
+                    for (int g = 0; g < 2; g++)
+                        for (int tt = 0; tt < 128; tt++) {
+                            const int64_t row = (c * 2 + h) * 2 + g;
+                            uint16_t *slot = qt + (((T * stages + s) * 16 + row) * 128 + tt) * 8;
+                            const int64_t t = 128 * T + tt;
+                            for (int e = 0; e < 8; e++) {
+                                const int64_t kk = 128 * s + 32 * c + 16 * g + 8 * h + order[e];
+                                slot[e] = t < n ? oracle_f32_to_f16((float)q8[t * k + kk]) : 0;
+                            }
+                        }
+    return 0;
+}
+
 /* ----------------------------------------------------------------- output */
 /* out[t][o] in float64, chunk order, from the two-term fold. */
 int oracle_out_f64(const uint8_t *w, int64_t m, int64_t k, const int8_t *q8,

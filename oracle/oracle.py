@@ -35,6 +35,8 @@ def _declare(lib):
     lib.oracle_out_f64.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_i64, c_p]
     lib.oracle_q4k_repack.argtypes = [c_p, c_i64, c_i64, c_p]
     lib.oracle_q4k_repack.restype = ctypes.c_int
+    lib.oracle_q8_tiles.argtypes = [c_p, c_i64, c_i64, c_p]
+    lib.oracle_q8_tiles.restype = ctypes.c_int
     lib.oracle_silu_mul.argtypes = [c_p, c_p, c_i64, c_p]
     lib.oracle_silu_mul.restype = None
     lib.oracle_q8_quantize_silu_mul.argtypes = [c_p, c_p, c_i64, c_i64, c_p, c_p]
@@ -166,6 +168,17 @@ def q4k_repack(w: np.ndarray, m: int, k: int, lib=None) -> np.ndarray:
     wr = np.empty(((m + 15) // 16) * (k // 256) * 2368, dtype=np.uint8)
     _check(lib.oracle_q4k_repack(_ptr(w), m, k, _ptr(wr)), "q4k_repack")
     return wr
+
+
+def q8_tiles(q: np.ndarray, lib=None) -> np.ndarray:
+    """q8 codes int8 [n, k] -> the binary16 operand-tile layout, as uint16 bits
+    [ceil(n/128) * 128 * k]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    n, k = q.shape
+    qt = np.empty(((n + 127) // 128) * 128 * k, dtype=np.uint16)
+    _check(lib.oracle_q8_tiles(_ptr(q), n, k, _ptr(qt)), "q8_tiles")
+    return qt
 
 
 def q6k_unpack(w: np.ndarray, m: int, k: int, lib=None):

@@ -540,6 +540,32 @@ def pin_q4k_repack(lib):
         assert np.array_equal(got, expected_repack(f)), "repack differs (m=%d k=%d)" % (m, k)
 
 
+# ------------------------------------------------------ q8 operand tiles
+def expected_q8_tiles(q: np.ndarray) -> np.ndarray:
+    """The operand-tile layout built with numpy reshapes from the codes (not
+    the oracle's loops): k = 128 s + 32 c + 16 g + 8 h + e', tokens padded
+    with zeros to 128, slots ordered (T, s, c, h, g, tt), a slot's element e
+    taking e' = 0, 2, 1, 3, 4, 6, 5, 7."""
+    n, k = q.shape
+    T = (n + 127) // 128
+    qp = np.zeros((T * 128, k), dtype=np.float16)
+    qp[:n] = q
+    a = qp.reshape(T, 128, k // 128, 4, 2, 2, 8)          # [T, tt, s, c, g, h, e']
+    a = a[..., [0, 2, 1, 3, 4, 6, 5, 7]]
+    a = a.transpose(0, 2, 3, 5, 4, 1, 6)                   # [T, s, c, h, g, tt, e]
+    return np.ascontiguousarray(a).reshape(-1).view(np.uint16)
+
+
+def pin_q8_tiles(lib):
+    """The oracle's operand tiles equal the numpy-built layout, for token
+    counts below one tile, at a tile boundary and past it."""
+    for seed, (n, k) in enumerate([(1, 256), (37, 512), (128, 256), (131, 768)]):
+        rng = np.random.default_rng(90 + seed)
+        q = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+        got = oracle.q8_tiles(q, lib=lib)
+        assert np.array_equal(got, expected_q8_tiles(q)), "q8 tiles differ (n=%d k=%d)" % (n, k)
+
+
 ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundtrip,
             pin_q8_golden, pin_q8_invariants, pin_q8_zero_block, pin_dots_bruteforce,
             pin_dots_closed_forms, pin_out_bruteforce, pin_out_special_cases,
@@ -547,4 +573,4 @@ ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundt
             pin_q6k_golden_block, pin_q6k_roundtrip, pin_q6k_dots_bruteforce,
             pin_q6k_dots_closed_forms, pin_q6k_out_bruteforce, pin_q6k_out_special_cases,
             pin_q6k_one_superblock, pin_silu_mul_float64, pin_silu_mul_closed_forms,
-            pin_quantize_silu_mul, pin_q4k_repack]
+            pin_quantize_silu_mul, pin_q4k_repack, pin_q8_tiles]

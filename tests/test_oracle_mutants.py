@@ -51,6 +51,11 @@ MUTANTS = [
      "sw[2] = (uint8_t)mn[2 * p + 1];\n                sw[3] = (uint8_t)mn[2 * p];"),
     ("repack_halves_swapped", "memcpy(rec + 320 + 512 * p + 256 * h + 16 * r, blk + 16 + 32 * p + 16 * h, 16);",
      "memcpy(rec + 320 + 512 * p + 256 * (1 - h) + 16 * r, blk + 16 + 32 * p + 16 * h, 16);"),
+    ("tiles_h_g_swapped", "const int64_t row = (c * 2 + h) * 2 + g;", "const int64_t row = (c * 2 + g) * 2 + h;"),
+    ("tiles_natural_order", "static const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};",
+     "static const int order[8] = {0, 1, 2, 3, 4, 5, 6, 7};"),
+    ("tiles_padding_repeats_last", "slot[e] = t < n ? oracle_f32_to_f16((float)q8[t * k + kk]) : 0;",
+     "slot[e] = oracle_f32_to_f16((float)q8[(t < n ? t : n - 1) * k + kk]);"),
     ("quantize_gate_not_h", "rc |= oracle_q8_quantize(row, 1, k,", "rc |= oracle_q8_quantize(g + t * k, 1, k,"),
 ]
 
