@@ -65,6 +65,13 @@ def build_workload(name: str):
         return ({"workload": "weight-bound q6_K W[%dx%d] at N=%d (10%% of scale groups sc=0)"
                              % (f.m, f.k, n), "m": f.m, "k": f.k, "n": n},
                 {"x": synth.q6k_activation("wide_in", n)}, [("wide_in", f, "x")])
+    if name.startswith("t_"):
+        desc, inputs, mats = build_workload(name[2:])
+        if any(not isinstance(f, synth.Q4KFields) for _, f, _ in mats):
+            raise SystemExit("the operand-tile entry points are for q4_K weights")
+        return (dict(desc, tiles=True, workload=desc["workload"] +
+                     ", activations quantized to binary16 operand tiles (q8_quantize_rows_tiled)"),
+                inputs, mats)
     if name.startswith("r_"):
         desc, inputs, mats = build_workload(name[2:])
         if any(not isinstance(f, synth.Q4KFields) for _, f, _ in mats):
@@ -270,9 +277,14 @@ def main():
               for lbl, f, src in mats]
         if desc.get("repacked"):   # load-time step, outside the timed region
             ws = [(lbl, binding.repack(w, m, k), m, k, src) for lbl, w, m, k, src in ws]
-        qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
-                  torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
-              for s, x in xs.items()}
+        if desc.get("tiles"):
+            qs = {s: (torch.empty(binding.tiles_elems(*x.shape), dtype=torch.int16, device=dev),
+                      torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
+                  for s, x in xs.items()}
+        else:
+            qs = {s: (torch.empty(x.shape, dtype=torch.int8, device=dev),
+                      torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.int32, device=dev))
+                  for s, x in xs.items()}
         odt = torch.float16 if args.f16_out else torch.float32
         outs = [torch.empty((xs[src].shape[0], m), dtype=odt, device=dev)
                 for _, _, m, _, src in ws]
@@ -283,7 +295,8 @@ def main():
     mmq_ops = sum(2.0 * inputs[src].shape[0] * f.m * f.k for _, f, src in mats)
     out_bytes = 2.0 if args.f16_out else 4.0
     wbytes = (lambda f: 2368.0 / 4096.0) if desc.get("repacked") else (lambda f: weight_format(f)[1])
-    mmq_alg_bytes = sum(wbytes(f) * f.m * f.k + 1.125 * inputs[src].shape[0] * f.k
+    act_bytes = 2.125 if desc.get("tiles") else 1.125   # binary16 tiles or int8 codes, + scale words
+    mmq_alg_bytes = sum(wbytes(f) * f.m * f.k + act_bytes * inputs[src].shape[0] * f.k
                         + out_bytes * inputs[src].shape[0] * f.m for _, f, src in mats)
     suffix = "_f16out" if args.f16_out else "_fp32out"
     names = sorted({weight_format(f)[2] + suffix for _, f, _ in mats})
@@ -291,18 +304,25 @@ def main():
         if args.f16_out:
             raise SystemExit("the repacked layout has a float32 entry point only")
         names = ["mmq_q4kr_q8_fp32out"]
+    if desc.get("tiles"):
+        if args.f16_out:
+            raise SystemExit("the operand-tile entry points are float32 only")
+        names = ["mmq_q4kr_q8t_fp32out" if desc.get("repacked") else "mmq_q4k_q8t_fp32out"]
     mmq_name = "+".join(names)
-    calls = [getattr(binding, names[0] if desc.get("repacked") else weight_format(f)[2] + suffix)
+    calls = [getattr(binding, names[0] if desc.get("repacked") or desc.get("tiles")
+                     else weight_format(f)[2] + suffix)
              for _, f, _ in mats]
+    quantize = binding.q8_quantize_rows_tiled if desc.get("tiles") else binding.q8_quantize_rows
+    quantize_name = "q8_quantize_rows_tiled" if desc.get("tiles") else "q8_quantize_rows"
 
     def step(i):
         xs, ws, qs, outs = sets[i % len(sets)]
         for s, x in xs.items():
             q, ds = qs[s]
-            binding.q8_quantize_rows(x, x.shape[0], x.shape[1], q, ds)
+            quantize(x, x.shape[0], x.shape[1], q, ds)
         for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
             q, ds = qs[src]
-            mmq(w, m, k, q, ds, q.shape[0], out)
+            mmq(w, m, k, q, ds, ds.shape[0], out)
 
     for i in range(args.warmup):
         step(i)
@@ -326,7 +346,7 @@ def main():
         xs, ws, qs, outs = sets[i % len(sets)]
         for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
             q, ds = qs[src]
-            mmq(w, m, k, q, ds, q.shape[0], out)
+            mmq(w, m, k, q, ds, ds.shape[0], out)
     e1.record(stream)
     torch.cuda.synchronize()
     mmq_ms = e0.elapsed_time(e1) / rounds          # all projections of one step
@@ -355,7 +375,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": dict(desc, step="q8_quantize_rows + %s per projection" % mmq_name,
+        "config": dict(desc, step="%s + %s per projection" % (quantize_name, mmq_name),
                        copies=len(sets)),
         "tok_per_s": round(n_tok / (ms_step * 1e-3), 1),
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),

@@ -224,6 +224,45 @@ int q4k_repack(const void *w, int64_t m, int64_t k, void *wr, hipStream_t stream
 int mmq_q4kr_q8_fp32out(const void *wr, int64_t m, int64_t k, const int8_t *q,
                         const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
 
+/*
+ * q8_quantize_rows_tiled - q8_quantize_rows with the codes written as the
+ * binary16 matrix-core operands of the prefill matmul, in its tile order (a
+ * quantize-transpose pass ahead of the matmul: the r22 page, section 5,
+ * names a later "quantize-transpose prepass" that changed the activation
+ * side's layout at its root; this layout is the library's).  The codes and
+ * scale words are q8_quantize_rows' bit for bit.
+ *
+ *   x  : float32 [n][k], k % 256 == 0.
+ *   qt : ceil(n/128) * 128 * k binary16 values (out, 2 bytes each): tokens in
+ *        tiles of 128, k in stages of 128, one block of 16 x 128 slots of 8
+ *        values (32768 bytes) per (tile T, stage s), blocks tile-major.  Slot
+ *        ((c*2 + h)*2 + g)*128 + tt of block (T, s) holds the codes of token
+ *        128T + tt at k = 128s + 32c + 16g + 8h + e for e = 0,2,1,3,4,6,5,7
+ *        (c < 4, h < 2, g < 2, tt < 128).  Tokens past n hold zeros.
+ *   ds : uint32 [n][k/32] (out), as for q8_quantize_rows.
+ * Errors as for q8_quantize_rows, except that k must be a multiple of 256
+ * (MMQ_ERR_SHAPE) and n at most 2^31 - 128.
+ */
+int q8_quantize_rows_tiled(const float *x, int64_t n, int64_t k, uint16_t *qt, uint32_t *ds,
+                           hipStream_t stream);
+
+/*
+ * mmq_q4k_q8t_fp32out / mmq_q4kr_q8t_fp32out - mmq_q4k_q8_fp32out (q4_K
+ * rows) and mmq_q4kr_q8_fp32out (q4k_repack records) with the activations
+ * as operand tiles (qt and ds from q8_quantize_rows_tiled of the same n and
+ * k).  Every n runs the binary16-MFMA kernel, whose producers copy the tiles
+ * straight into LDS instead of converting q8; the arithmetic and its order
+ * are that kernel's, so the result equals mmq_q4k_q8_fp32out's bit for bit
+ * wherever that takes the binary16 kernel (n > 64).  Meant for prefill (few
+ * tokens run faster on mmq_q4k_q8_fp32out).  Other arguments, errors and
+ * empty calls as for mmq_q4k_q8_fp32out / mmq_q4kr_q8_fp32out, and n at most
+ * 2^31 - 128.
+ */
+int mmq_q4k_q8t_fp32out(const void *w, int64_t m, int64_t k, const uint16_t *qt,
+                        const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+int mmq_q4kr_q8t_fp32out(const void *wr, int64_t m, int64_t k, const uint16_t *qt,
+                         const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);
 

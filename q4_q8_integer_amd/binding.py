@@ -16,9 +16,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
            "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "q4k_repack",
-           "mmq_q4kr_q8_fp32out", "mmq_status_string")
+           "mmq_q4kr_q8_fp32out", "q8_quantize_rows_tiled", "mmq_q4k_q8t_fp32out",
+           "mmq_q4kr_q8t_fp32out", "mmq_status_string")
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out")
+              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
+              "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out")
 _lib = None
 
 
@@ -42,6 +44,8 @@ def load_library(path: str = LIB_PATH):
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.q8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_rows.restype = ctypes.c_int
+    lib.q8_quantize_rows_tiled.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.q8_quantize_rows_tiled.restype = ctypes.c_int
     lib.q8_quantize_silu_mul.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_silu_mul.restype = ctypes.c_int
     lib.q4k_repack.argtypes = [vp, i64, i64, vp, vp]
@@ -86,6 +90,12 @@ def q8_quantize_rows(x, n, k, q, ds):
         _ptr(x), n, k, _ptr(q), _ptr(ds), _stream()))
 
 
+def q8_quantize_rows_tiled(x, n, k, qt, ds):
+    """Enqueue the quantizer with the codes as binary16 operand tiles."""
+    _check("q8_quantize_rows_tiled", load_library().q8_quantize_rows_tiled(
+        _ptr(x), n, k, _ptr(qt), _ptr(ds), _stream()))
+
+
 def q8_quantize_silu_mul(gate, up, n, k, q, ds):
     """Enqueue the fused SiLU-gate quantizer on preallocated outputs."""
     _check("q8_quantize_silu_mul", load_library().q8_quantize_silu_mul(
@@ -116,6 +126,16 @@ def mmq_q4kr_q8_fp32out(wr, m, k, q, ds, n, out):
         _ptr(wr), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
+def mmq_q4k_q8t_fp32out(w, m, k, qt, ds, n, out):
+    _check("mmq_q4k_q8t_fp32out", load_library().mmq_q4k_q8t_fp32out(
+        _ptr(w), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
+
+
+def mmq_q4kr_q8t_fp32out(wr, m, k, qt, ds, n, out):
+    _check("mmq_q4kr_q8t_fp32out", load_library().mmq_q4kr_q8t_fp32out(
+        _ptr(wr), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
+
+
 def mmq_q6k_q8(w, m, k, q, ds, n, dots):
     _check("mmq_q6k_q8", load_library().mmq_q6k_q8(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
@@ -140,6 +160,22 @@ def quantize(x: torch.Tensor):
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
     q8_quantize_rows(x, n, k, q, ds)
     return q, ds
+
+
+def tiles_elems(n: int, k: int) -> int:
+    """binary16 values in q8_quantize_rows_tiled's output for n tokens of k."""
+    return (n + 127) // 128 * 128 * k
+
+
+def quantize_tiled(x: torch.Tensor):
+    """x float32 [n, k] -> (qt int16 [tiles_elems(n, k)] holding the binary16
+    operand tiles, ds int32 [n, k/32])."""
+    _need(x, torch.float32, "x")
+    n, k = x.shape
+    qt = torch.empty(tiles_elems(n, k), dtype=torch.int16, device=x.device)
+    ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
+    q8_quantize_rows_tiled(x, n, k, qt, ds)
+    return qt, ds
 
 
 def quantize_silu_mul(gate: torch.Tensor, up: torch.Tensor):
@@ -228,6 +264,22 @@ def q6k_fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor,
     else:
         _need(out, torch.float16, "out")
     mmq_q6k_q8_f16out(w, m, k, q, ds, n, out)
+    return out
+
+
+def fp32_tiles(w: torch.Tensor, m: int, k: int, qt: torch.Tensor, ds: torch.Tensor, out=None,
+               repacked: bool = False):
+    """The fold on q8 operand tiles (from quantize_tiled): float32 [n, m]; w is
+    q4_K rows, or q4k_repack records with repacked=True."""
+    _need(w, torch.uint8, "w")
+    _need(qt, torch.int16, "qt")
+    _need(ds, torch.int32, "ds")
+    n = ds.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=ds.device)
+    else:
+        _need(out, torch.float32, "out")
+    (mmq_q4kr_q8t_fp32out if repacked else mmq_q4k_q8t_fp32out)(w, m, k, qt, ds, n, out)
     return out
 
 

@@ -15,6 +15,11 @@ constexpr int kRepackRecordBytes = 2368;
 hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
                               hipStream_t stream);
 
+// q8 quantize with the codes written as binary16 operand tiles (token tiles
+// of 128, k stages of 128, 32 KiB per tile and stage; k % 256 == 0).
+hipError_t launch_q8_quantize_tiled(const float* x, int n, int k, uint16_t* qt, uint32_t* ds,
+                                    hipStream_t stream);
+
 // q8 quantize of h = float32(g*u / (1 + exp(-g))) (float64 evaluation).
 hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,
                                        uint32_t* ds, hipStream_t stream);
@@ -65,6 +70,12 @@ hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q,
 // as launch_mmq_fp32_f16, so the same float32 result bit for bit).
 hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
                                         const uint32_t* ds, int n, float* out, hipStream_t stream);
+
+// The binary16-MFMA kernel with the activations as q8 operand tiles (from
+// launch_q8_quantize_tiled), on q4_K rows or q4k_repack records; the same
+// float32 result bit for bit as the int8-activation kernel.
+hipError_t launch_mmq_fp32_f16_tiles(const uint8_t* w, bool repacked, int m, int k, const uint16_t* qt,
+                                     const uint32_t* ds, int n, float* out, hipStream_t stream);
 
 // Two-term fold, out[t][o], for n <= 64 tokens: weight-streaming int8-MFMA
 // kernel (8 waves per 16 rows, each over a slice of k).

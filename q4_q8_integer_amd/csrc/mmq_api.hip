@@ -121,6 +121,24 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
                              half_out, stream));
 }
 
+// The fold entry points on q8 operand tiles: always the binary16-MFMA kernel
+// (the tiles are its operand layout), on q4_K rows or repacked records.
+int tiles_fold_entry(const void* w, bool repacked, int64_t m, int64_t k, const uint16_t* qt,
+                     const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(w, m, k, reinterpret_cast<const int8_t*>(qt), n, out, &empty);
+    if (rc != MMQ_OK || empty) return rc;
+    if (n > kMaxDim - 127 || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (repacked && (m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems)
+        return MMQ_ERR_OVERFLOW;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    return hip_status(mmq::launch_mmq_fp32_f16_tiles(static_cast<const uint8_t*>(w), repacked, (int)m,
+                                                     (int)k, qt, ds, (int)n, out, stream));
+}
+
 // q6_K kernel behind the fold entry points: the vector-ALU dot4 kernel for
 // n <= 8, the binary16-MFMA kernel above.  MMQ_Q6K_KERNEL=i8|f16|gemv forces
 // one (for comparisons and tests; "gemv" only where n <= 8).
@@ -170,6 +188,18 @@ int q8_quantize_rows(const float* x, int64_t n, int64_t k, int8_t* q, uint32_t* 
     const int dev = check_device();
     if (dev != MMQ_OK) return dev;
     return hip_status(mmq::launch_q8_quantize(x, n * (k / 32), q, ds, stream));
+}
+
+int q8_quantize_rows_tiled(const float* x, int64_t n, int64_t k, uint16_t* qt, uint32_t* ds,
+                           hipStream_t stream) {
+    if (n < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
+    if (n > kMaxDim - 127 || k > kMaxK || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (n == 0) return MMQ_OK;
+    if (!x || !qt || !ds) return MMQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qt) || !aligned16(ds)) return MMQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != MMQ_OK) return dev;
+    return hip_status(mmq::launch_q8_quantize_tiled(x, (int)n, (int)k, qt, ds, stream));
 }
 
 int q8_quantize_silu_mul(const float* gate, const float* up, int64_t n, int64_t k, int8_t* q,
@@ -277,6 +307,16 @@ int mmq_q4kr_q8_fp32out(const void* wr, int64_t m, int64_t k, const int8_t* q,
         if (rc != MMQ_OK) return rc;
     }
     return MMQ_OK;
+}
+
+int mmq_q4k_q8t_fp32out(const void* w, int64_t m, int64_t k, const uint16_t* qt,
+                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    return tiles_fold_entry(w, false, m, k, qt, ds, n, out, stream);
+}
+
+int mmq_q4kr_q8t_fp32out(const void* wr, int64_t m, int64_t k, const uint16_t* qt,
+                         const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    return tiles_fold_entry(wr, true, m, k, qt, ds, n, out, stream);
 }
 
 const char* mmq_status_string(int status) {

@@ -53,6 +53,12 @@ constexpr int CS = 4;  // chunks per stage (128 k)
 constexpr int NTW = 1;  // 32-token tiles per consumer wave
 // Word 3 of a raw (unformatted, stride 0) buffer resource on gfx950.
 constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt operand: at most n vector-memory operations outstanding, the
+// other counters unconstrained.
+constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// One (token tile, stage) block of the q8 operand tiles: 16 slot rows x 128
+// tokens x 8 binary16 values.
+constexpr int kQtBlockBytes = 16 * BN * 16;
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
@@ -122,10 +128,16 @@ __device__ __forceinline__ uint32_t f16x2_splat(float v) {
     return (uint32_t)h | ((uint32_t)h << 16);
 }
 
-// One stage of operands (128 k = 4 chunks) in LDS.
+// One stage of operands (128 k = 4 chunks) in LDS.  The q8 operands are an
+// LDS array of their own (StageB), so that the compiler can tell the
+// direct-to-LDS copies into it from the weight stores (it would otherwise
+// wait for the copies, and with them for the next stage's loads, before
+// every store).
+struct StageB {
+    uint4 B[CS][2][2][BN];   // q8 binary16 operand slots [chunk][k-half][lane-half][token]
+};
 struct Stage {
     uint4 A[CS][2][2][BM];   // sc*q4 binary16 operand slots [chunk][k-half][lane-half][row]
-    uint4 B[CS][2][2][BN];   // q8 binary16 operand slots [chunk][k-half][lane-half][token]
     float D[BM];             // d of the stage's super-block
     float CA[CS][BM];        // -dmin*m per (chunk, row)
     float Da[CS][BN];        // da per (chunk, token)
@@ -148,6 +160,8 @@ struct Raw {
 // zeros instead of faulting.
 struct Src {
     __amdgpu_buffer_rsrc_t w, q, ds;
+    const uint16_t* qt;      // operand tiles (QT): the workgroup's 128-token tile
+    int qhalf;               // QT with 64-token tiles: which half of it
     int wh[WPC], wq[WPC];    // weight piece offsets: block header (repacked: d | dmin), nibbles
     int wsc[WPC];            // repacked records: scale dword
     int y[APC];              // q8 piece offsets
@@ -158,7 +172,7 @@ struct Src {
 // leave CUs idle); the LDS stage keeps its BN-token size.
 // REP: w holds q4k_repack records (16-row tiles, one 2368-byte record per
 // tile and super-block) instead of q4_K rows.
-template <int TB, bool REP>
+template <int TB, bool REP, bool QT>
 __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                          const int8_t* __restrict__ q,
                                          const uint32_t* __restrict__ ds, int pt, int row0,
@@ -178,6 +192,10 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                             (int)((uint32_t)toks * (uint32_t)K), kBufferFlags);   // up to 2^31 bytes
     p.ds = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ds + (int64_t)tok0 * C), 0,
                                              toks * C * 4, kBufferFlags);
+    if (QT) {
+        p.qt = reinterpret_cast<const uint16_t*>(q) + (int64_t)(tok0 >> 7) * (K >> 7) * (kQtBlockBytes / 2);
+        p.qhalf = (tok0 >> 6) & 1;
+    }
 #pragma unroll
     for (int rr = 0; rr < WPC; ++rr) {
         const int i = pt + rr * PT;
@@ -212,9 +230,8 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     }
 }
 
-template <int TB, bool REP>
+template <int TB, bool REP, bool QT>
 __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
-    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     if (REP) {
         // stage st: record st / 2, chunk pairs 2 (st & 1) and 2 (st & 1) + 1
         const int roff = (st >> 1) * kRepackRecordBytes, hs = st & 1;
@@ -232,16 +249,17 @@ __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int st) {
             r.qs[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.w, p.wq[rr], qoff, 0));
         }
     }
+    if (!QT)
 #pragma unroll
-    for (int rr = 0; rr < TB * 8 / PT; ++rr)
-        r.y[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y[rr], 128 * st, 0));
+        for (int rr = 0; rr < TB * 8 / PT; ++rr)
+            r.y[rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y[rr], 128 * st, 0));
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr)
         r.word[rr] = __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word[rr], 16 * st, 0);
 }
 
-template <int TB, bool REP>
-__device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, int st) {
+template <int TB, bool REP, bool QT>
+__device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, StageB& sb, int pt, int st) {
     const int hs = st & 1;
 #pragma unroll
     for (int rr = 0; rr < WPC; ++rr) {
@@ -287,7 +305,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         }
     }
 #pragma unroll
-    for (int rr = 0; rr < TB * 8 / PT; ++rr) {
+    for (int rr = 0; rr < (QT ? 0 : TB * 8 / PT); ++rr) {   // QT: copied by dma_stage
         const int i = pt + rr * PT;
         const int tok = (i & 15) | ((i >> 7) << 4);
         const int j = (i >> 4) & 7, cl = j >> 1, gg = j & 1;
@@ -297,8 +315,8 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
         q8_word(y.y, p[2], p[3]);
         q8_word(y.z, p[4], p[5]);
         q8_word(y.w, p[6], p[7]);
-        sg.B[cl][0][gg][tok] = make_uint4(p[0], p[1], p[2], p[3]);
-        sg.B[cl][1][gg][tok] = make_uint4(p[4], p[5], p[6], p[7]);
+        sb.B[cl][0][gg][tok] = make_uint4(p[0], p[1], p[2], p[3]);
+        sb.B[cl][1][gg][tok] = make_uint4(p[4], p[5], p[6], p[7]);
     }
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr) {
@@ -312,6 +330,74 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
     }
 }
 
+// Vector-memory operations load_stage issues (the wait that completes a
+// stage's operand-tile copies leaves these in flight).
+template <bool REP, bool QT>
+constexpr int stage_loads() { return WPC * (REP ? 3 : 2) + SPC + (QT ? 0 : APC); }
+
+// QT: the stage's q8 operands are one 32 KiB block of the operand tiles, in
+// the order of StageB, copied with direct-to-LDS buffer loads (lane i of an
+// instruction writes 16 bytes at M0 + 16 i: one KiB, 64 token slots of one
+// slot row).  128-token tiles take the whole block (32 copies, 4 per producer
+// wave), 64-token tiles their half of each row (16 copies).  Every copy is
+// issued by a full wave.
+//
+// The copies are inline asm, outside the compiler's wait bookkeeping: with
+// the builtin it waits for them (and with them for the next stage's register
+// loads) before the first LDS store of every stage.  The producer loop
+// places the waits itself: everything older is complete before the copies
+// are issued, and a vmcnt that leaves only the next stage's loads in flight
+// completes them before the barrier.  The compiler's own waits can then only
+// be stricter than needed, never looser.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// M0 is a reserved register; in these kernels nothing else sets or reads it
+// (the compiler's own direct-to-LDS and LDS-bounds uses are absent), so the
+// clobber only tells the compiler what the asm does.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// An empty asm that reads a stage's raw registers: the compiler completes
+// their loads here (nothing newer is in flight yet), so that no later use
+// waits on a count that the uncounted copies would make too strict.
+template <bool REP>
+__device__ __forceinline__ void settle(const Raw& r) {
+#pragma unroll
+    for (int rr = 0; rr < WPC; ++rr) {
+        if (REP)
+            asm volatile("" ::"v"(r.hdr[rr].x), "v"(r.hdr[rr].y));
+        else
+            asm volatile("" ::"v"(r.hdr[rr].x), "v"(r.hdr[rr].y), "v"(r.hdr[rr].z), "v"(r.hdr[rr].w));
+        asm volatile("" ::"v"(r.qs[rr].x), "v"(r.qs[rr].y), "v"(r.qs[rr].z), "v"(r.qs[rr].w));
+    }
+#pragma unroll
+    for (int rr = 0; rr < SPC; ++rr) asm volatile("" ::"v"(r.word[rr]));
+}
+
+template <int TB>
+__device__ __forceinline__ void dma_stage(StageB& sb, const Src& p, int st, int pw, int lane) {
+    constexpr int kCopies = TB * 16 / 64 / (PT / 64);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.qt + (int64_t)st * (kQtBlockBytes / 2));
+    const u32x4 rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)kQtBlockBytes,
+                        (uint32_t)kBufferFlags};
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&sb.B[0][0][0][0];
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+        const int i = pw * kCopies + j;
+        const int row = TB == BN ? i >> 1 : i;
+        const int half = TB == BN ? (i & 1) : p.qhalf;
+        const int dst = row * BN + (TB == BN ? half * 64 : 0);
+        lds_copy16(rsrc, base + 16 * dst, (row * BN + half * 64 + lane) * 16);
+    }
+}
+
 // One stage for one consumer wave (64 rows x 32*NTW tokens as 2 x NTW tiles of 32x32).
 // HS is the stage's half of the super-block: HS = 0 starts acc_b (the first
 // chunk multiplies instead of accumulating), HS = 1 ends it with the d fold.
@@ -320,7 +406,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, int pt, i
 // RT: 32-row tiles per wave (2 with 128-token tiles, 1 with 64: the 8
 // waves then cover 4 x 32 rows x 2 x 32 tokens); r0 = the wave's first row.
 template <int HS, int RT>
-__device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, int g, int l32,
+__device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb, int wm, int wn, int g, int l32,
                                               v16f (&acc)[2][NTW], v16f (&accb)[2][NTW]) {
 #pragma unroll
     for (int cl = 0; cl < CS; ++cl) {
@@ -329,8 +415,8 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int t = wn * 32 * NTW + nt * 32 + l32;
-            b0[nt] = __builtin_bit_cast(v8h, sg.B[cl][0][g][t]);
-            b1[nt] = __builtin_bit_cast(v8h, sg.B[cl][1][g][t]);
+            b0[nt] = __builtin_bit_cast(v8h, sb.B[cl][0][g][t]);
+            b1[nt] = __builtin_bit_cast(v8h, sb.B[cl][1][g][t]);
             da[nt] = sg.Da[cl][t];
         }
 #pragma unroll
@@ -399,13 +485,14 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
 // binary16 operand slots).  Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
-template <int TB, bool H, bool REP>
+template <int TB, bool H, bool REP, bool QT>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
                                                      int M, int N, int K, int tiles_m,
                                                      void* __restrict__ out) {
     __shared__ Stage stage[2];
+    __shared__ StageB stage_b[2];
 
     const int tid = threadIdx.x;
     const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
@@ -419,19 +506,33 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
         // wait on them).
         const int pt = tid - CT;
         Src src;
-        init_src<TB, REP>(src, w, q, ds, pt, row0, tok0, M, N, K);
+        init_src<TB, REP, QT>(src, w, q, ds, pt, row0, tok0, M, N, K);
+        const int pw = __builtin_amdgcn_readfirstlane(pt >> 6), lane = pt & 63;
         Raw ra, rb;
-        load_stage<TB, REP>(ra, src, 0);
+        load_stage<TB, REP, QT>(ra, src, 0);
         // k is a multiple of 256, so the stage count is even and the loop
         // runs whole (even, odd) pairs.  Every load is unconditional (the
         // last prefetch re-reads the final stage), which lets the compiler
         // wait only for the older register set.
         for (int it = 0; it < stages; it += 2) {
-            load_stage<TB, REP>(rb, src, it + 1);
-            convert_stage<TB, REP>(ra, stage[0], pt, it);
+            // QT: everything older completes first (loads issued a half-step
+            // ago), then the stage's q8 copies, so that waiting for them
+            // before the barrier leaves only the next stage's loads in flight.
+            if (QT) {
+                settle<REP>(ra);
+                dma_stage<TB>(stage_b[0], src, it, pw, lane);
+            }
+            load_stage<TB, REP, QT>(rb, src, it + 1);
+            convert_stage<TB, REP, QT>(ra, stage[0], stage_b[0], pt, it);
+            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
             __syncthreads();
-            load_stage<TB, REP>(ra, src, min(it + 2, stages - 1));
-            convert_stage<TB, REP>(rb, stage[1], pt, it + 1);
+            if (QT) {
+                settle<REP>(rb);
+                dma_stage<TB>(stage_b[1], src, it + 1, pw, lane);
+            }
+            load_stage<TB, REP, QT>(ra, src, min(it + 2, stages - 1));
+            convert_stage<TB, REP, QT>(rb, stage[1], stage_b[1], pt, it + 1);
+            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
             __syncthreads();
         }
         __syncthreads();  // the consumers' last stage
@@ -457,9 +558,9 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
     // even stages, stage[1] odd ones.  The barriers pair with the producers'.
     __syncthreads();
     for (int st = 0; st < stages; st += 2) {
-        consume_stage<0, RT>(stage[0], wm, wn, g, l32, acc, accb);
+        consume_stage<0, RT>(stage[0], stage_b[0], wm, wn, g, l32, acc, accb);
         __syncthreads();
-        consume_stage<1, RT>(stage[1], wm, wn, g, l32, acc, accb);
+        consume_stage<1, RT>(stage[1], stage_b[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
     }
 
@@ -509,8 +610,8 @@ hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, 
     tile_shape(m, n, tiles_m, half_tiles, tiles);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true, false> : (const void*)mmq_f16_kernel<BN / 2, false, false>)
-                               : (half_out ? (const void*)mmq_f16_kernel<BN, true, false> : (const void*)mmq_f16_kernel<BN, false, false>);
+    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true, false, false> : (const void*)mmq_f16_kernel<BN / 2, false, false, false>)
+                               : (half_out ? (const void*)mmq_f16_kernel<BN, true, false, false> : (const void*)mmq_f16_kernel<BN, false, false, false>);
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 
@@ -522,8 +623,24 @@ hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const i
     tile_shape(m, n, tiles_m, half_tiles, tiles);
     void* args[] = {(void*)&wr, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true>
-                               : (const void*)mmq_f16_kernel<BN, false, true>;
+    const void* f = half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true, false>
+                               : (const void*)mmq_f16_kernel<BN, false, true, false>;
+    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+}
+
+hipError_t launch_mmq_fp32_f16_tiles(const uint8_t* w, bool repacked, int m, int k, const uint16_t* qt,
+                                     const uint32_t* ds, int n, float* out, hipStream_t stream) {
+    int tiles_m;
+    bool half_tiles;
+    int64_t tiles;
+    tile_shape(m, n, tiles_m, half_tiles, tiles);
+    const int8_t* q = reinterpret_cast<const int8_t*>(qt);
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
+                    (void*)&tiles_m, (void*)&out};
+    const void* f = repacked ? (half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true, true>
+                                           : (const void*)mmq_f16_kernel<BN, false, true, true>)
+                             : (half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, false, true>
+                                           : (const void*)mmq_f16_kernel<BN, false, false, true>);
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 

@@ -16,6 +16,15 @@
 // input of an FFN's down projection): the block's values are computed from
 // the two inputs as they are loaded.
 //
+// Tiled output (q8_quantize_rows_tiled): the same codes and words, the codes
+// written as the binary16 operands of the binary16-MFMA matmul, in its LDS
+// stage order (token tiles of 128, k stages of 128, 32 KiB per tile and
+// stage; a quantize-transpose pass ahead of the matmul).  A lane's 8 codes
+// are exactly one 16-byte operand slot (k = 32c + 8 part .. +7, in the pair
+// order 0,2,1,3,4,6,5,7), so the wave takes 16 consecutive tokens of one
+// block index and its lanes of one part write 256 contiguous bytes.  Tokens
+// past n (up to the tile's 128) get zero slots and no scale word.
+//
 // Numerics: x/da is the IEEE fp32 division (hipcc's default correctly
 // rounded divide; never built with fast-math), roundf rounds ties away from
 // zero, and v_cvt_f16_f32 rounds to nearest even keeping subnormals.
@@ -80,17 +89,38 @@ struct SiluMulSrc {
     }
 };
 
-template <class Src>
-__global__ __launch_bounds__(256) void q8_quantize_kernel(Src src, int64_t nblocks,
+// TILES = false: quad i takes block i (row-major blocks), codes to q.
+// TILES = true:  wave w takes block c = w % C of tokens 16 (w / C) .. +15
+//                (one per quad), codes to the operand tiles qt.
+template <class Src, bool TILES>
+__global__ __launch_bounds__(256) void q8_quantize_kernel(Src src, int64_t nblocks, int n, int C,
                                                           int8_t* __restrict__ q,
+                                                          uint16_t* __restrict__ qt,
                                                           uint32_t* __restrict__ ds) {
     const int64_t lane_id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = lane_id >> 2;  // quads are aligned, so a quad is all in or all out
-    if (blk >= nblocks) return;
     const int part = threadIdx.x & 3;
+    int64_t blk = lane_id >> 2;  // quads are aligned, so a quad is all in or all out
+    int tok = 0, c = 0;
+    bool pad = false;
+    if (TILES) {
+        const int64_t w = lane_id >> 6;
+        const int64_t tg = w / C;
+        c = (int)(w - tg * C);
+        tok = (int)(tg * 16 + ((lane_id >> 2) & 15));
+        if (tok >= ((n + 127) & ~127)) return;   // past the last tile (whole waves)
+        pad = tok >= n;
+        blk = (int64_t)tok * C + c;
+    } else if (blk >= nblocks) {
+        return;
+    }
 
     float v[8];
-    src.load(blk, part, v);
+    if (TILES && pad) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    } else {
+        src.load(blk, part, v);
+    }
 
     float amax = 0.0f;
 #pragma unroll
@@ -115,15 +145,34 @@ __global__ __launch_bounds__(256) void q8_quantize_kernel(Src src, int64_t nbloc
     sum = quad_sum(sum);
     word |= (uint32_t)(uint16_t)(int16_t)sum << 16;
 
-    *reinterpret_cast<uint2*>(q + blk * 32 + part * 8) = make_uint2(packed[0], packed[1]);
-    if (part == 0) ds[blk] = word;
+    if (TILES) {
+        // slot ((cl * 2 + h) * 2 + g) * 128 + tt of block (tile, stage), part = 2 g + h
+        const int cl = c & 3, g = part >> 1, h = part & 1;
+        const int64_t stage = c >> 2, stages = C >> 2;
+        const int64_t slot = (((int64_t)(tok >> 7) * stages + stage) * 16 + (cl * 2 + h) * 2 + g) * 128 +
+                             (tok & 127);
+        uint32_t hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int qi = (int8_t)(uint8_t)(packed[i >> 2] >> (8 * (i & 3)));
+            hv[i] = __builtin_bit_cast(unsigned short, (_Float16)(float)qi);   // exact
+        }
+        *reinterpret_cast<uint4*>(qt + slot * 8) =
+            make_uint4(hv[0] | (hv[2] << 16), hv[1] | (hv[3] << 16), hv[4] | (hv[6] << 16),
+                       hv[5] | (hv[7] << 16));
+        if (part == 0 && !pad) ds[blk] = word;
+    } else {
+        *reinterpret_cast<uint2*>(q + blk * 32 + part * 8) = make_uint2(packed[0], packed[1]);
+        if (part == 0) ds[blk] = word;
+    }
 }
 
 template <class Src>
 hipError_t launch(Src src, int64_t nblocks, int8_t* q, uint32_t* ds, hipStream_t stream) {
     const int64_t lanes = nblocks * 4;
     const unsigned grid = (unsigned)((lanes + 255) / 256);
-    hipLaunchKernelGGL((q8_quantize_kernel<Src>), dim3(grid), dim3(256), 0, stream, src, nblocks, q, ds);
+    hipLaunchKernelGGL((q8_quantize_kernel<Src, false>), dim3(grid), dim3(256), 0, stream, src, nblocks,
+                       0, 0, q, (uint16_t*)nullptr, ds);
     return hipGetLastError();
 }
 
@@ -132,6 +181,17 @@ hipError_t launch(Src src, int64_t nblocks, int8_t* q, uint32_t* ds, hipStream_t
 hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32_t* ds,
                               hipStream_t stream) {
     return launch(PlainSrc{x}, nblocks, q, ds, stream);
+}
+
+hipError_t launch_q8_quantize_tiled(const float* x, int n, int k, uint16_t* qt, uint32_t* ds,
+                                    hipStream_t stream) {
+    // 16 tokens x one block per wave, over whole tiles of 128 tokens
+    const int C = k / 32;
+    const int64_t waves = (int64_t)((n + 127) / 128) * 8 * C;
+    const unsigned grid = (unsigned)((waves * 64 + 255) / 256);
+    hipLaunchKernelGGL((q8_quantize_kernel<PlainSrc, true>), dim3(grid), dim3(256), 0, stream, PlainSrc{x},
+                       (int64_t)n * C, n, C, (int8_t*)nullptr, qt, ds);
+    return hipGetLastError();
 }
 
 hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,

@@ -69,13 +69,32 @@ def test_quantize_validation(lib, args, want):
     assert lib.q8_quantize_silu_mul(x, A, n, k, q, ds, None) == want
 
 
+@pytest.mark.parametrize("args,want", [
+    ((A, -1, 256, A, A), SHAPE),
+    ((A, 4, 0, A, A), SHAPE),
+    ((A, 4, 64, A, A), SHAPE),           # the tiled codes need k % 256 == 0
+    ((A, 4, (1 << 24) + 256, A, A), OVERFLOW),
+    ((A, (1 << 31) - 127, 256, A, A), OVERFLOW),
+    ((0, 4, 256, A, A), NULL),
+    ((A, 4, 256, 0, A), NULL),
+    ((A, 4, 256, A, 0), NULL),
+    ((MIS, 4, 256, A, A), ALIGN),
+    ((A, 4, 256, MIS, A), ALIGN),
+    ((A, 4, 256, A, MIS), ALIGN),
+    ((A, 0, 256, 0, 0), OK),
+])
+def test_quantize_tiled_validation(lib, args, want):
+    assert lib.q8_quantize_rows_tiled(*args, None) == want
+
+
 def test_silu_quantize_checks_up(lib):
     assert lib.q8_quantize_silu_mul(A, 0, 4, 64, A, A, None) == NULL
     assert lib.q8_quantize_silu_mul(A, MIS, 4, 64, A, A, None) == ALIGN
 
 
 MMQ_CALLS = ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-             "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out"]
+             "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
+             "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out"]
 
 
 @pytest.mark.parametrize("fn", MMQ_CALLS)
@@ -101,7 +120,8 @@ def test_mmq_validation(lib, fn, args, want):
 
 
 @pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-                                "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out"])
+                                "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
+                                "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out"])
 def test_fold_needs_scales(lib, fn):
     assert getattr(lib, fn)(A, 8, 512, A, 0, 3, A, None) == NULL
     assert getattr(lib, fn)(A, 8, 512, A, MIS, 3, A, None) == ALIGN
@@ -121,6 +141,17 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.mmq_q6k_q8_f16out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.q4k_repack(A, 8, 512, A, None) == DEVICE
     assert lib.mmq_q4kr_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.q8_quantize_rows_tiled(A, 4, 256, A, A, None) == DEVICE
+    assert lib.mmq_q4k_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.mmq_q4kr_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+
+
+def test_tiled_fold_token_limit(lib):
+    # the operand tiles round n up to 128 tokens: n within 127 of 2^31 is
+    # rejected (n*k and n*m are inside the other limits here)
+    n = (1 << 31) - 100
+    assert lib.mmq_q4k_q8t_fp32out(A, 8, 256, A, A, n, A, None) == OVERFLOW
+    assert lib.mmq_q4kr_q8t_fp32out(A, 8, 256, A, A, n, A, None) == OVERFLOW
 
 
 @pytest.mark.parametrize("args,want", [
