@@ -67,8 +67,6 @@ def build_workload(name: str):
                 {"x": synth.q6k_activation("wide_in", n)}, [("wide_in", f, "x")])
     if name.startswith("t_"):
         desc, inputs, mats = build_workload(name[2:])
-        if any(not isinstance(f, synth.Q4KFields) for _, f, _ in mats):
-            raise SystemExit("the operand-tile entry points are for q4_K weights")
         return (dict(desc, tiles=True, workload=desc["workload"] +
                      ", activations quantized to binary16 operand tiles (q8_quantize_rows_tiled)"),
                 inputs, mats)
@@ -307,7 +305,8 @@ def main():
     if desc.get("tiles"):
         if args.f16_out:
             raise SystemExit("the operand-tile entry points are float32 only")
-        names = ["mmq_q4kr_q8t_fp32out" if desc.get("repacked") else "mmq_q4k_q8t_fp32out"]
+        names = ["mmq_q4kr_q8t_fp32out" if desc.get("repacked") else
+                 "mmq_q6k_q8t_fp32out" if isinstance(mats[0][1], synth.Q6KFields) else "mmq_q4k_q8t_fp32out"]
     mmq_name = "+".join(names)
     calls = [getattr(binding, names[0] if desc.get("repacked") or desc.get("tiles")
                      else weight_format(f)[2] + suffix)

@@ -263,6 +263,18 @@ int mmq_q4k_q8t_fp32out(const void *w, int64_t m, int64_t k, const uint16_t *qt,
 int mmq_q4kr_q8t_fp32out(const void *wr, int64_t m, int64_t k, const uint16_t *qt,
                          const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
 
+/*
+ * mmq_q6k_q8t_fp32out - mmq_q6k_q8_fp32out with the activations as operand
+ * tiles (from q8_quantize_rows_tiled; one tiled quantization serves q4_K and
+ * q6_K layers alike).  Every n runs the q6_K binary16-MFMA kernel, whose
+ * producers copy the tiles straight into LDS; same arithmetic in the same
+ * order, so the result equals mmq_q6k_q8_fp32out's bit for bit wherever that
+ * takes the binary16 kernel (n > 8).  Other arguments, errors and empty
+ * calls as for mmq_q6k_q8_fp32out, and n at most 2^31 - 128.
+ */
+int mmq_q6k_q8t_fp32out(const void *w, int64_t m, int64_t k, const uint16_t *qt,
+                        const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);
 

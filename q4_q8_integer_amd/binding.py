@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
            "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "q4k_repack",
            "mmq_q4kr_q8_fp32out", "q8_quantize_rows_tiled", "mmq_q4k_q8t_fp32out",
-           "mmq_q4kr_q8t_fp32out", "mmq_status_string")
+           "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out", "mmq_status_string")
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
               "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
-              "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out")
+              "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out")
 _lib = None
 
 
@@ -134,6 +134,11 @@ def mmq_q4k_q8t_fp32out(w, m, k, qt, ds, n, out):
 def mmq_q4kr_q8t_fp32out(wr, m, k, qt, ds, n, out):
     _check("mmq_q4kr_q8t_fp32out", load_library().mmq_q4kr_q8t_fp32out(
         _ptr(wr), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
+
+
+def mmq_q6k_q8t_fp32out(w, m, k, qt, ds, n, out):
+    _check("mmq_q6k_q8t_fp32out", load_library().mmq_q6k_q8t_fp32out(
+        _ptr(w), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q6k_q8(w, m, k, q, ds, n, dots):
@@ -280,6 +285,20 @@ def fp32_tiles(w: torch.Tensor, m: int, k: int, qt: torch.Tensor, ds: torch.Tens
     else:
         _need(out, torch.float32, "out")
     (mmq_q4kr_q8t_fp32out if repacked else mmq_q4k_q8t_fp32out)(w, m, k, qt, ds, n, out)
+    return out
+
+
+def q6k_fp32_tiles(w: torch.Tensor, m: int, k: int, qt: torch.Tensor, ds: torch.Tensor, out=None):
+    """The q6_K fold on q8 operand tiles (from quantize_tiled): float32 [n, m]."""
+    _need(w, torch.uint8, "w")
+    _need(qt, torch.int16, "qt")
+    _need(ds, torch.int32, "ds")
+    n = ds.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=ds.device)
+    else:
+        _need(out, torch.float32, "out")
+    mmq_q6k_q8t_fp32out(w, m, k, qt, ds, n, out)
     return out
 
 

@@ -121,6 +121,10 @@ hipError_t launch_q6k_i8(const uint8_t* w, int m, int k, const int8_t* q, const 
 hipError_t launch_q6k_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n,
                           void* out, bool half_out, hipStream_t stream);
 
+// launch_q6k_f16 with the activations as q8 operand tiles (float32 output).
+hipError_t launch_q6k_f16_tiles(const uint8_t* w, int m, int k, const uint16_t* qt, const uint32_t* ds,
+                                int n, float* out, hipStream_t stream);
+
 // out[t][o] for 1 <= n <= kQ6kGemvMaxN: 4-way int8 dots on the vector ALU.
 hipError_t launch_q6k_gemv(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                            int n, void* out, bool half_out, hipStream_t stream);

@@ -319,6 +319,20 @@ int mmq_q4kr_q8t_fp32out(const void* wr, int64_t m, int64_t k, const uint16_t* q
     return tiles_fold_entry(wr, true, m, k, qt, ds, n, out, stream);
 }
 
+int mmq_q6k_q8t_fp32out(const void* w, int64_t m, int64_t k, const uint16_t* qt,
+                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
+    bool empty = false;
+    int rc = check_mmq(w, m, k, reinterpret_cast<const int8_t*>(qt), n, out, &empty, mmq::kQ6kBlockBytes);
+    if (rc != MMQ_OK || empty) return rc;
+    if (n > kMaxDim - 127 || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!ds) return MMQ_ERR_NULL;
+    if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    rc = check_device();
+    if (rc != MMQ_OK) return rc;
+    return hip_status(mmq::launch_q6k_f16_tiles(static_cast<const uint8_t*>(w), (int)m, (int)k, qt, ds,
+                                                (int)n, out, stream));
+}
+
 const char* mmq_status_string(int status) {
     switch (status) {
         case MMQ_OK: return "MMQ_OK";

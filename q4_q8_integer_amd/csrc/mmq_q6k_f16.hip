@@ -51,6 +51,10 @@ constexpr int PT = 512;          // producer threads (8 waves)
 constexpr int NT = CT + PT;
 constexpr int CS = 2;            // chunks per stage (64 k)
 constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer resource on gfx950
+// s_waitcnt operand: at most n vector-memory operations outstanding.
+constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// One (token tile, 128-k stage) block of the q8 operand tiles (bytes).
+constexpr int kQtBlockBytes = 16 * BN * 16;
 
 __device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -89,11 +93,17 @@ __device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13
 }
 
 // One stage (64 k = 2 chunks) of operands.  Slots of 8 halves laid out
-// [chunk][part][k-half][lane-half][row or token]: the 32 lanes of a half-wave
-// read 32 consecutive 16-byte slots.
+// [chunk][part][j][lane-half][row or token]: MFMA j of a chunk takes, in
+// lane half g, k = 16 g + 8 j .. +7 of the chunk (the q4_K kernel's order, so
+// that q8 operand tiles serve both); the 32 lanes of a half-wave read 32
+// consecutive 16-byte slots.  The q8 operands are an LDS array of their own
+// (StageB), so that the compiler can tell direct-to-LDS copies into it from
+// the weight stores.
+struct StageB {
+    uint4 B[CS][2][2][BN];      // q8 as binary16
+};
 struct Stage {
     uint4 A[CS][2][2][2][BM];   // parts A1, A2
-    uint4 B[CS][2][2][BN];      // q8 as binary16
     float D[BM];                // 64*d of the super-block, per row
     float Da[CS][BN];           // da per (chunk, token)
 };
@@ -128,6 +138,7 @@ struct RawPieces {
 // token, so every offset fits 32 bits and an offset past the extent reads 0.
 struct Src {
     __amdgpu_buffer_rsrc_t w, q, ds;
+    const uint16_t* qt;   // operand tiles (QT): the workgroup's 128-token tile
     int extent;           // bytes of the weight resource
     int rbytes;           // bytes of one row (k/256 blocks)
     int y, word;          // q8 piece and scale-word byte offsets (stage 0)
@@ -162,6 +173,7 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
                                              toks * C * 4, kBufferFlags);
     // q8 piece pt: token pt & 127, 16-byte piece pt >> 7 of the stage's 64 bytes
     p.y = min(pt & (BN - 1), toks - 1) * K + 16 * (pt >> 7);
+    p.qt = reinterpret_cast<const uint16_t*>(q) + (int64_t)(tok0 >> 7) * (K >> 7) * (kQtBlockBytes / 2);
     // scale word (threads < 256): token pt & 127, chunk-in-stage pt >> 7
     p.word = (min(pt & (BN - 1), toks - 1) * C + ((pt >> 7) & 1)) * 4;
 }
@@ -211,8 +223,9 @@ __device__ __forceinline__ void store_raw(const RawPieces& rp, Raw16& raw, int p
     }
 }
 
+template <bool QT>
 __device__ __forceinline__ void load_stage(Raw& r, const Src& p, int pt, int st) {
-    r.y = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y, 64 * st, 0));
+    if (!QT) r.y = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(p.q, p.y, 64 * st, 0));
     r.word = pt < 2 * BN ? __builtin_amdgcn_raw_buffer_load_b32(p.ds, p.word, 8 * st, 0) : 0u;
 }
 
@@ -223,8 +236,9 @@ __device__ __forceinline__ void raw_run(const uint8_t* row_raw, int a, uint32_t 
     for (int i = 0; i < 5; ++i) v[i] = q4[i];
 }
 
-__device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, Stage& sg, const Src& p,
-                                              int rows, int pt, int st) {
+template <bool QT>
+__device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, Stage& sg, StageB& sgb,
+                                              const Src& p, int rows, int pt, int st) {
     int row, gi, kh;
     item_of(pt, row, gi, kh);
     const int sb = st >> 2, s4 = st & 3, h = s4 >> 1, g = 2 * (s4 & 1) + gi;
@@ -252,26 +266,29 @@ __device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, St
         a2[2 * i] = pk_mul_f16(pk_add_f16(and_or(y, 0x00030003u, 0x64006400u), m1026), c2);
         a2[2 * i + 1] = pk_mul_f16(pk_add_f16(and_or(y >> 8, 0x00030003u, 0x64006400u), m1026), c2);
     }
+    // the item's 16 k (16 kh .. +15 of chunk gi): its first 8 go to MFMA 0,
+    // its last 8 to MFMA 1, both in lane half kh
     const int c = gi;
-    sg.A[c][0][kh][0][row] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
-    sg.A[c][0][kh][1][row] = make_uint4(a1[4], a1[5], a1[6], a1[7]);
-    sg.A[c][1][kh][0][row] = make_uint4(a2[0], a2[1], a2[2], a2[3]);
-    sg.A[c][1][kh][1][row] = make_uint4(a2[4], a2[5], a2[6], a2[7]);
+    sg.A[c][0][0][kh][row] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+    sg.A[c][0][1][kh][row] = make_uint4(a1[4], a1[5], a1[6], a1[7]);
+    sg.A[c][1][0][kh][row] = make_uint4(a2[0], a2[1], a2[2], a2[3]);
+    sg.A[c][1][1][kh][row] = make_uint4(a2[4], a2[5], a2[6], a2[7]);
     if (gi == 0 && kh == 0) {
         const int od = lo + 208;   // 2-aligned: d lies in the dword at od & ~3
         const uint32_t dw = *reinterpret_cast<const uint32_t*>(row_raw + (od & ~3)) >> (8 * (od & 3));
         sg.D[row] = 64.0f * q6k::half_to_float(dw);
     }
-    // q8 piece: token pt & 127, k 16*(pt >> 7) .. +15 of the stage
-    {
+    // q8 piece: token pt & 127, k 16*(pt >> 7) .. +15 of the stage (QT: copied
+    // by dma_stage instead)
+    if (!QT) {
         const int tok = pt & (BN - 1), pc = pt >> 7, cc = pc >> 1, kk = pc & 1;
         uint32_t pp[8];
         q8_word(r.y.x, pp[0], pp[1]);
         q8_word(r.y.y, pp[2], pp[3]);
         q8_word(r.y.z, pp[4], pp[5]);
         q8_word(r.y.w, pp[6], pp[7]);
-        sg.B[cc][kk][0][tok] = make_uint4(pp[0], pp[1], pp[2], pp[3]);
-        sg.B[cc][kk][1][tok] = make_uint4(pp[4], pp[5], pp[6], pp[7]);
+        sgb.B[cc][0][kk][tok] = make_uint4(pp[0], pp[1], pp[2], pp[3]);
+        sgb.B[cc][1][kk][tok] = make_uint4(pp[4], pp[5], pp[6], pp[7]);
     }
     if (pt < 2 * BN) sg.Da[pt >> 7][pt & (BN - 1)] = q6k::half_to_float(r.word);
 }
@@ -280,13 +297,13 @@ __device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, St
 // FIRST: the stage opens a super-block (the first chunk sets acc_b);
 // LAST: it closes one (out += 64 d * acc_b).
 template <bool FIRST, bool LAST>
-__device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, int g, int l32,
-                                              v16f (&acc)[2], v16f (&accb)[2]) {
+__device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb, int wm, int wn, int g,
+                                              int l32, v16f (&acc)[2], v16f (&accb)[2]) {
     const int t = wn * 32 + l32;
 #pragma unroll
     for (int c = 0; c < CS; ++c) {
-        const v8h b0 = __builtin_bit_cast(v8h, sg.B[c][0][g][t]);
-        const v8h b1 = __builtin_bit_cast(v8h, sg.B[c][1][g][t]);
+        const v8h b0 = __builtin_bit_cast(v8h, sb.B[c][0][g][t]);
+        const v8h b1 = __builtin_bit_cast(v8h, sb.B[c][1][g][t]);
         const float da = sg.Da[c][t];
         v16f pr[2];
         const v16f zero = {};
@@ -337,17 +354,60 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, int wm, int wn, i
     }
 }
 
+// QT: a stage's q8 operands (64 k) are the half (st & 1) of the operand-tile
+// block of 128 k, slot rows 8 (st & 1) .. +7: 16 KiB, copied with 16
+// direct-to-LDS loads of one KiB (64 token slots), 2 per producer wave.  As
+// in the q4_K kernel, the copies are inline asm outside the compiler's wait
+// bookkeeping, and the producer loop completes older loads before issuing
+// them and waits for everything before the stage barrier.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// M0 is a reserved register; in this kernel nothing else sets or reads it,
+// so the clobber only tells the compiler what the asm does.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void dma_stage(StageB& sb, const Src& p, int st, int pw, int lane) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p.qt + (int64_t)(st >> 1) * (kQtBlockBytes / 2));
+    const u32x4 rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)kQtBlockBytes,
+                        (uint32_t)kBufferFlags};
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&sb.B[0][0][0][0];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = pw * 2 + j, row = i >> 1, half = i & 1;
+        const int dst = row * BN + half * 64;
+        lds_copy16(rsrc, base + 16 * dst, ((8 * (st & 1) + row) * BN + half * 64 + lane) * 16);
+    }
+}
+
+// An empty asm that reads registers a producer loaded earlier: the compiler
+// completes those loads here, before the uncounted copies are issued.
+__device__ __forceinline__ void settle(const Raw& r) { asm volatile("" ::"v"(r.word)); }
+__device__ __forceinline__ void settle(const RawPieces& rp) {
+#pragma unroll
+    for (int j = 0; j < kRawPiecesPerThread; ++j)
+        asm volatile("" ::"v"(rp.v[j].x), "v"(rp.v[j].y), "v"(rp.v[j].z), "v"(rp.v[j].w));
+}
+
 // Waves 0-7 consume (MFMA + fold), waves 8-15 produce (load, convert).  Two
 // LDS stages alternate: while the consumers work on stage s, the producers
 // fill stage s+1, their loads running one stage further ahead in registers.
 // One workgroup barrier per stage.
-template <bool H>
+template <bool H, bool QT>
 __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restrict__ w,
                                                          const int8_t* __restrict__ q,
                                                          const uint32_t* __restrict__ ds,
                                                          int M, int N, int K, int tiles_m,
                                                          void* __restrict__ out) {
     __shared__ Stage stage[2];
+    __shared__ StageB stage_b[2];
     __shared__ Raw16 raw[2];
 
     const int tid = threadIdx.x;
@@ -370,17 +430,27 @@ __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restri
         RawPieces rp;
         load_raw(rp, src, rows, pt, 0);
         store_raw(rp, raw[0], pt);
-        load_stage(ra, src, pt, 0);
+        load_stage<QT>(ra, src, pt, 0);
+        const int pw = __builtin_amdgcn_readfirstlane(pt >> 6), lane = pt & 63;
         __syncthreads();   // raw copy 0 visible (the consumers meet it too)
         for (int it = 0; it < stages; it += 2) {
             const int sb = it >> 2;
+            if (QT) settle(ra);
             if ((it & 3) == 0) load_raw(rp, src, rows, pt, min(sb + 1, S - 1));
-            load_stage(rb, src, pt, it + 1);
-            convert_stage(ra, raw[sb & 1], stage[0], src, rows, pt, it);
+            load_stage<QT>(rb, src, pt, it + 1);
+            if (QT) dma_stage(stage_b[0], src, it, pw, lane);
+            convert_stage<QT>(ra, raw[sb & 1], stage[0], stage_b[0], src, rows, pt, it);
+            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
             __syncthreads();
-            load_stage(ra, src, pt, min(it + 2, stages - 1));
-            convert_stage(rb, raw[sb & 1], stage[1], src, rows, pt, it + 1);
+            if (QT) {
+                settle(rb);
+                settle(rp);
+            }
+            load_stage<QT>(ra, src, pt, min(it + 2, stages - 1));
+            if (QT) dma_stage(stage_b[1], src, it + 1, pw, lane);
+            convert_stage<QT>(rb, raw[sb & 1], stage[1], stage_b[1], src, rows, pt, it + 1);
             if ((it & 3) == 0 && sb + 1 < S) store_raw(rp, raw[(sb + 1) & 1], pt);
+            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
             __syncthreads();
         }
         __syncthreads();  // the consumers' last stage
@@ -401,13 +471,13 @@ __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restri
     __syncthreads();   // the producers' raw copy 0
     __syncthreads();
     for (int st = 0; st < stages; st += 4) {
-        consume_stage<true, false>(stage[0], wm, wn, g, l32, acc, accb);
+        consume_stage<true, false>(stage[0], stage_b[0], wm, wn, g, l32, acc, accb);
         __syncthreads();
-        consume_stage<false, false>(stage[1], wm, wn, g, l32, acc, accb);
+        consume_stage<false, false>(stage[1], stage_b[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
-        consume_stage<false, false>(stage[0], wm, wn, g, l32, acc, accb);
+        consume_stage<false, false>(stage[0], stage_b[0], wm, wn, g, l32, acc, accb);
         __syncthreads();
-        consume_stage<false, true>(stage[1], wm, wn, g, l32, acc, accb);
+        consume_stage<false, true>(stage[1], stage_b[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
     }
 
@@ -440,8 +510,19 @@ hipError_t launch_q6k_f16(const uint8_t* w, int m, int k, const int8_t* q, const
     const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_out ? (const void*)mmq_q6k_f16_kernel<true> : (const void*)mmq_q6k_f16_kernel<false>;
+    const void* f = half_out ? (const void*)mmq_q6k_f16_kernel<true, false> : (const void*)mmq_q6k_f16_kernel<false, false>;
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+}
+
+hipError_t launch_q6k_f16_tiles(const uint8_t* w, int m, int k, const uint16_t* qt, const uint32_t* ds,
+                                int n, float* out, hipStream_t stream) {
+    int tiles_m = (m + BM - 1) / BM;
+    const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    const int8_t* q = reinterpret_cast<const int8_t*>(qt);
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
+                    (void*)&tiles_m, (void*)&out};
+    return hipLaunchKernel((const void*)mmq_q6k_f16_kernel<false, true>, dim3((unsigned)tiles), dim3(NT), args,
+                           0, stream);
 }
 
 }  // namespace mmq

@@ -94,7 +94,7 @@ def test_silu_quantize_checks_up(lib):
 
 MMQ_CALLS = ["mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
              "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
-             "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out"]
+             "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out"]
 
 
 @pytest.mark.parametrize("fn", MMQ_CALLS)
@@ -121,7 +121,7 @@ def test_mmq_validation(lib, fn, args, want):
 
 @pytest.mark.parametrize("fn", ["mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
                                 "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
-                                "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out"])
+                                "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out"])
 def test_fold_needs_scales(lib, fn):
     assert getattr(lib, fn)(A, 8, 512, A, 0, 3, A, None) == NULL
     assert getattr(lib, fn)(A, 8, 512, A, MIS, 3, A, None) == ALIGN
@@ -144,6 +144,7 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.q8_quantize_rows_tiled(A, 4, 256, A, A, None) == DEVICE
     assert lib.mmq_q4k_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4kr_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
+    assert lib.mmq_q6k_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
 
 
 def test_tiled_fold_token_limit(lib):
@@ -152,6 +153,7 @@ def test_tiled_fold_token_limit(lib):
     n = (1 << 31) - 100
     assert lib.mmq_q4k_q8t_fp32out(A, 8, 256, A, A, n, A, None) == OVERFLOW
     assert lib.mmq_q4kr_q8t_fp32out(A, 8, 256, A, A, n, A, None) == OVERFLOW
+    assert lib.mmq_q6k_q8t_fp32out(A, 8, 256, A, A, n, A, None) == OVERFLOW
 
 
 @pytest.mark.parametrize("args,want", [

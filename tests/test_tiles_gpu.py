@@ -1,10 +1,10 @@
 """The q8 operand tiles on the GPU: q8_quantize_rows_tiled writes the
 oracle's tile layout bit for bit (and the scale words of q8_quantize_rows),
 touching nothing outside its buffers; the folds on the tiles
-(mmq_q4k_q8t_fp32out on q4_K rows, mmq_q4kr_q8t_fp32out on repacked records)
-meet the float32 bar against the oracle for every n, and equal
-mmq_q4k_q8_fp32out bit for bit wherever that runs the same binary16-MFMA
-kernel (n > 64)."""
+(mmq_q4k_q8t_fp32out on q4_K rows, mmq_q4kr_q8t_fp32out on repacked records,
+mmq_q6k_q8t_fp32out on q6_K rows) meet the float32 bar against the oracle for
+every n, and equal the int8-code entry point bit for bit wherever that runs
+the same binary16-MFMA kernel (q4_K n > 64, q6_K n > 8)."""
 import numpy as np
 import pytest
 import torch
@@ -84,3 +84,27 @@ def test_tiles_qproj_full():
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int32), base.view(torch.int32))
     assert torch.equal(got_r.view(torch.int32), base.view(torch.int32))
+
+
+# q6_K on the same tiles: 9 tokens and more take the binary16 kernel on both
+# sides (bitwise equal); one token checks the bar only.
+@pytest.mark.parametrize("n,m,k", [(1, 33, 512), (9, 40, 768), (65, 129, 512), (300, 200, 2304),
+                                   (200, 40, 16640), (1100, 4096, 512)])
+def test_q6k_tiles_fold(n, m, k):
+    note("q6k tiles fold n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_q6k_fields(930 + n, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(930 + n, n, k, "outliers")
+    w = synth.pack_q6k(f)
+    wd = to_dev(w)
+    xd = to_dev(x)
+    qt, ds = binding.quantize_tiled(xd)
+    got = binding.q6k_fp32_tiles(wd, m, k, qt, ds)
+    q, ds_rows = binding.quantize(xd)
+    base = binding.q6k_fp32(wd, m, k, q, ds_rows)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    if n > 8:
+        assert np.array_equal(got.view(np.uint32), base.cpu().numpy().view(np.uint32))
+    toks = sample_tokens(n, 24)
+    rq, rds = oracle.quantize(x[toks])
+    check_fp32(got[toks], oracle.q6k_out_f64(w, m, k, rq, rds), "q6k tiles fold")
