@@ -247,6 +247,16 @@ int q8_quantize_rows_tiled(const float *x, int64_t n, int64_t k, uint16_t *qt, u
                            hipStream_t stream);
 
 /*
+ * q8_quantize_silu_mul_tiled - q8_quantize_silu_mul (h = SiLU(gate) * up,
+ * never written) with the codes written as operand tiles, as
+ * q8_quantize_rows_tiled does; codes and words bit for bit those of
+ * q8_quantize_silu_mul.  Errors as for q8_quantize_rows_tiled, with `up`
+ * checked beside `gate`.
+ */
+int q8_quantize_silu_mul_tiled(const float *gate, const float *up, int64_t n, int64_t k,
+                               uint16_t *qt, uint32_t *ds, hipStream_t stream);
+
+/*
  * mmq_q4k_q8t_fp32out / mmq_q4kr_q8t_fp32out - mmq_q4k_q8_fp32out (q4_K
  * rows) and mmq_q4kr_q8_fp32out (q4k_repack records) with the activations
  * as operand tiles (qt and ds from q8_quantize_rows_tiled of the same n and

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
            "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "q4k_repack",
            "mmq_q4kr_q8_fp32out", "q8_quantize_rows_tiled", "mmq_q4k_q8t_fp32out",
-           "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out", "mmq_status_string")
+           "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out", "q8_quantize_silu_mul_tiled",
+           "mmq_status_string")
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
               "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
               "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out")
@@ -46,6 +47,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_quantize_rows.restype = ctypes.c_int
     lib.q8_quantize_rows_tiled.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_rows_tiled.restype = ctypes.c_int
+    lib.q8_quantize_silu_mul_tiled.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.q8_quantize_silu_mul_tiled.restype = ctypes.c_int
     lib.q8_quantize_silu_mul.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.q8_quantize_silu_mul.restype = ctypes.c_int
     lib.q4k_repack.argtypes = [vp, i64, i64, vp, vp]
@@ -94,6 +97,12 @@ def q8_quantize_rows_tiled(x, n, k, qt, ds):
     """Enqueue the quantizer with the codes as binary16 operand tiles."""
     _check("q8_quantize_rows_tiled", load_library().q8_quantize_rows_tiled(
         _ptr(x), n, k, _ptr(qt), _ptr(ds), _stream()))
+
+
+def q8_quantize_silu_mul_tiled(gate, up, n, k, qt, ds):
+    """Enqueue the fused SiLU-gate quantizer with the codes as operand tiles."""
+    _check("q8_quantize_silu_mul_tiled", load_library().q8_quantize_silu_mul_tiled(
+        _ptr(gate), _ptr(up), n, k, _ptr(qt), _ptr(ds), _stream()))
 
 
 def q8_quantize_silu_mul(gate, up, n, k, q, ds):
@@ -180,6 +189,19 @@ def quantize_tiled(x: torch.Tensor):
     qt = torch.empty(tiles_elems(n, k), dtype=torch.int16, device=x.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
     q8_quantize_rows_tiled(x, n, k, qt, ds)
+    return qt, ds
+
+
+def quantize_silu_mul_tiled(gate: torch.Tensor, up: torch.Tensor):
+    """Operand tiles of q8(SiLU(gate) * up): (qt int16 [tiles_elems(n, k)], ds int32 [n, k/32])."""
+    _need(gate, torch.float32, "gate")
+    _need(up, torch.float32, "up")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    n, k = gate.shape
+    qt = torch.empty(tiles_elems(n, k), dtype=torch.int16, device=gate.device)
+    ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=gate.device)
+    q8_quantize_silu_mul_tiled(gate, up, n, k, qt, ds)
     return qt, ds
 
 

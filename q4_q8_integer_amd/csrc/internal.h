@@ -20,6 +20,10 @@ hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32
 hipError_t launch_q8_quantize_tiled(const float* x, int n, int k, uint16_t* qt, uint32_t* ds,
                                     hipStream_t stream);
 
+// The same, with the codes written as operand tiles.
+hipError_t launch_q8_quantize_silu_mul_tiled(const float* g, const float* u, int n, int k, uint16_t* qt,
+                                             uint32_t* ds, hipStream_t stream);
+
 // q8 quantize of h = float32(g*u / (1 + exp(-g))) (float64 evaluation).
 hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,
                                        uint32_t* ds, hipStream_t stream);

@@ -214,6 +214,18 @@ int q8_quantize_silu_mul(const float* gate, const float* up, int64_t n, int64_t 
     return hip_status(mmq::launch_q8_quantize_silu_mul(gate, up, n * (k / 32), q, ds, stream));
 }
 
+int q8_quantize_silu_mul_tiled(const float* gate, const float* up, int64_t n, int64_t k, uint16_t* qt,
+                               uint32_t* ds, hipStream_t stream) {
+    if (n < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
+    if (n > kMaxDim - 127 || k > kMaxK || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (n == 0) return MMQ_OK;
+    if (!gate || !up || !qt || !ds) return MMQ_ERR_NULL;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(qt) || !aligned16(ds)) return MMQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != MMQ_OK) return dev;
+    return hip_status(mmq::launch_q8_quantize_silu_mul_tiled(gate, up, (int)n, (int)k, qt, ds, stream));
+}
+
 int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
                int64_t n, int32_t* dots, hipStream_t stream) {
     (void)ds;  // not read: the block dots do not depend on the scales

@@ -183,15 +183,25 @@ hipError_t launch_q8_quantize(const float* x, int64_t nblocks, int8_t* q, uint32
     return launch(PlainSrc{x}, nblocks, q, ds, stream);
 }
 
-hipError_t launch_q8_quantize_tiled(const float* x, int n, int k, uint16_t* qt, uint32_t* ds,
-                                    hipStream_t stream) {
-    // 16 tokens x one block per wave, over whole tiles of 128 tokens
+// 16 tokens x one block per wave, over whole tiles of 128 tokens.
+template <class Src>
+hipError_t launch_tiled(Src src, int n, int k, uint16_t* qt, uint32_t* ds, hipStream_t stream) {
     const int C = k / 32;
     const int64_t waves = (int64_t)((n + 127) / 128) * 8 * C;
     const unsigned grid = (unsigned)((waves * 64 + 255) / 256);
-    hipLaunchKernelGGL((q8_quantize_kernel<PlainSrc, true>), dim3(grid), dim3(256), 0, stream, PlainSrc{x},
+    hipLaunchKernelGGL((q8_quantize_kernel<Src, true>), dim3(grid), dim3(256), 0, stream, src,
                        (int64_t)n * C, n, C, (int8_t*)nullptr, qt, ds);
     return hipGetLastError();
+}
+
+hipError_t launch_q8_quantize_tiled(const float* x, int n, int k, uint16_t* qt, uint32_t* ds,
+                                    hipStream_t stream) {
+    return launch_tiled(PlainSrc{x}, n, k, qt, ds, stream);
+}
+
+hipError_t launch_q8_quantize_silu_mul_tiled(const float* g, const float* u, int n, int k, uint16_t* qt,
+                                             uint32_t* ds, hipStream_t stream) {
+    return launch_tiled(SiluMulSrc{g, u}, n, k, qt, ds, stream);
 }
 
 hipError_t launch_q8_quantize_silu_mul(const float* g, const float* u, int64_t nblocks, int8_t* q,

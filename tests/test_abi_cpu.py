@@ -85,6 +85,13 @@ def test_quantize_validation(lib, args, want):
 ])
 def test_quantize_tiled_validation(lib, args, want):
     assert lib.q8_quantize_rows_tiled(*args, None) == want
+    x, n, k, qt, ds = args
+    assert lib.q8_quantize_silu_mul_tiled(x, A, n, k, qt, ds, None) == want
+
+
+def test_silu_quantize_tiled_checks_up(lib):
+    assert lib.q8_quantize_silu_mul_tiled(A, 0, 4, 256, A, A, None) == NULL
+    assert lib.q8_quantize_silu_mul_tiled(A, MIS, 4, 256, A, A, None) == ALIGN
 
 
 def test_silu_quantize_checks_up(lib):
@@ -142,6 +149,7 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.q4k_repack(A, 8, 512, A, None) == DEVICE
     assert lib.mmq_q4kr_q8_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.q8_quantize_rows_tiled(A, 4, 256, A, A, None) == DEVICE
+    assert lib.q8_quantize_silu_mul_tiled(A, A, 4, 256, A, A, None) == DEVICE
     assert lib.mmq_q4k_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q4kr_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE
     assert lib.mmq_q6k_q8t_fp32out(A, 8, 512, A, A, 3, A, None) == DEVICE

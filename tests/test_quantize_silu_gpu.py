@@ -1,6 +1,7 @@
 """q8_quantize_silu_mul on the GPU: bit-exact against the oracle (q and the
 scale words) on ragged shapes, extreme gates and the full FFN down-projection
-input, and equal to q8_quantize_rows applied to the oracle's h."""
+input, and equal to q8_quantize_rows applied to the oracle's h; its tiled
+output (q8_quantize_silu_mul_tiled) is the oracle's operand tiles of those codes."""
 import numpy as np
 import pytest
 import torch
@@ -81,3 +82,16 @@ def test_silu_quantize_guard_bands_and_empty():
     z = torch.zeros((0, 64), device="cuda:0")
     q0, ds0 = binding.quantize_silu_mul(z, z)
     assert q0.shape == (0, 64) and ds0.shape == (0, 2)
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (77, 11008), (130, 2048), (2630, 11008)])
+def test_silu_quantize_tiled_matches_oracle(n, k):
+    """The tiled output: the oracle's operand tiles of the oracle's codes, and
+    its scale words, bit for bit."""
+    g, u = _inputs(n * 5 + k, n, k)
+    note("silu quantize tiled n=%d k=%d" % (n, k))
+    qt, ds = binding.quantize_silu_mul_tiled(to_dev(g), to_dev(u))
+    torch.cuda.synchronize()
+    rq, rds = oracle.quantize_silu_mul(g, u)
+    assert np.array_equal(qt.cpu().numpy().view(np.uint16), oracle.q8_tiles(rq))
+    assert np.array_equal(host_ds(ds), rds)
