@@ -34,6 +34,11 @@
 // (sc and m as bytes) in place of the 16-byte block header, and skip the
 // 6-bit scale decode; everything after the scales is the same arithmetic, so
 // the two layouts give the same result bit for bit.
+//
+// With QT the activations arrive as q8_quantize_rows_tiled's operand tiles,
+// already binary16 and already in the B slot order: the producers copy each
+// stage's 32 KiB block into LDS with buffer_load ... lds and convert weights
+// only.
 #include "internal.h"
 
 namespace mmq {
@@ -481,8 +486,9 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb,
     }
 }
 
-// Waves 0-3 consume (MFMA + fold), waves 4-7 produce (load, convert to
-// binary16 operand slots).  Two LDS stages alternate: while the consumers
+// Waves 0-7 consume (MFMA + fold), waves 8-15 produce (load, convert to
+// binary16 operand slots, or with QT copy the tile block straight into LDS).
+// Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
 template <int TB, bool H, bool REP, bool QT>

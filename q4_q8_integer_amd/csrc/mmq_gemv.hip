@@ -77,18 +77,31 @@ __device__ __forceinline__ uint32_t ld4w(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
-// Chunk dots of pair p in super-block J of the step, as float32 (exact:
-// |D| < 2^16):  D0 = sum_i dot4(lo[i], token word i), D1 = sum_i dot4(hi[i],
-// token word 8 + i), where token words 4c..4c+3 sit in lane 4J + c of the DPP
-// row (row_newbcast).  Inline asm hides these instructions from the
-// compiler's hazard checks, so the blocks keep the rules themselves: a DPP
-// read needs 2 wait states after a VALU write of its source (s_nop 1 first),
-// and a VALU other than a dot that reads a v_dot4 result needs 3 (the chains
-// are interleaved and converted in the order they finish).
+// Chunk dots of pair p in super-block J of the step:  D0 = sum_i dot4(lo[i],
+// token word i), D1 = sum_i dot4(hi[i], token word 8 + i), where token words
+// 4c..4c+3 sit in lane 4J + c of the DPP row (row_newbcast).  Each chain
+// starts from the bits of kMagic = 1.5 * 2^23 instead of 0: as |D| < 2^16,
+// the integer sum kMagic_bits + D is the float32 kMagic + D exactly, so the
+// results come back as floats with no conversion (see scaled_dot).  Inline
+// asm hides these instructions from the compiler's hazard checks, so the
+// blocks keep the rules themselves: a DPP read needs 2 wait states after a
+// VALU write of its source (s_nop 1 first), and a VALU other than a dot that
+// reads a v_dot4 result needs 3 (s_nop 2 last).
+constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr int kMagicBits = 0x4B400000;
+
+// dsc * D from a chain's result kMagic + D, rounded once as dsc * float(D)
+// would be: kneg = -kMagic * dsc is exact (dsc = d * sc carries at most 17
+// significant bits, times 3 * 2^22 at most 19), so the fused multiply-add
+// rounds the exact dsc * D.
+__device__ __forceinline__ float scaled_dot(float dsc, float kneg, float chain) {
+    return fmaf(dsc, chain, kneg);
+}
+
 template <int J>
 __device__ __forceinline__ void dots_two_tokens(float& a0, float& a1, float& b0, float& b1, v4u ta,
                                                 v4u tb, const int* lo, const int* hi) {
-    int A0 = 0, A1 = 0, B0 = 0, B1 = 0;
+    int A0 = kMagicBits, A1 = kMagicBits, B0 = kMagicBits, B1 = kMagicBits;
     asm(
         "s_nop 1\n\t"
         "v_dot4c_i32_i8_dpp %0, %4, %12 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n\t"
@@ -123,10 +136,7 @@ __device__ __forceinline__ void dots_two_tokens(float& a0, float& a1, float& b0,
         "v_dot4c_i32_i8_dpp %1, %7, %27 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %2, %11, %19 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %3, %11, %27 row_newbcast:%c31 row_mask:0xf bank_mask:0xf\n\t"
-        "v_cvt_f32_i32 %0, %0\n\t"
-        "v_cvt_f32_i32 %1, %1\n\t"
-        "v_cvt_f32_i32 %2, %2\n\t"
-        "v_cvt_f32_i32 %3, %3"
+        "s_nop 2"
         : "+v"(A0), "+v"(A1), "+v"(B0), "+v"(B1)
         : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3]), "v"(tb[0]), "v"(tb[1]), "v"(tb[2]), "v"(tb[3]),
           "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(lo[4]), "v"(lo[5]), "v"(lo[6]), "v"(lo[7]),
@@ -141,7 +151,7 @@ __device__ __forceinline__ void dots_two_tokens(float& a0, float& a1, float& b0,
 template <int J>
 __device__ __forceinline__ void dots_one_token(float& a0, float& a1, v4u ta, const int* lo,
                                                const int* hi) {
-    int A0 = 0, A1 = 0;
+    int A0 = kMagicBits, A1 = kMagicBits;
     asm(
         "s_nop 1\n\t"
         "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:%c22 row_mask:0xf bank_mask:0xf\n\t"
@@ -160,9 +170,7 @@ __device__ __forceinline__ void dots_one_token(float& a0, float& a1, v4u ta, con
         "v_dot4c_i32_i8_dpp %1, %4, %20 row_newbcast:%c25 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %0, %5, %13 row_newbcast:%c23 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %1, %5, %21 row_newbcast:%c25 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_cvt_f32_i32 %0, %0\n\t"
-        "v_cvt_f32_i32 %1, %1"
+        "s_nop 2"
         : "+v"(A0), "+v"(A1)
         : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3]),
           "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(lo[4]), "v"(lo[5]), "v"(lo[6]), "v"(lo[7]),
@@ -235,6 +243,7 @@ __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb,
         m1 = __builtin_amdgcn_ubfe(xm, sh + 8 + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + 8 + oh, 2) << 4);
     }
     const float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1;
+    const float kn0 = -kMagic * dsc0, kn1 = -kMagic * dsc1;
     const float dmm0 = -(dmin * (float)m0), dmm1 = -(dmin * (float)m1);
     int lo[8], hi[8];
 #pragma unroll
@@ -248,13 +257,15 @@ __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb,
     for (int t = 0; t + 1 < N; t += 2) {
         float a0, a1, b0, b1;
         dots_two_tokens<J>(a0, a1, b0, b1, tq[t], tq[t + 1], lo, hi);
-        fold_two_tokens<J>(acc[t], acc[t + 1], tda[t], tdass[t], tda[t + 1], tdass[t + 1], dsc0 * a0,
-                           dsc1 * a1, dsc0 * b0, dsc1 * b1, dmm0, dmm1);
+        fold_two_tokens<J>(acc[t], acc[t + 1], tda[t], tdass[t], tda[t + 1], tdass[t + 1],
+                           scaled_dot(dsc0, kn0, a0), scaled_dot(dsc1, kn1, a1),
+                           scaled_dot(dsc0, kn0, b0), scaled_dot(dsc1, kn1, b1), dmm0, dmm1);
     }
     if constexpr ((N & 1) != 0) {
         float a0, a1;
         dots_one_token<J>(a0, a1, tq[N - 1], lo, hi);
-        fold_one_token<J>(acc[N - 1], tda[N - 1], tdass[N - 1], dsc0 * a0, dsc1 * a1, dmm0, dmm1);
+        fold_one_token<J>(acc[N - 1], tda[N - 1], tdass[N - 1], scaled_dot(dsc0, kn0, a0),
+                          scaled_dot(dsc1, kn1, a1), dmm0, dmm1);
     }
 }
 
@@ -356,8 +367,19 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int 
     if constexpr (SW > 3) gemv_sb<N, 3, L>(st.hdr[3], st.qa[3], st.qb[3], p, ns > 3, st.tq, tda, tdass, acc);
 }
 
+// Waves per SIMD the register allocation is held to.  The repacked layout at
+// 8 tokens takes 148 VGPRs otherwise (3 waves per SIMD); held to 128 (4
+// waves, no spills) it measured 37.6 -> 35.1 us on 28672 x 8192 and 39.0 ->
+// 38.6 us on 8192 x 28672.  The GGUF layout at 7 tokens gained nothing from
+// the same (146 -> 128 VGPRs, within 2%), and at 8 it spills.
+template <int N, int L>
+constexpr int min_waves_per_simd() {
+    return L == kRepacked && N == 8 ? 4 : 1;
+}
+
 template <int N, int SW, bool H, int L>
-__global__ __launch_bounds__(64 * kMaxWaves) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(64 * kMaxWaves)
+__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<N, L>()))) void mmq_gemv_kernel(const uint8_t* __restrict__ w,
                                                                   const int8_t* __restrict__ q,
                                                                   const uint32_t* __restrict__ ds,
                                                                   int M, int K,

@@ -36,13 +36,22 @@ namespace {
 
 constexpr int kMaxWaves = 4;   // waves per workgroup (split of the super-blocks)
 
-// Four group dots of one token: D_g = sum_i dot4(cw[g][i], token word 4g + i
-// of the DPP row), as float32 (exact: |D| <= 65024).  The asm keeps the
+// Each dot chain starts from the bits of kMagic = 1.5 * 2^23 instead of 0:
+// as |D| < 2^22, the integer sum kMagic_bits + D is the float32 kMagic + D
+// exactly, and fma(dsc, kMagic + D, -kMagic * dsc) rounds the exact dsc * D
+// once, as dsc * float(D) does (-kMagic * dsc is exact: dsc = d * sc has at
+// most 19 significant bits, times 3 * 2^22 at most 21).  One instruction in
+// place of a conversion and a multiply.
+constexpr float kMagic = 12582912.0f;
+constexpr int kMagicBits = 0x4B400000;
+
+// Four group dots of one token: Df[g] = kMagic + sum_i dot4(cw[g][i], token
+// word 4g + i of the DPP row), exact as |D| <= 65024.  The asm keeps the
 // hazard rules the compiler cannot see: 2 wait states before a DPP read of a
 // VALU-written source (s_nop 1), and 3 between a v_dot4 result and a non-dot
-// VALU reading it (four interleaved chains, converted in the order they end).
+// VALU reading it (s_nop 2 last).
 __device__ __forceinline__ void group_dots(float (&Df)[4], uint32_t tok, const uint32_t (&cw)[4][4]) {
-    int A0 = 0, A1 = 0, A2 = 0, A3 = 0;
+    int A0 = kMagicBits, A1 = kMagicBits, A2 = kMagicBits, A3 = kMagicBits;
     asm("s_nop 1\n\t"
         "v_dot4c_i32_i8_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %1, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
@@ -60,11 +69,7 @@ __device__ __forceinline__ void group_dots(float (&Df)[4], uint32_t tok, const u
         "v_dot4c_i32_i8_dpp %1, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %2, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
         "v_dot4c_i32_i8_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 0\n\t"
-        "v_cvt_f32_i32 %0, %0\n\t"
-        "v_cvt_f32_i32 %1, %1\n\t"
-        "v_cvt_f32_i32 %2, %2\n\t"
-        "v_cvt_f32_i32 %3, %3"
+        "s_nop 2"
         : "+v"(A0), "+v"(A1), "+v"(A2), "+v"(A3)
         : "v"(tok), "v"(cw[0][0]), "v"(cw[0][1]), "v"(cw[0][2]), "v"(cw[0][3]), "v"(cw[1][0]),
           "v"(cw[1][1]), "v"(cw[1][2]), "v"(cw[1][3]), "v"(cw[2][0]), "v"(cw[2][1]), "v"(cw[2][2]),
@@ -221,16 +226,18 @@ __device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, const uint8_
         const uint32_t w0 = q6k::run_word(sc, 0, sh), w1 = q6k::run_word(sc, 1, sh);
         const uint32_t w2 = q6k::run_word(sc, 2, sh), w3 = q6k::run_word(sc, 3, sh);
         const uint32_t lo = h ? w2 : w0, hi = h ? w3 : w1;
-        float dsc[4];
+        float dsc[4], kn[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g) {
             dsc[g] = d * (float)(int)(int8_t)(((g >> 1) ? hi : lo) >> (8 * (2 * (g & 1) + e)));
+            kn[g] = -kMagic * dsc[g];
+        }
 #pragma unroll
         for (int t = 0; t < N; ++t) {
             float Df[4], y[4];
             group_dots(Df, f.tq[t][j], cw);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) y[g] = dsc[g] * Df[g];
+            for (int g = 0; g < 4; ++g) y[g] = fmaf(dsc[g], Df[g], kn[g]);
             fold4(acc[t], q6k::half_to_float(f.tw[t][j]), y);
         }
     }
