@@ -255,6 +255,23 @@ def pin_out_bruteforce(lib):
         assert np.abs(got - ref).max() <= 1e-12 * scale, "case %d" % seed
 
 
+def pin_out_negative_scales(lib):
+    """The super-block scales d and dmin are signed binary16 fields: with the
+    sign set on a random half of each, the fp64 output still equals the numpy
+    float64 matmul of the dequantized operands."""
+    for seed, (n, m, k) in enumerate([(5, 9, 512), (33, 17, 768)]):
+        f = synth.random_fields(60 + seed, m, k, sc_zero_frac=0.1)
+        rng = np.random.default_rng([60, seed])
+        f.d = np.where(rng.random(f.d.shape) < 0.5, -f.d, f.d).astype(np.float16)
+        f.dmin = np.where(rng.random(f.dmin.shape) < 0.5, -f.dmin, f.dmin).astype(np.float16)
+        assert (f.d < 0).any() and (f.dmin < 0).any()
+        x = synth.random_activations(60 + seed, n, k, "outliers")
+        q, ds = oracle.quantize(x, lib=lib)
+        got = oracle.out_f64(synth.pack_q4k(f), m, k, q, ds, lib=lib)
+        ref = deq_acts(q, ds) @ deq_weights(f).T
+        assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max(), "case %d" % seed
+
+
 def pin_out_special_cases(lib):
     """q4 = 0 leaves only the min term; m = 0 leaves only the main term;
     d = dmin = 0 gives exactly 0."""
@@ -568,7 +585,7 @@ def pin_q8_tiles(lib):
 
 ALL_PINS = [pin_f16_encode, pin_f16_decode, pin_q4k_golden_block, pin_q4k_roundtrip,
             pin_q8_golden, pin_q8_invariants, pin_q8_zero_block, pin_dots_bruteforce,
-            pin_dots_closed_forms, pin_out_bruteforce, pin_out_special_cases,
+            pin_dots_closed_forms, pin_out_bruteforce, pin_out_negative_scales, pin_out_special_cases,
             pin_out_zero_scale_block, pin_one_superblock,
             pin_q6k_golden_block, pin_q6k_roundtrip, pin_q6k_dots_bruteforce,
             pin_q6k_dots_closed_forms, pin_q6k_out_bruteforce, pin_q6k_out_special_cases,

@@ -166,6 +166,47 @@ def test_weight_bound(name, n):
 
 
 # ------------------------------------------------------------- metamorphic
+@pytest.mark.parametrize("n", [1, 4, 7, 9, 16, 33, 130])
+def test_negative_super_block_scales(n):
+    """d and dmin are signed binary16 fields: with the sign set on a random
+    half of each, every kernel (dot4, the few-token MFMA kernels, the binary16
+    kernel) on every weight layout and activation format meets the float32
+    bar against the oracle."""
+    m, k = 40, 768
+    note("negative scales n=%d" % n)
+    f = synth.random_fields(970 + n, m, k, sc_zero_frac=0.1)
+    rng = np.random.default_rng([970, n])
+    f.d = np.where(rng.random(f.d.shape) < 0.5, -f.d, f.d).astype(np.float16)
+    f.dmin = np.where(rng.random(f.dmin.shape) < 0.5, -f.dmin, f.dmin).astype(np.float16)
+    assert (f.d < 0).any() and (f.dmin < 0).any()
+    x = synth.random_activations(970 + n, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    wd = to_dev(w)
+    q, ds = gpu_quantize(x)
+    rq, rds = oracle.quantize(x)
+    ref = oracle.out_f64(w, m, k, rq, rds)
+    check_fp32(gpu_fp32(wd, m, k, q, ds), ref, "negative scales, q4_K rows")
+    wr = binding.repack(wd, m, k)
+    got_r = binding.fp32_repacked(wr, m, k, q, ds)
+    qt, dst = binding.quantize_tiled(to_dev(x))
+    got_t = binding.fp32_tiles(wd, m, k, qt, dst)
+    torch.cuda.synchronize()
+    check_fp32(got_r.cpu().numpy(), ref, "negative scales, repacked")
+    check_fp32(got_t.cpu().numpy(), ref, "negative scales, operand tiles")
+    # q6_K: d is a signed binary16 field as well (its 8-bit scales are signed
+    # already)
+    f6 = synth.random_q6k_fields(970 + n, m, k, sc_zero_frac=0.1)
+    f6.d = np.where(rng.random(f6.d.shape) < 0.5, -f6.d, f6.d).astype(np.float16)
+    w6 = synth.pack_q6k(f6)
+    w6d = to_dev(w6)
+    ref6 = oracle.q6k_out_f64(w6, m, k, rq, rds)
+    got6 = binding.q6k_fp32(w6d, m, k, q, ds)
+    got6t = binding.q6k_fp32_tiles(w6d, m, k, qt, dst)
+    torch.cuda.synchronize()
+    check_fp32(got6.cpu().numpy(), ref6, "negative scales, q6_K")
+    check_fp32(got6t.cpu().numpy(), ref6, "negative scales, q6_K on operand tiles")
+
+
 def test_run_to_run_and_token_slice_bitwise():
     f = synth.random_fields(61, 300, 1024)
     x = synth.random_activations(61, 200, 1024)
