@@ -369,8 +369,8 @@ __device__ __forceinline__ void compute_step(const Step<N, SW>& st, int ns, int 
 
 // Waves per SIMD the register allocation is held to.  The repacked layout at
 // 8 tokens takes 148 VGPRs otherwise (3 waves per SIMD); held to 128 (4
-// waves, no spills) it measured 37.6 -> 35.1 us on 28672 x 8192 and 39.0 ->
-// 38.6 us on 8192 x 28672.  The GGUF layout at 7 tokens gained nothing from
+// waves, at the cost of a 16-byte spill per lane) it measured 37.8 -> 35.4 us
+// on 28672 x 8192 and 39.0 -> 38.6 us on 8192 x 28672.  The GGUF layout at 7 tokens gained nothing from
 // the same (146 -> 128 VGPRs, within 2%), and at 8 it spills.
 template <int N, int L>
 constexpr int min_waves_per_simd() {
