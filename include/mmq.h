@@ -263,8 +263,10 @@ int q8_quantize_silu_mul_tiled(const float *gate, const float *up, int64_t n, in
  * k).  Every n runs the binary16-MFMA kernel, whose producers copy the tiles
  * straight into LDS instead of converting q8; the arithmetic and its order
  * are that kernel's, so the result equals mmq_q4k_q8_fp32out's bit for bit
- * wherever that takes the binary16 kernel (n > 64).  Meant for prefill (few
- * tokens run faster on mmq_q4k_q8_fp32out).  Other arguments, errors and
+ * wherever that takes the binary16 kernel (n > 64).  Meant for prefill.
+ * With few tokens it is faster than mmq_q4k_q8_fp32out only where m gives
+ * many 128-row tiles (m = 28672 at n = 33); with few row tiles (m = 8192)
+ * or n <= 8 the int8-code entry point is faster.  Other arguments, errors and
  * empty calls as for mmq_q4k_q8_fp32out / mmq_q4kr_q8_fp32out, and n at most
  * 2^31 - 128.
  */
