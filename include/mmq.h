@@ -263,7 +263,8 @@ int q8_quantize_silu_mul_tiled(const float *gate, const float *up, int64_t n, in
  * k).  Every n runs the binary16-MFMA kernel, whose producers copy the tiles
  * straight into LDS instead of converting q8; the arithmetic and its order
  * are that kernel's, so the result equals mmq_q4k_q8_fp32out's bit for bit
- * wherever that takes the binary16 kernel (n > 64).  Meant for prefill.
+ * wherever that takes the binary16 kernel (n > 64, and n > 32 where m
+ * gives at least 160 tiles of 128 x 128).  Meant for prefill.
  * With few tokens it is faster than mmq_q4k_q8_fp32out only where m gives
  * many 128-row tiles (m = 28672 at n = 33); with few row tiles (m = 8192)
  * or n <= 8 the int8-code entry point is faster.  Other arguments, errors and

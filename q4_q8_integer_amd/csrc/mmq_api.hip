@@ -61,14 +61,14 @@ int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, c
 // Kernel behind the fold entry points, by token count (measured on the
 // 28672 x 8192 and 8192 x 28672 matrices across n = 9..64):
 //   n <= 8:   the vector-ALU dot4 kernel;
-//   n <= 48:  the few-token int8-MFMA kernels (one 16-token tile up to
+//   n <= 32:  the few-token int8-MFMA kernels (one 16-token tile up to
 //             16 tokens: 42-49 us against 66-75 us for the chunk-pair
-//             kernel; 2-3 tiles up to 48: 65-101 us against 119-121 us for
-//             the binary16 kernel);
+//             kernel; two tiles up to 32: 74-77 us against 87-89 us for the
+//             binary16 kernel on 28672 x 8192);
 //   n <= 64:  the few-token kernel, unless the binary16-MFMA kernel has
 //             enough 128 x 128 tiles to occupy the chip (>= 160: on 28672
-//             rows the two are level, 121-123 us; with 64 tiles, on 8192
-//             rows, the binary16 kernel is three times slower);
+//             rows at 33 / 48 tokens 90.7 / 92.5 us against 97 / 101.5 us;
+//             with 64 tiles, on 8192 rows, it is three times slower);
 //   n > 64:   the binary16-MFMA kernel.
 // The environment variable MMQ_FP32_KERNEL=i8|f16|small|gemv|pair forces one
 // kernel (for comparisons and tests; "small" only where n <= 64, "pair" only
@@ -109,7 +109,7 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
     const Fp32Kernel f = forced_fp32_kernel();
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
     auto launch = n <= mmq::kGemvMaxN                         ? mmq::launch_mmq_fp32_gemv
-                  : n <= 48                                  ? mmq::launch_mmq_fp32_small
+                  : n <= 32                                  ? mmq::launch_mmq_fp32_small
                   : n <= mmq::kSmallMaxN && f16_tiles < 160  ? mmq::launch_mmq_fp32_small
                                                              : mmq::launch_mmq_fp32_f16;
     if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
