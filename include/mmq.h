@@ -55,11 +55,15 @@ enum mmq_status {
     MMQ_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
     MMQ_ERR_OVERFLOW = -4,  /* a size beyond the kernels' index range (see limits below) */
     MMQ_ERR_DEVICE = -5,    /* no HIP device, or the current device is not gfx950 */
-    MMQ_ERR_HIP = -6        /* the HIP runtime reported an error at launch */
+    MMQ_ERR_HIP = -6,       /* the HIP runtime reported an error at launch */
+    MMQ_ERR_KERNEL = -7     /* unknown kernel or format id, or a kernel outside its token range */
 };
 
 /* Size limits (MMQ_ERR_OVERFLOW beyond them): n, m <= 2^31 - 1; k <= 2^24;
- * n*k and m*k/256*144 below 2^40; for mmq_q4k_q8 also n*m*(k/32) < 2^40. */
+ * n*k and m*k/256*144 below 2^40; for mmq_q4k_q8 also n*m*(k/32) < 2^40;
+ * and every launch the call makes below 2^32 work-items (HIP's grid limit):
+ * for the quantizers n*k/8 (tiled: ceil(n/128)*128*k/8), for the matmuls
+ * 1024 per tile of 128 rows x 64 tokens, 512 per 16 rows (few tokens). */
 
 /*
  * q8_quantize_rows - per-token, per-32-element q8 quantization of activations.
@@ -116,7 +120,9 @@ int mmq_q4k_q8(const void *w, int64_t m, int64_t k, const int8_t *q, const uint3
  *   q   : int8 [n][k];  ds : uint32 [n][k/32] (as written by q8_quantize_rows).
  *   out : float [n][m] (out), token-major: out[t][o].  The summation order is
  *         the kernel's; results agree with the exact value to float32
- *         rounding of the accumulation (relative L2 error <= 1e-5).
+ *         rounding of the accumulation: relative L2 error <= 1e-5, and every
+ *         element within 1e-3 of its token row's largest |value|, for every
+ *         k accepted (no float32 sum runs over more than 256 super-blocks).
  */
 int mmq_q4k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
                        const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
@@ -137,6 +143,31 @@ int mmq_q4k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
  */
 int mmq_q4k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
                       const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
+
+/*
+ * Kernels behind the fold entry points.  Every one computes the same exact
+ * integer dots and the same fold; they differ in how the work maps onto the
+ * chip, and each meets the same accuracy bar on every shape it accepts.
+ */
+enum mmq_kernel {
+    MMQ_KERNEL_AUTO = 0,  /* the entry point's own choice, by m and n (mmq_kernel_choice) */
+    MMQ_KERNEL_DOT4 = 1,  /* vector-ALU 4-way int8 dots, weights streamed once; n <= 8 */
+    MMQ_KERNEL_FEW = 2,   /* int8 MFMA on 16-token tiles, weights streamed once; n <= 64 (q4_K) */
+    MMQ_KERNEL_F16 = 3,   /* binary16 MFMA on exact sc*q4 and q8 operands, 128-row tiles; any n */
+    MMQ_KERNEL_I8 = 4     /* int8 MFMA on 128 x 128 tiles with a three-operation fold; any n */
+};
+
+/*
+ * mmq_q4k_q8_fold - mmq_q4k_q8_fp32out (out_f16 == 0) or mmq_q4k_q8_f16out
+ * (out_f16 != 0) on a kernel the caller names, for comparisons, benchmarks
+ * and validation of every kernel on any shape.  With MMQ_KERNEL_AUTO it is
+ * exactly that entry point.  A kernel outside its token range (DOT4 above 8
+ * tokens, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
+ * HIP call; other arguments, errors and empty calls as for
+ * mmq_q4k_q8_fp32out.
+ */
+int mmq_q4k_q8_fold(const void *w, int64_t m, int64_t k, const int8_t *q, const uint32_t *ds,
+                    int64_t n, void *out, int out_f16, int kernel, hipStream_t stream);
 
 /*
  * q6_K weights: the second k-quant format, named in the r31 page's closing
@@ -187,6 +218,14 @@ int mmq_q6k_q8_fp32out(const void *w, int64_t m, int64_t k, const int8_t *q,
  */
 int mmq_q6k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
                       const uint32_t *ds, int64_t n, uint16_t *out, hipStream_t stream);
+
+/*
+ * mmq_q6k_q8_fold - mmq_q4k_q8_fold for q6_K weights: MMQ_KERNEL_AUTO,
+ * MMQ_KERNEL_DOT4 (n <= 8), MMQ_KERNEL_F16 or MMQ_KERNEL_I8 (MMQ_KERNEL_FEW
+ * returns MMQ_ERR_KERNEL).
+ */
+int mmq_q6k_q8_fold(const void *w, int64_t m, int64_t k, const int8_t *q, const uint32_t *ds,
+                    int64_t n, void *out, int out_f16, int kernel, hipStream_t stream);
 
 /*
  * q4k_repack - load-time re-layout of q4_K weights (read by the few-token
@@ -287,6 +326,24 @@ int mmq_q4kr_q8t_fp32out(const void *wr, int64_t m, int64_t k, const uint16_t *q
  */
 int mmq_q6k_q8t_fp32out(const void *w, int64_t m, int64_t k, const uint16_t *qt,
                         const uint32_t *ds, int64_t n, float *out, hipStream_t stream);
+
+/* Weight and activation formats of the fold entry points. */
+enum mmq_format {
+    MMQ_FORMAT_Q4K = 0,                /* mmq_q4k_q8_fp32out / _f16out */
+    MMQ_FORMAT_Q4K_REPACKED = 1,       /* mmq_q4kr_q8_fp32out */
+    MMQ_FORMAT_Q6K = 2,                /* mmq_q6k_q8_fp32out / _f16out */
+    MMQ_FORMAT_Q4K_TILES = 3,          /* mmq_q4k_q8t_fp32out */
+    MMQ_FORMAT_Q4K_REPACKED_TILES = 4, /* mmq_q4kr_q8t_fp32out */
+    MMQ_FORMAT_Q6K_TILES = 5           /* mmq_q6k_q8t_fp32out */
+};
+
+/*
+ * mmq_kernel_choice - the kernel (enum mmq_kernel, never MMQ_KERNEL_AUTO)
+ * that the fold entry point of `format` runs for an m x k weight and n
+ * tokens; host logic only, no HIP call.  MMQ_ERR_SHAPE for negative sizes or
+ * k not a positive multiple of 256, MMQ_ERR_KERNEL for an unknown format.
+ */
+int mmq_kernel_choice(int format, int64_t m, int64_t k, int64_t n);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *mmq_status_string(int status);

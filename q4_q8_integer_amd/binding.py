@@ -15,10 +15,17 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4q8mmq.so")
 EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
-           "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "q4k_repack",
-           "mmq_q4kr_q8_fp32out", "q8_quantize_rows_tiled", "mmq_q4k_q8t_fp32out",
+           "mmq_q4k_q8_fold", "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q6k_q8_fold",
+           "q4k_repack", "mmq_q4kr_q8_fp32out", "q8_quantize_rows_tiled", "mmq_q4k_q8t_fp32out",
            "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out", "q8_quantize_silu_mul_tiled",
-           "mmq_status_string")
+           "mmq_kernel_choice", "mmq_status_string")
+
+# enum mmq_kernel / enum mmq_format of include/mmq.h
+KERNEL_AUTO, KERNEL_DOT4, KERNEL_FEW, KERNEL_F16, KERNEL_I8 = 0, 1, 2, 3, 4
+KERNEL_NAMES = {KERNEL_DOT4: "dot4", KERNEL_FEW: "few", KERNEL_F16: "f16", KERNEL_I8: "i8"}
+(FORMAT_Q4K, FORMAT_Q4K_REPACKED, FORMAT_Q6K, FORMAT_Q4K_TILES, FORMAT_Q4K_REPACKED_TILES,
+ FORMAT_Q6K_TILES) = range(6)
+Q4K_BLOCK_BYTES, Q6K_BLOCK_BYTES, REPACK_RECORD_BYTES = 144, 210, 2368
 _MMQ_CALLS = ("mmq_q4k_q8", "mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out",
               "mmq_q6k_q8", "mmq_q6k_q8_fp32out", "mmq_q6k_q8_f16out", "mmq_q4kr_q8_fp32out",
               "mmq_q4k_q8t_fp32out", "mmq_q4kr_q8t_fp32out", "mmq_q6k_q8t_fp32out")
@@ -57,6 +64,12 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
         fn.restype = ctypes.c_int
+    for name in ("mmq_q4k_q8_fold", "mmq_q6k_q8_fold"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i64, i64, vp, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp]
+        fn.restype = ctypes.c_int
+    lib.mmq_kernel_choice.argtypes = [ctypes.c_int, i64, i64, i64]
+    lib.mmq_kernel_choice.restype = ctypes.c_int
     lib.mmq_status_string.argtypes = [ctypes.c_int]
     lib.mmq_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -86,89 +99,238 @@ def _need(t, dtype, name):
         raise TypeError("%s must be a contiguous %s tensor on a HIP device" % (name, dtype))
 
 
+# Size checks.  The C ABI sees pointers only, so a wrong m, k or n would make
+# the kernels read or write past a tensor; every wrapper below checks that
+# each tensor holds what the sizes say (and that all sit on one device)
+# before it calls the library, and raises ValueError otherwise.
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _fits(t, nbytes: int, name: str):
+    """A tensor argument (None passes through as NULL) holds >= nbytes bytes."""
+    if t is not None and isinstance(t, torch.Tensor) and _nbytes(t) < nbytes:
+        raise ValueError("%s holds %d bytes, the sizes given need %d" % (name, _nbytes(t), nbytes))
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError("all tensors must be on one device, got %s" % sorted(str(d) for d in devs))
+
+
+def _mmq_sizes(m: int, k: int, n: int):
+    if m < 0 or n < 0 or k <= 0 or k % 256:
+        raise ValueError("need m, n >= 0 and k a positive multiple of 256 (m=%d k=%d n=%d)" % (m, k, n))
+
+
+def _check_fold_args(w, wbytes, m, k, q, qbytes, ds, n, out, outbytes):
+    _mmq_sizes(m, k, n)
+    _fits(w, wbytes, "w")
+    _fits(q, qbytes, "q")
+    _fits(ds, n * (k // 32) * 4, "ds")
+    _fits(out, outbytes, "out")
+    _same_device(w, q, ds, out)
+
+
+def _w_bytes(m: int, k: int, fmt: str) -> int:
+    if fmt == "q6k":
+        return m * (k // 256) * Q6K_BLOCK_BYTES
+    if fmt == "repacked":
+        return (m + 15) // 16 * (k // 256) * REPACK_RECORD_BYTES
+    return m * (k // 256) * Q4K_BLOCK_BYTES
+
+
 # -------------------------------------------------------------- raw entries
+# Same names and arguments as the C ABI (tensors for pointers); each checks
+# that its tensors hold what the sizes say before the call.
 def q8_quantize_rows(x, n, k, q, ds):
     """Enqueue the quantizer on preallocated outputs (C ABI call, same name)."""
+    if n >= 0 and k > 0 and k % 32 == 0:
+        _fits(x, n * k * 4, "x")
+        _fits(q, n * k, "q")
+        _fits(ds, n * (k // 32) * 4, "ds")
+        _same_device(x, q, ds)
     _check("q8_quantize_rows", load_library().q8_quantize_rows(
         _ptr(x), n, k, _ptr(q), _ptr(ds), _stream()))
 
 
 def q8_quantize_rows_tiled(x, n, k, qt, ds):
     """Enqueue the quantizer with the codes as binary16 operand tiles."""
+    if n >= 0 and k > 0 and k % 256 == 0:
+        _fits(x, n * k * 4, "x")
+        _fits(qt, tiles_elems(n, k) * 2, "qt")
+        _fits(ds, n * (k // 32) * 4, "ds")
+        _same_device(x, qt, ds)
     _check("q8_quantize_rows_tiled", load_library().q8_quantize_rows_tiled(
         _ptr(x), n, k, _ptr(qt), _ptr(ds), _stream()))
 
 
 def q8_quantize_silu_mul_tiled(gate, up, n, k, qt, ds):
     """Enqueue the fused SiLU-gate quantizer with the codes as operand tiles."""
+    if n >= 0 and k > 0 and k % 256 == 0:
+        _fits(gate, n * k * 4, "gate")
+        _fits(up, n * k * 4, "up")
+        _fits(qt, tiles_elems(n, k) * 2, "qt")
+        _fits(ds, n * (k // 32) * 4, "ds")
+        _same_device(gate, up, qt, ds)
     _check("q8_quantize_silu_mul_tiled", load_library().q8_quantize_silu_mul_tiled(
         _ptr(gate), _ptr(up), n, k, _ptr(qt), _ptr(ds), _stream()))
 
 
 def q8_quantize_silu_mul(gate, up, n, k, q, ds):
     """Enqueue the fused SiLU-gate quantizer on preallocated outputs."""
+    if n >= 0 and k > 0 and k % 32 == 0:
+        _fits(gate, n * k * 4, "gate")
+        _fits(up, n * k * 4, "up")
+        _fits(q, n * k, "q")
+        _fits(ds, n * (k // 32) * 4, "ds")
+        _same_device(gate, up, q, ds)
     _check("q8_quantize_silu_mul", load_library().q8_quantize_silu_mul(
         _ptr(gate), _ptr(up), n, k, _ptr(q), _ptr(ds), _stream()))
 
 
+def _sized(m, k, n):
+    return m >= 0 and n >= 0 and k > 0 and k % 256 == 0
+
+
 def mmq_q4k_q8(w, m, k, q, ds, n, dots):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q4k"), m, k, q, n * k, None, n, dots, n * m * (k // 32) * 4)
+        _fits(ds, n * (k // 32) * 4, "ds")
     _check("mmq_q4k_q8", load_library().mmq_q4k_q8(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
 
 
 def mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q4k"), m, k, q, n * k, ds, n, out, n * m * 4)
     _check("mmq_q4k_q8_fp32out", load_library().mmq_q4k_q8_fp32out(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q4k_q8_f16out(w, m, k, q, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q4k"), m, k, q, n * k, ds, n, out, n * m * 2)
     _check("mmq_q4k_q8_f16out", load_library().mmq_q4k_q8_f16out(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
+def mmq_q4k_q8_fold(w, m, k, q, ds, n, out, out_f16, kernel):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q4k"), m, k, q, n * k, ds, n, out, n * m * (2 if out_f16 else 4))
+    _check("mmq_q4k_q8_fold", load_library().mmq_q4k_q8_fold(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), int(out_f16), int(kernel), _stream()))
+
+
 def q4k_repack(w, m, k, wr):
+    if m >= 0 and k > 0 and k % 256 == 0:
+        _fits(w, _w_bytes(m, k, "q4k"), "w")
+        _fits(wr, _w_bytes(m, k, "repacked"), "wr")
+        _same_device(w, wr)
     _check("q4k_repack", load_library().q4k_repack(_ptr(w), m, k, _ptr(wr), _stream()))
 
 
 def mmq_q4kr_q8_fp32out(wr, m, k, q, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(wr, _w_bytes(m, k, "repacked"), m, k, q, n * k, ds, n, out, n * m * 4)
     _check("mmq_q4kr_q8_fp32out", load_library().mmq_q4kr_q8_fp32out(
         _ptr(wr), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q4k_q8t_fp32out(w, m, k, qt, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q4k"), m, k, qt, tiles_elems(n, k) * 2, ds, n, out, n * m * 4)
     _check("mmq_q4k_q8t_fp32out", load_library().mmq_q4k_q8t_fp32out(
         _ptr(w), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q4kr_q8t_fp32out(wr, m, k, qt, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(wr, _w_bytes(m, k, "repacked"), m, k, qt, tiles_elems(n, k) * 2, ds, n, out, n * m * 4)
     _check("mmq_q4kr_q8t_fp32out", load_library().mmq_q4kr_q8t_fp32out(
         _ptr(wr), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q6k_q8t_fp32out(w, m, k, qt, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q6k"), m, k, qt, tiles_elems(n, k) * 2, ds, n, out, n * m * 4)
     _check("mmq_q6k_q8t_fp32out", load_library().mmq_q6k_q8t_fp32out(
         _ptr(w), m, k, _ptr(qt), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q6k_q8(w, m, k, q, ds, n, dots):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q6k"), m, k, q, n * k, None, n, dots, n * m * (k // 16) * 4)
+        _fits(ds, n * (k // 32) * 4, "ds")
     _check("mmq_q6k_q8", load_library().mmq_q6k_q8(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(dots), _stream()))
 
 
 def mmq_q6k_q8_fp32out(w, m, k, q, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q6k"), m, k, q, n * k, ds, n, out, n * m * 4)
     _check("mmq_q6k_q8_fp32out", load_library().mmq_q6k_q8_fp32out(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
 def mmq_q6k_q8_f16out(w, m, k, q, ds, n, out):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q6k"), m, k, q, n * k, ds, n, out, n * m * 2)
     _check("mmq_q6k_q8_f16out", load_library().mmq_q6k_q8_f16out(
         _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), _stream()))
 
 
+def mmq_q6k_q8_fold(w, m, k, q, ds, n, out, out_f16, kernel):
+    if _sized(m, k, n):
+        _check_fold_args(w, _w_bytes(m, k, "q6k"), m, k, q, n * k, ds, n, out, n * m * (2 if out_f16 else 4))
+    _check("mmq_q6k_q8_fold", load_library().mmq_q6k_q8_fold(
+        _ptr(w), m, k, _ptr(q), _ptr(ds), n, _ptr(out), int(out_f16), int(kernel), _stream()))
+
+
+def mmq_kernel_choice(fmt: int, m: int, k: int, n: int) -> int:
+    """The kernel id (KERNEL_*) a fold entry point of format fmt runs for an
+    m x k weight and n tokens (host logic only; raises on a bad argument)."""
+    r = load_library().mmq_kernel_choice(int(fmt), m, k, n)
+    _check("mmq_kernel_choice", r if r < 0 else 0)
+    return r
+
+
 # --------------------------------------------------------- tensor helpers
+def _tokens(q, k, name="q"):
+    """Token count of a q8 code tensor [n, k] (raises unless its rows are k long)."""
+    if q.dim() != 2 or q.shape[1] != k:
+        raise ValueError("%s must be [n, %d], got %s" % (name, k, tuple(q.shape)))
+    return q.shape[0]
+
+
+def _scale_words(ds, n, k):
+    if tuple(ds.shape) != (n, k // 32):
+        raise ValueError("ds must be [%d, %d], got %s" % (n, k // 32, tuple(ds.shape)))
+
+
+def _out_tensor(out, n, m, dtype, dev):
+    if out is None:
+        return torch.empty((n, m), dtype=dtype, device=dev)
+    _need(out, dtype, "out")
+    if tuple(out.shape) != (n, m):
+        raise ValueError("out must be [%d, %d], got %s" % (n, m, tuple(out.shape)))
+    return out
+
+
+def _weights(w, m, k, fmt, name="w"):
+    _need(w, torch.uint8, name)
+    _mmq_sizes(m, k, 0)
+    if w.numel() != _w_bytes(m, k, fmt):
+        raise ValueError("%s must hold %d bytes for a %d x %d %s matrix, got %d"
+                         % (name, _w_bytes(m, k, fmt), m, k, fmt, w.numel()))
+
+
 def quantize(x: torch.Tensor):
     """x float32 [n, k] -> (q int8 [n, k], ds int32 [n, k/32] holding the uint32 words)."""
     _need(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [n, k]")
     n, k = x.shape
     q = torch.empty((n, k), dtype=torch.int8, device=x.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
@@ -185,6 +347,8 @@ def quantize_tiled(x: torch.Tensor):
     """x float32 [n, k] -> (qt int16 [tiles_elems(n, k)] holding the binary16
     operand tiles, ds int32 [n, k/32])."""
     _need(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [n, k]")
     n, k = x.shape
     qt = torch.empty(tiles_elems(n, k), dtype=torch.int16, device=x.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=x.device)
@@ -196,8 +360,8 @@ def quantize_silu_mul_tiled(gate: torch.Tensor, up: torch.Tensor):
     """Operand tiles of q8(SiLU(gate) * up): (qt int16 [tiles_elems(n, k)], ds int32 [n, k/32])."""
     _need(gate, torch.float32, "gate")
     _need(up, torch.float32, "up")
-    if gate.shape != up.shape:
-        raise ValueError("gate and up must have the same shape")
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must have the same shape [n, k]")
     n, k = gate.shape
     qt = torch.empty(tiles_elems(n, k), dtype=torch.int16, device=gate.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=gate.device)
@@ -209,8 +373,8 @@ def quantize_silu_mul(gate: torch.Tensor, up: torch.Tensor):
     """q8 of SiLU(gate) * up: (q int8 [n, k], ds int32 [n, k/32])."""
     _need(gate, torch.float32, "gate")
     _need(up, torch.float32, "up")
-    if gate.shape != up.shape:
-        raise ValueError("gate and up must have the same shape")
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must have the same shape [n, k]")
     n, k = gate.shape
     q = torch.empty((n, k), dtype=torch.int8, device=gate.device)
     ds = torch.empty((n, k // 32 if k % 32 == 0 else 0), dtype=torch.int32, device=gate.device)
@@ -220,47 +384,47 @@ def quantize_silu_mul(gate: torch.Tensor, up: torch.Tensor):
 
 def blockdots(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds=None):
     """Exact int32 block dots [n, m, k/32]."""
-    _need(w, torch.uint8, "w")
+    _weights(w, m, k, "q4k")
     _need(q, torch.int8, "q")
-    n = q.shape[0]
+    n = _tokens(q, k)
     dots = torch.empty((n, m, k // 32), dtype=torch.int32, device=q.device)
     mmq_q4k_q8(w, m, k, q, ds, n, dots)
     return dots
 
 
-def fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
-    """Two-term-fold output float32 [n, m]."""
-    _need(w, torch.uint8, "w")
+def _fold(w, m, k, q, ds, out, fmt, out_dtype, call):
+    _weights(w, m, k, fmt)
     _need(q, torch.int8, "q")
     _need(ds, torch.int32, "ds")
-    n = q.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
-    else:
-        _need(out, torch.float32, "out")
-    mmq_q4k_q8_fp32out(w, m, k, q, ds, n, out)
+    n = _tokens(q, k)
+    _scale_words(ds, n, k)
+    out = _out_tensor(out, n, m, out_dtype, q.device)
+    call(w, m, k, q, ds, n, out)
     return out
+
+
+def fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
+    """Two-term-fold output float32 [n, m]."""
+    return _fold(w, m, k, q, ds, out, "q4k", torch.float32, mmq_q4k_q8_fp32out)
 
 
 def fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
     """Two-term-fold output as binary16 [n, m] (the float32 result, rounded to nearest-even)."""
-    _need(w, torch.uint8, "w")
-    _need(q, torch.int8, "q")
-    _need(ds, torch.int32, "ds")
-    n = q.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float16, device=q.device)
-    else:
-        _need(out, torch.float16, "out")
-    mmq_q4k_q8_f16out(w, m, k, q, ds, n, out)
-    return out
+    return _fold(w, m, k, q, ds, out, "q4k", torch.float16, mmq_q4k_q8_f16out)
+
+
+def fold_kernel(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, kernel: int,
+                f16: bool = False, out=None):
+    """The q4_K fold on a named kernel (KERNEL_*): float32 or binary16 [n, m]."""
+    return _fold(w, m, k, q, ds, out, "q4k", torch.float16 if f16 else torch.float32,
+                 lambda *a: mmq_q4k_q8_fold(*a, int(f16), kernel))
 
 
 def q6k_dots(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds=None):
     """Exact int32 q6_K group dots [n, m, k/16]."""
-    _need(w, torch.uint8, "w")
+    _weights(w, m, k, "q6k")
     _need(q, torch.int8, "q")
-    n = q.shape[0]
+    n = _tokens(q, k)
     dots = torch.empty((n, m, k // 16), dtype=torch.int32, device=q.device)
     mmq_q6k_q8(w, m, k, q, ds, n, dots)
     return dots
@@ -268,29 +432,34 @@ def q6k_dots(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds=None):
 
 def q6k_fp32(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
     """q6_K output float32 [n, m]."""
-    _need(w, torch.uint8, "w")
-    _need(q, torch.int8, "q")
-    _need(ds, torch.int32, "ds")
-    n = q.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
-    else:
-        _need(out, torch.float32, "out")
-    mmq_q6k_q8_fp32out(w, m, k, q, ds, n, out)
-    return out
+    return _fold(w, m, k, q, ds, out, "q6k", torch.float32, mmq_q6k_q8_fp32out)
 
 
 def q6k_fp16(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
     """q6_K output as binary16 [n, m] (the float32 result, rounded to nearest-even)."""
-    _need(w, torch.uint8, "w")
-    _need(q, torch.int8, "q")
+    return _fold(w, m, k, q, ds, out, "q6k", torch.float16, mmq_q6k_q8_f16out)
+
+
+def q6k_fold_kernel(w: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, kernel: int,
+                    f16: bool = False, out=None):
+    """The q6_K fold on a named kernel (KERNEL_*): float32 or binary16 [n, m]."""
+    return _fold(w, m, k, q, ds, out, "q6k", torch.float16 if f16 else torch.float32,
+                 lambda *a: mmq_q6k_q8_fold(*a, int(f16), kernel))
+
+
+def _tiles_fold(w, m, k, qt, ds, out, fmt, call):
+    _weights(w, m, k, fmt)
+    _need(qt, torch.int16, "qt")
     _need(ds, torch.int32, "ds")
-    n = q.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float16, device=q.device)
-    else:
-        _need(out, torch.float16, "out")
-    mmq_q6k_q8_f16out(w, m, k, q, ds, n, out)
+    if ds.dim() != 2:
+        raise ValueError("ds must be [n, k/32]")
+    n = ds.shape[0]
+    _scale_words(ds, n, k)
+    if qt.numel() != tiles_elems(n, k):
+        raise ValueError("qt must hold tiles_elems(%d, %d) = %d values, got %d"
+                         % (n, k, tiles_elems(n, k), qt.numel()))
+    out = _out_tensor(out, n, m, torch.float32, ds.device)
+    call(w, m, k, qt, ds, n, out)
     return out
 
 
@@ -298,40 +467,23 @@ def fp32_tiles(w: torch.Tensor, m: int, k: int, qt: torch.Tensor, ds: torch.Tens
                repacked: bool = False):
     """The fold on q8 operand tiles (from quantize_tiled): float32 [n, m]; w is
     q4_K rows, or q4k_repack records with repacked=True."""
-    _need(w, torch.uint8, "w")
-    _need(qt, torch.int16, "qt")
-    _need(ds, torch.int32, "ds")
-    n = ds.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float32, device=ds.device)
-    else:
-        _need(out, torch.float32, "out")
-    (mmq_q4kr_q8t_fp32out if repacked else mmq_q4k_q8t_fp32out)(w, m, k, qt, ds, n, out)
-    return out
+    return _tiles_fold(w, m, k, qt, ds, out, "repacked" if repacked else "q4k",
+                       mmq_q4kr_q8t_fp32out if repacked else mmq_q4k_q8t_fp32out)
 
 
 def q6k_fp32_tiles(w: torch.Tensor, m: int, k: int, qt: torch.Tensor, ds: torch.Tensor, out=None):
     """The q6_K fold on q8 operand tiles (from quantize_tiled): float32 [n, m]."""
-    _need(w, torch.uint8, "w")
-    _need(qt, torch.int16, "qt")
-    _need(ds, torch.int32, "ds")
-    n = ds.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float32, device=ds.device)
-    else:
-        _need(out, torch.float32, "out")
-    mmq_q6k_q8t_fp32out(w, m, k, qt, ds, n, out)
-    return out
+    return _tiles_fold(w, m, k, qt, ds, out, "q6k", mmq_q6k_q8t_fp32out)
 
 
 def repack_bytes(m: int, k: int) -> int:
     """Size of q4k_repack's output for an m x k matrix."""
-    return (m + 15) // 16 * (k // 256) * 2368
+    return _w_bytes(m, k, "repacked")
 
 
 def repack(w: torch.Tensor, m: int, k: int):
     """Load-time repack of q4_K weights: uint8 tensor of repack_bytes(m, k)."""
-    _need(w, torch.uint8, "w")
+    _weights(w, m, k, "q4k")
     wr = torch.empty(repack_bytes(m, k), dtype=torch.uint8, device=w.device)
     q4k_repack(w, m, k, wr)
     return wr
@@ -339,13 +491,4 @@ def repack(w: torch.Tensor, m: int, k: int):
 
 def fp32_repacked(wr: torch.Tensor, m: int, k: int, q: torch.Tensor, ds: torch.Tensor, out=None):
     """mmq_q4k_q8_fp32out on repacked weights: float32 [n, m]."""
-    _need(wr, torch.uint8, "wr")
-    _need(q, torch.int8, "q")
-    _need(ds, torch.int32, "ds")
-    n = q.shape[0]
-    if out is None:
-        out = torch.empty((n, m), dtype=torch.float32, device=q.device)
-    else:
-        _need(out, torch.float32, "out")
-    mmq_q4kr_q8_fp32out(wr, m, k, q, ds, n, out)
-    return out
+    return _fold(wr, m, k, q, ds, out, "repacked", torch.float32, mmq_q4kr_q8_fp32out)

@@ -6,11 +6,6 @@ the objects are linked into one shared library that exports the C ABI of
 (``-packed-fp32-ops``); fast-math is never used, so fp32 division stays
 correctly rounded.
 
-Per-source extra flags: the chunk-pair kernel keeps its matrix-core results in
-ordinary VGPRs (``-amdgpu-mfma-vgpr-form``).  Every one of its MFMA results
-feeds vector-ALU math, which would otherwise copy it out of the accumulation
-registers one instruction per value.  (The option is not applied everywhere:
-this compiler crashes on it for the int8-MFMA GEMM source.)
 """
 from __future__ import annotations
 
@@ -29,7 +24,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
                "-Wall", "-Wno-unused-result",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCE_FLAGS = {"mmq_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {}   # per-source extra flags (none at present)
 
 
 def sources():

@@ -101,13 +101,6 @@ hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const 
                                          const uint32_t* ds, int n, void* out, bool half_out,
                                          hipStream_t stream);
 
-// Two-term fold, out[t][o], for n <= kPairMaxN tokens: one int8 MFMA per
-// chunk pair, 8 tokens x 16 rows, weights streamed once.
-hipError_t launch_mmq_fp32_pair(const uint8_t* w, int m, int k, const int8_t* q,
-                                const uint32_t* ds, int n, void* out, bool half_out,
-                                hipStream_t stream);
-constexpr int kPairMaxN = 16;
-
 // Largest token count the few-token kernel takes.
 constexpr int kSmallMaxN = 64;
 

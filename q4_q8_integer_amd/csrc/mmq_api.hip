@@ -4,7 +4,6 @@
 // the current device checked (once per device: gfx950 or MMQ_ERR_DEVICE) and
 // the kernel enqueued on the caller's stream.  Nothing here allocates.
 #include <atomic>
-#include <cstdlib>
 #include <cstring>
 
 #include "../../include/mmq.h"
@@ -58,35 +57,64 @@ int check_mmq(const void* w, int64_t m, int64_t k, const int8_t* q, int64_t n, c
     return MMQ_OK;
 }
 
-// Kernel behind the fold entry points, by token count (measured on the
-// 28672 x 8192 and 8192 x 28672 matrices across n = 9..64):
+using FoldLaunch = hipError_t (*)(const uint8_t*, int, int, const int8_t*, const uint32_t*, int, void*, bool,
+                                  hipStream_t);
+
+// HIP takes at most 2^32 - 1 work-items per grid dimension.
+bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block < (1LL << 32); }
+
+// Kernel behind the q4_K fold entry points for MMQ_KERNEL_AUTO, by token
+// count (measured on the 28672 x 8192 and 8192 x 28672 matrices across
+// n = 9..64):
 //   n <= 8:   the vector-ALU dot4 kernel;
 //   n <= 32:  the few-token int8-MFMA kernels (one 16-token tile up to
-//             16 tokens: 42-49 us against 66-75 us for the chunk-pair
-//             kernel; two tiles up to 32: 74-77 us against 87-89 us for the
-//             binary16 kernel on 28672 x 8192);
+//             16 tokens, two tiles up to 32: 74-77 us against 87-89 us for
+//             the binary16 kernel on 28672 x 8192);
 //   n <= 64:  the few-token kernel, unless the binary16-MFMA kernel has
 //             enough 128 x 128 tiles to occupy the chip (>= 160: on 28672
 //             rows at 33 / 48 tokens 90.7 / 92.5 us against 97 / 101.5 us;
 //             with 64 tiles, on 8192 rows, it is three times slower);
 //   n > 64:   the binary16-MFMA kernel.
-// The environment variable MMQ_FP32_KERNEL=i8|f16|small|gemv|pair forces one
-// kernel (for comparisons and tests; "small" only where n <= 64, "pair" only
-// where n <= 16, "gemv" only where n <= 8).  All meet the same accuracy bar.
-enum class Fp32Kernel { Auto, I8, F16, Small, Gemv, Pair };
+int q4k_auto_kernel(int64_t m, int64_t n) {
+    const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    return n <= mmq::kGemvMaxN                        ? MMQ_KERNEL_DOT4
+           : n <= 32                                  ? MMQ_KERNEL_FEW
+           : n <= mmq::kSmallMaxN && f16_tiles < 160  ? MMQ_KERNEL_FEW
+                                                      : MMQ_KERNEL_F16;
+}
 
-Fp32Kernel forced_fp32_kernel() {
-    static const Fp32Kernel k = [] {
-        const char* v = std::getenv("MMQ_FP32_KERNEL");
-        if (!v) return Fp32Kernel::Auto;
-        if (std::strcmp(v, "i8") == 0) return Fp32Kernel::I8;
-        if (std::strcmp(v, "f16") == 0) return Fp32Kernel::F16;
-        if (std::strcmp(v, "small") == 0) return Fp32Kernel::Small;
-        if (std::strcmp(v, "gemv") == 0) return Fp32Kernel::Gemv;
-        if (std::strcmp(v, "pair") == 0) return Fp32Kernel::Pair;
-        return Fp32Kernel::Auto;
-    }();
-    return k;
+// The repacked-weight entry: above 16 tokens the binary16-MFMA kernel on the
+// records, where it has tiles enough for the CUs (>= 160 of 128 x 128) or the
+// slices would be many (> 40 tokens); otherwise the dot4 kernel, in slices of
+// 8 tokens.  Measured per call: 28672 x 8192 (224 tiles) at 9 / 16 / 24
+// tokens 60 / 76 / 121 us in slices against 75 us; 8192 x 28672 (64 tiles)
+// at 33 / 48 tokens 197 / 273 us in slices against 221 us.
+int q4kr_auto_kernel(int64_t m, int64_t n) {
+    const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    return n > 16 && (f16_tiles >= 160 || n > 40) ? MMQ_KERNEL_F16 : MMQ_KERNEL_DOT4;
+}
+
+// The launcher of a q4_K fold kernel choice, and whether its grid fits.
+int q4k_fold_launcher(int kernel, int64_t m, int64_t n, FoldLaunch* f) {
+    if (kernel == MMQ_KERNEL_AUTO) kernel = q4k_auto_kernel(m, n);
+    switch (kernel) {
+        case MMQ_KERNEL_DOT4:
+            if (n > mmq::kGemvMaxN) return MMQ_ERR_KERNEL;
+            *f = mmq::launch_mmq_fp32_gemv;
+            return threads_ok((m + 15) / 16, 256) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_FEW:
+            if (n > mmq::kSmallMaxN) return MMQ_ERR_KERNEL;
+            *f = mmq::launch_mmq_fp32_small;
+            return threads_ok((m + 15) / 16, 512) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_F16:
+            *f = mmq::launch_mmq_fp32_f16;
+            return threads_ok((m + 127) / 128 * ((n + 63) / 64), 1024) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_I8:
+            *f = mmq::launch_mmq_fp32;
+            return threads_ok((m + 127) / 128 * ((n + 127) / 128), 256) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        default:
+            return MMQ_ERR_KERNEL;
+    }
 }
 
 int hip_status(hipError_t e) {
@@ -95,30 +123,22 @@ int hip_status(hipError_t e) {
     return MMQ_ERR_HIP;
 }
 
-// The two fold entry points: same checks, same kernels, float32 or binary16
+// The q4_K fold entry points: same checks, same kernels, float32 or binary16
 // stores of the same float32 result.
 int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds, int64_t n,
-               void* out, bool half_out, hipStream_t stream) {
+               void* out, bool half_out, int kernel, hipStream_t stream) {
     bool empty = false;
     int rc = check_mmq(w, m, k, q, n, out, &empty);
     if (rc != MMQ_OK || empty) return rc;
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    FoldLaunch launch = nullptr;
+    rc = q4k_fold_launcher(kernel, m, n, &launch);
+    if (rc != MMQ_OK) return rc;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    const Fp32Kernel f = forced_fp32_kernel();
-    const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    auto launch = n <= mmq::kGemvMaxN                         ? mmq::launch_mmq_fp32_gemv
-                  : n <= 32                                  ? mmq::launch_mmq_fp32_small
-                  : n <= mmq::kSmallMaxN && f16_tiles < 160  ? mmq::launch_mmq_fp32_small
-                                                             : mmq::launch_mmq_fp32_f16;
-    if (f == Fp32Kernel::I8) launch = mmq::launch_mmq_fp32;
-    if (f == Fp32Kernel::F16) launch = mmq::launch_mmq_fp32_f16;
-    if (f == Fp32Kernel::Small && n <= mmq::kSmallMaxN) launch = mmq::launch_mmq_fp32_small;
-    if (f == Fp32Kernel::Gemv && n <= mmq::kGemvMaxN) launch = mmq::launch_mmq_fp32_gemv;
-    if (f == Fp32Kernel::Pair && n <= mmq::kPairMaxN) launch = mmq::launch_mmq_fp32_pair;
-    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
-                             half_out, stream));
+    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out, half_out,
+                             stream));
 }
 
 // The fold entry points on q8 operand tiles: always the binary16-MFMA kernel
@@ -131,6 +151,7 @@ int tiles_fold_entry(const void* w, bool repacked, int64_t m, int64_t k, const u
     if (n > kMaxDim - 127 || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
     if (repacked && (m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems)
         return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((m + 127) / 128 * ((n + 63) / 64), 1024)) return MMQ_ERR_OVERFLOW;
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
@@ -139,39 +160,42 @@ int tiles_fold_entry(const void* w, bool repacked, int64_t m, int64_t k, const u
                                                      (int)k, qt, ds, (int)n, out, stream));
 }
 
-// q6_K kernel behind the fold entry points: the vector-ALU dot4 kernel for
-// n <= 8, the binary16-MFMA kernel above.  MMQ_Q6K_KERNEL=i8|f16|gemv forces
-// one (for comparisons and tests; "gemv" only where n <= 8).
-enum class Q6kKernel { Auto, I8, F16, Gemv };
+// Kernel behind the q6_K fold entry points for MMQ_KERNEL_AUTO: the
+// vector-ALU dot4 kernel for n <= 8, the binary16-MFMA kernel above.
+int q6k_auto_kernel(int64_t n) { return n <= mmq::kQ6kGemvMaxN ? MMQ_KERNEL_DOT4 : MMQ_KERNEL_F16; }
 
-Q6kKernel forced_q6k_kernel() {
-    static const Q6kKernel k = [] {
-        const char* v = std::getenv("MMQ_Q6K_KERNEL");
-        if (!v) return Q6kKernel::Auto;
-        if (std::strcmp(v, "i8") == 0) return Q6kKernel::I8;
-        if (std::strcmp(v, "f16") == 0) return Q6kKernel::F16;
-        if (std::strcmp(v, "gemv") == 0) return Q6kKernel::Gemv;
-        return Q6kKernel::Auto;
-    }();
-    return k;
+int q6k_fold_launcher(int kernel, int64_t m, int64_t n, FoldLaunch* f) {
+    if (kernel == MMQ_KERNEL_AUTO) kernel = q6k_auto_kernel(n);
+    switch (kernel) {
+        case MMQ_KERNEL_DOT4:
+            if (n > mmq::kQ6kGemvMaxN) return MMQ_ERR_KERNEL;
+            *f = mmq::launch_q6k_gemv;
+            return threads_ok((m + 15) / 16, 256) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_F16:
+            *f = mmq::launch_q6k_f16;
+            return threads_ok((m + 127) / 128 * ((n + 127) / 128), 1024) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_I8:
+            *f = mmq::launch_q6k_i8;
+            return threads_ok((m + 127) / 128 * ((n + 127) / 128), 256) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        default:
+            return MMQ_ERR_KERNEL;
+    }
 }
 
 int q6k_fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
-                   int64_t n, void* out, bool half_out, hipStream_t stream) {
+                   int64_t n, void* out, bool half_out, int kernel, hipStream_t stream) {
     bool empty = false;
     int rc = check_mmq(w, m, k, q, n, out, &empty, mmq::kQ6kBlockBytes);
     if (rc != MMQ_OK || empty) return rc;
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    FoldLaunch launch = nullptr;
+    rc = q6k_fold_launcher(kernel, m, n, &launch);
+    if (rc != MMQ_OK) return rc;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    const Q6kKernel f = forced_q6k_kernel();
-    auto launch = n <= mmq::kQ6kGemvMaxN ? mmq::launch_q6k_gemv : mmq::launch_q6k_f16;
-    if (f == Q6kKernel::I8) launch = mmq::launch_q6k_i8;
-    if (f == Q6kKernel::F16) launch = mmq::launch_q6k_f16;
-    if (f == Q6kKernel::Gemv && n <= mmq::kQ6kGemvMaxN) launch = mmq::launch_q6k_gemv;
-    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out,
-                             half_out, stream));
+    return hip_status(launch(static_cast<const uint8_t*>(w), (int)m, (int)k, q, ds, (int)n, out, half_out,
+                             stream));
 }
 
 }  // namespace
@@ -182,6 +206,7 @@ int q8_quantize_rows(const float* x, int64_t n, int64_t k, int8_t* q, uint32_t* 
                      hipStream_t stream) {
     if (n < 0 || k <= 0 || (k & 31) != 0) return MMQ_ERR_SHAPE;
     if (n > kMaxDim || k > kMaxK || n * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok(n * (k / 32) * 4, 1)) return MMQ_ERR_OVERFLOW;   // 4 lanes per 32-block
     if (n == 0) return MMQ_OK;
     if (!x || !q || !ds) return MMQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(q) || !aligned16(ds)) return MMQ_ERR_ALIGN;
@@ -194,6 +219,7 @@ int q8_quantize_rows_tiled(const float* x, int64_t n, int64_t k, uint16_t* qt, u
                            hipStream_t stream) {
     if (n < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
     if (n > kMaxDim - 127 || k > kMaxK || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((n + 127) / 128 * 128 * (k / 32) * 4, 1)) return MMQ_ERR_OVERFLOW;   // 4 lanes per 32-block
     if (n == 0) return MMQ_OK;
     if (!x || !qt || !ds) return MMQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(qt) || !aligned16(ds)) return MMQ_ERR_ALIGN;
@@ -206,6 +232,7 @@ int q8_quantize_silu_mul(const float* gate, const float* up, int64_t n, int64_t 
                          uint32_t* ds, hipStream_t stream) {
     if (n < 0 || k <= 0 || (k & 31) != 0) return MMQ_ERR_SHAPE;
     if (n > kMaxDim || k > kMaxK || n * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok(n * (k / 32) * 4, 1)) return MMQ_ERR_OVERFLOW;
     if (n == 0) return MMQ_OK;
     if (!gate || !up || !q || !ds) return MMQ_ERR_NULL;
     if (!aligned16(gate) || !aligned16(up) || !aligned16(q) || !aligned16(ds)) return MMQ_ERR_ALIGN;
@@ -218,6 +245,7 @@ int q8_quantize_silu_mul_tiled(const float* gate, const float* up, int64_t n, in
                                uint32_t* ds, hipStream_t stream) {
     if (n < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
     if (n > kMaxDim - 127 || k > kMaxK || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((n + 127) / 128 * 128 * (k / 32) * 4, 1)) return MMQ_ERR_OVERFLOW;   // 4 lanes per 32-block
     if (n == 0) return MMQ_OK;
     if (!gate || !up || !qt || !ds) return MMQ_ERR_NULL;
     if (!aligned16(gate) || !aligned16(up) || !aligned16(qt) || !aligned16(ds)) return MMQ_ERR_ALIGN;
@@ -233,6 +261,7 @@ int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
     int rc = check_mmq(w, m, k, q, n, dots, &empty);
     if (rc != MMQ_OK || empty) return rc;
     if (n * m >= kMaxElems / (k / 32)) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((m + 127) / 128 * ((n + 127) / 128), 256)) return MMQ_ERR_OVERFLOW;
     if (ds && !aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
@@ -242,12 +271,17 @@ int mmq_q4k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
 
 int mmq_q4k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
-    return fold_entry(w, m, k, q, ds, n, out, false, stream);
+    return fold_entry(w, m, k, q, ds, n, out, false, MMQ_KERNEL_AUTO, stream);
 }
 
 int mmq_q4k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
                       const uint32_t* ds, int64_t n, uint16_t* out, hipStream_t stream) {
-    return fold_entry(w, m, k, q, ds, n, out, true, stream);
+    return fold_entry(w, m, k, q, ds, n, out, true, MMQ_KERNEL_AUTO, stream);
+}
+
+int mmq_q4k_q8_fold(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds, int64_t n,
+                    void* out, int out_f16, int kernel, hipStream_t stream) {
+    return fold_entry(w, m, k, q, ds, n, out, out_f16 != 0, kernel, stream);
 }
 
 int mmq_q6k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds,
@@ -257,6 +291,7 @@ int mmq_q6k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
     int rc = check_mmq(w, m, k, q, n, dots, &empty, mmq::kQ6kBlockBytes);
     if (rc != MMQ_OK || empty) return rc;
     if (n * m >= kMaxElems / (k / 16)) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((m + 127) / 128 * ((n + 127) / 128), 256)) return MMQ_ERR_OVERFLOW;
     if (ds && !aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
@@ -266,12 +301,30 @@ int mmq_q6k_q8(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
 
 int mmq_q6k_q8_fp32out(const void* w, int64_t m, int64_t k, const int8_t* q,
                        const uint32_t* ds, int64_t n, float* out, hipStream_t stream) {
-    return q6k_fold_entry(w, m, k, q, ds, n, out, false, stream);
+    return q6k_fold_entry(w, m, k, q, ds, n, out, false, MMQ_KERNEL_AUTO, stream);
 }
 
 int mmq_q6k_q8_f16out(const void* w, int64_t m, int64_t k, const int8_t* q,
                       const uint32_t* ds, int64_t n, uint16_t* out, hipStream_t stream) {
-    return q6k_fold_entry(w, m, k, q, ds, n, out, true, stream);
+    return q6k_fold_entry(w, m, k, q, ds, n, out, true, MMQ_KERNEL_AUTO, stream);
+}
+
+int mmq_q6k_q8_fold(const void* w, int64_t m, int64_t k, const int8_t* q, const uint32_t* ds, int64_t n,
+                    void* out, int out_f16, int kernel, hipStream_t stream) {
+    return q6k_fold_entry(w, m, k, q, ds, n, out, out_f16 != 0, kernel, stream);
+}
+
+int mmq_kernel_choice(int format, int64_t m, int64_t k, int64_t n) {
+    if (n < 0 || m < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
+    switch (format) {
+        case MMQ_FORMAT_Q4K: return q4k_auto_kernel(m, n);
+        case MMQ_FORMAT_Q4K_REPACKED: return q4kr_auto_kernel(m, n);
+        case MMQ_FORMAT_Q6K: return q6k_auto_kernel(n);
+        case MMQ_FORMAT_Q4K_TILES:
+        case MMQ_FORMAT_Q4K_REPACKED_TILES:
+        case MMQ_FORMAT_Q6K_TILES: return MMQ_KERNEL_F16;
+        default: return MMQ_ERR_KERNEL;
+    }
 }
 
 int q4k_repack(const void* w, int64_t m, int64_t k, void* wr, hipStream_t stream) {
@@ -279,6 +332,7 @@ int q4k_repack(const void* w, int64_t m, int64_t k, void* wr, hipStream_t stream
     if (m > kMaxDim || k > kMaxK) return MMQ_ERR_OVERFLOW;
     if (m * (k / 256) * 144 >= kMaxElems || (m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems)
         return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((m + 15) / 16 * (k / 256), 64)) return MMQ_ERR_OVERFLOW;   // 64 lanes per record
     if (m == 0) return MMQ_OK;
     if (!w || !wr) return MMQ_ERR_NULL;
     if (!aligned16(w) || !aligned16(wr)) return MMQ_ERR_ALIGN;
@@ -296,15 +350,12 @@ int mmq_q4kr_q8_fp32out(const void* wr, int64_t m, int64_t k, const int8_t* q,
     if ((m + 15) / 16 * (k / 256) * mmq::kRepackRecordBytes >= kMaxElems) return MMQ_ERR_OVERFLOW;
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
+    const bool f16 = q4kr_auto_kernel(m, n) == MMQ_KERNEL_F16;
+    if (f16 ? !threads_ok((m + 127) / 128 * ((n + 63) / 64), 1024) : !threads_ok((m + 15) / 16, 256))
+        return MMQ_ERR_OVERFLOW;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
-    // Above 16 tokens the binary16-MFMA kernel on the records, where it has
-    // tiles enough for the CUs (>= 160 of 128 x 128) or the slices would be
-    // many (> 40 tokens).  Measured per call: 28672 x 8192 (224 tiles) at 9 /
-    // 16 / 24 tokens 60 / 76 / 121 us in slices against 75 us; 8192 x 28672
-    // (64 tiles) at 33 / 48 tokens 197 / 273 us in slices against 221 us.
-    const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    if (n > 16 && (f16_tiles >= 160 || n > 40))
+    if (f16)
         return hip_status(mmq::launch_mmq_fp32_f16_repacked(static_cast<const uint8_t*>(wr), (int)m, (int)k,
                                                             q, ds, (int)n, out, stream));
     // Up to 8 tokens per launch; more tokens run as slices of 8 (each reads
@@ -337,6 +388,7 @@ int mmq_q6k_q8t_fp32out(const void* w, int64_t m, int64_t k, const uint16_t* qt,
     int rc = check_mmq(w, m, k, reinterpret_cast<const int8_t*>(qt), n, out, &empty, mmq::kQ6kBlockBytes);
     if (rc != MMQ_OK || empty) return rc;
     if (n > kMaxDim - 127 || (n + 127) / 128 * 128 * k >= kMaxElems) return MMQ_ERR_OVERFLOW;
+    if (!threads_ok((m + 127) / 128 * ((n + 127) / 128), 1024)) return MMQ_ERR_OVERFLOW;
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     rc = check_device();
@@ -354,6 +406,7 @@ const char* mmq_status_string(int status) {
         case MMQ_ERR_OVERFLOW: return "MMQ_ERR_OVERFLOW: size beyond the kernels' index range";
         case MMQ_ERR_DEVICE: return "MMQ_ERR_DEVICE: no HIP device, or the current device is not gfx950";
         case MMQ_ERR_HIP: return "MMQ_ERR_HIP: the HIP runtime reported a launch error";
+        case MMQ_ERR_KERNEL: return "MMQ_ERR_KERNEL: unknown kernel or format, or a kernel outside its token range";
         default: return "unknown mmq status";
     }
 }

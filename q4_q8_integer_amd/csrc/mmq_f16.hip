@@ -40,6 +40,7 @@
 // stage's 32 KiB block into LDS with buffer_load ... lds and convert weights
 // only.
 #include "internal.h"
+#include "kquant_device.h"
 
 namespace mmq {
 namespace {
@@ -56,11 +57,6 @@ constexpr int APC = 1024 / PT;   // q8 pieces per producer thread (128 tokens x 
 constexpr int SPC = 512 / PT;    // scale words per producer thread (128 tokens x 4)
 constexpr int CS = 4;  // chunks per stage (128 k)
 constexpr int NTW = 1;  // 32-token tiles per consumer wave
-// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx950.
-constexpr int kBufferFlags = 0x00020000;
-// s_waitcnt operand: at most n vector-memory operations outstanding, the
-// other counters unconstrained.
-constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // One (token tile, stage) block of the q8 operand tiles: 16 slot rows x 128
 // tokens x 8 binary16 values.
 constexpr int kQtBlockBytes = 16 * BN * 16;
@@ -112,20 +108,6 @@ __device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13
     const uint32_t m1152 = 0xE480E480u;  // (-1152, -1152)
     p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
     p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
-}
-
-// 6-bit (sc, m) of sub-block j (0..7) from the twelve scale bytes held in
-// three dwords s03 = bytes 0-3, s47 = bytes 4-7, s811 = bytes 8-11 (GGUF
-// k-quant packing): j < 4 keeps the low 6 bits of bytes j and j+4; j >= 4
-// takes the nibbles of byte j+4 and the top 2 bits of bytes j-4 and j.
-// Register bit-field extracts only (a byte array here would live in scratch).
-__device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
-                                          int& sc, int& mn) {
-    const int sh = 8 * (j & 3);
-    const int by = (s03 >> sh) & 0xFF, bz = (s47 >> sh) & 0xFF, bw = (s811 >> sh) & 0xFF;
-    const bool hi = j >= 4;
-    sc = hi ? ((bw & 15) | ((by >> 6) << 4)) : (by & 63);
-    mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
 }
 
 __device__ __forceinline__ uint32_t f16x2_splat(float v) {
@@ -486,12 +468,20 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb,
     }
 }
 
+// Super-blocks per float32 partial of the output (BIG kernels only, k
+// above kGroup * 256): every kGroup super-blocks the consumers add their
+// partial into a second accumulator and restart it, so that no float32 sum
+// runs over more than kGroup super-blocks.  (Serial rounding error grows with
+// the square root of the term count: at the largest k, 65536 super-blocks,
+// one sum reaches 1.4e-5 relative; two levels of 256 stay near 2e-6.)
+constexpr int kGroup = 256;
+
 // Waves 0-7 consume (MFMA + fold), waves 8-15 produce (load, convert to
 // binary16 operand slots, or with QT copy the tile block straight into LDS).
 // Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
 // stage further ahead, in registers).  One workgroup barrier per stage.
-template <int TB, bool H, bool REP, bool QT>
+template <int TB, bool H, bool REP, bool QT, bool BIG>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
@@ -552,13 +542,13 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
     const int wm = wave % RW, wn = wave / RW;
     const int g = lane >> 5, l32 = lane & 31;
 
-    v16f acc[2][NTW], accb[2][NTW];
+    v16f acc[2][NTW], accb[2][NTW], acc2[2][NTW];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < NTW; ++b)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = acc2[a][b][v] = 0.0f;
 
     // Stages come in (first, second) half-super-block pairs: stage[0] holds
     // even stages, stage[1] odd ones.  The barriers pair with the producers'.
@@ -568,7 +558,21 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
         __syncthreads();
         consume_stage<1, RT>(stage[1], stage_b[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
+        if (BIG && (((st >> 1) + 1) & (kGroup - 1)) == 0) {
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+#pragma unroll
+                for (int b = 0; b < NTW; ++b) {
+                    acc2[a][b] += acc[a][b];
+                    acc[a][b] = v16f{};
+                }
+        }
     }
+    if (BIG)
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b = 0; b < NTW; ++b) acc[a][b] += acc2[a][b];
 
     const bool vec = (M & 3) == 0;
 #pragma unroll
@@ -608,17 +612,34 @@ static void tile_shape(int m, int n, int& tiles_m, bool& half_tiles, int64_t& ti
     tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
 }
 
+// The kernel instance for a launch: token tile, output type, weight layout,
+// activation format, and whether k has more than kGroup super-blocks.
+template <bool H, bool REP, bool QT>
+static const void* pick_kernel(bool half_tiles, bool big) {
+    if (half_tiles)
+        return big ? (const void*)mmq_f16_kernel<BN / 2, H, REP, QT, true>
+                   : (const void*)mmq_f16_kernel<BN / 2, H, REP, QT, false>;
+    return big ? (const void*)mmq_f16_kernel<BN, H, REP, QT, true>
+               : (const void*)mmq_f16_kernel<BN, H, REP, QT, false>;
+}
+
+static hipError_t launch(const void* f, const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                         int n, void* out, int tiles_m, int64_t tiles, hipStream_t stream) {
+    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
+                    (void*)&tiles_m, (void*)&out};
+    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+}
+
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                                int n, void* out, bool half_out, hipStream_t stream) {
     int tiles_m;
     bool half_tiles;
     int64_t tiles;
     tile_shape(m, n, tiles_m, half_tiles, tiles);
-    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
-                    (void*)&tiles_m, (void*)&out};
-    const void* f = half_tiles ? (half_out ? (const void*)mmq_f16_kernel<BN / 2, true, false, false> : (const void*)mmq_f16_kernel<BN / 2, false, false, false>)
-                               : (half_out ? (const void*)mmq_f16_kernel<BN, true, false, false> : (const void*)mmq_f16_kernel<BN, false, false, false>);
-    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+    const bool big = (k >> 8) > kGroup;
+    const void* f = half_out ? pick_kernel<true, false, false>(half_tiles, big)
+                             : pick_kernel<false, false, false>(half_tiles, big);
+    return launch(f, w, m, k, q, ds, n, out, tiles_m, tiles, stream);
 }
 
 hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
@@ -627,11 +648,9 @@ hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const i
     bool half_tiles;
     int64_t tiles;
     tile_shape(m, n, tiles_m, half_tiles, tiles);
-    void* args[] = {(void*)&wr, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
-                    (void*)&tiles_m, (void*)&out};
-    const void* f = half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true, false>
-                               : (const void*)mmq_f16_kernel<BN, false, true, false>;
-    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+    const bool big = (k >> 8) > kGroup;
+    return launch(pick_kernel<false, true, false>(half_tiles, big), wr, m, k, q, ds, n, out, tiles_m, tiles,
+                  stream);
 }
 
 hipError_t launch_mmq_fp32_f16_tiles(const uint8_t* w, bool repacked, int m, int k, const uint16_t* qt,
@@ -640,14 +659,10 @@ hipError_t launch_mmq_fp32_f16_tiles(const uint8_t* w, bool repacked, int m, int
     bool half_tiles;
     int64_t tiles;
     tile_shape(m, n, tiles_m, half_tiles, tiles);
-    const int8_t* q = reinterpret_cast<const int8_t*>(qt);
-    void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
-                    (void*)&tiles_m, (void*)&out};
-    const void* f = repacked ? (half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, true, true>
-                                           : (const void*)mmq_f16_kernel<BN, false, true, true>)
-                             : (half_tiles ? (const void*)mmq_f16_kernel<BN / 2, false, false, true>
-                                           : (const void*)mmq_f16_kernel<BN, false, false, true>);
-    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+    const bool big = (k >> 8) > kGroup;
+    const void* f = repacked ? pick_kernel<false, true, true>(half_tiles, big)
+                             : pick_kernel<false, false, true>(half_tiles, big);
+    return launch(f, w, m, k, reinterpret_cast<const int8_t*>(qt), ds, n, out, tiles_m, tiles, stream);
 }
 
 }  // namespace mmq

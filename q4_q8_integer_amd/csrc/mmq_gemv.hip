@@ -37,6 +37,7 @@
 //     chunk-pair lanes of a row, then the waves in index order): results do
 //     not depend on timing.
 #include "internal.h"
+#include "kquant_device.h"
 
 namespace mmq {
 namespace {
@@ -55,8 +56,6 @@ constexpr int kStagedRow = 4 * kBlockBytes + 16;   // LDS bytes per row of a 4-b
 constexpr int kStagedArea = 16 * kStagedRow;        // LDS bytes of one step's copy
 // s_waitcnt operand: at most n vector-memory operations outstanding, the
 // other counters untouched (vmcnt bits 3:0 and 15:14)
-constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-constexpr int kBufferFlags = 0x00020000;            // word 3 of a raw buffer resource on gfx950
 // Cache policy of the staged weight copies and of the repacked layout's
 // loads: non-temporal (each weight byte is read once; measured at one token
 // staged 24.0 -> 23.4 us and repacked 23.8 -> 21.6 us on 28672 x 8192).  Not
@@ -228,19 +227,8 @@ __device__ __forceinline__ void gemv_sb(const v4u h, const v4u qa, const v4u qb,
         m0 = (h[1] >> 16) & 0xFF;
         m1 = h[1] >> 24;
     } else {
-    // 6-bit (sc, m) of chunks 2p and 2p+1 (GGUF k-quant scale packing).
-    // Chunks 0-3: low 6 bits of scale bytes j (sc) and j+4 (m).  Chunks 4-7:
-    // a nibble of byte j+4 (low: sc, high: m) topped with the 2 high bits of
-    // byte j-4 (sc) or j (m).  Both cases as a 4-bit field plus a 2-bit
-    // field, so no lane branches.
-        const bool lo4 = p < 2;
-        const int sh = 16 * (p & 1);
-        const uint32_t xs = lo4 ? h[1] : h[3], xm = lo4 ? h[2] : h[3];
-        const int oh = lo4 ? 4 : 6, om = lo4 ? 0 : 4;
-        sc0 = __builtin_amdgcn_ubfe(xs, sh, 4) | (__builtin_amdgcn_ubfe(h[1], sh + oh, 2) << 4);
-        sc1 = __builtin_amdgcn_ubfe(xs, sh + 8, 4) | (__builtin_amdgcn_ubfe(h[1], sh + 8 + oh, 2) << 4);
-        m0 = __builtin_amdgcn_ubfe(xm, sh + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + oh, 2) << 4);
-        m1 = __builtin_amdgcn_ubfe(xm, sh + 8 + om, 4) | (__builtin_amdgcn_ubfe(h[2], sh + 8 + oh, 2) << 4);
+        // 6-bit (sc, m) of chunks 2p and 2p+1 (GGUF k-quant scale packing)
+        scale_min_pair(h[1], h[2], h[3], p, sc0, sc1, m0, m1);
     }
     const float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1;
     const float kn0 = -kMagic * dsc0, kn1 = -kMagic * dsc1;

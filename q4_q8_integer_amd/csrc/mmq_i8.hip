@@ -26,6 +26,7 @@
 //   kFp32  float32 out[t][o] with the two-term fold applied per chunk;
 //   kF16   the same, stored as binary16 (nearest-even from the float32 value).
 #include "internal.h"
+#include "kquant_device.h"
 
 namespace mmq {
 namespace {
@@ -43,17 +44,6 @@ enum { kDots = 0, kFp32 = 1, kF16 = 2 };
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
-// 6-bit (sc, m) of sub-block j from the 12 scale bytes (GGUF k-quant packing).
-__device__ __forceinline__ void scale_min(const uint8_t* s, int j, int& sc, int& mn) {
-    if (j < 4) {
-        sc = s[j] & 63;
-        mn = s[j + 4] & 63;
-    } else {
-        sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
-        mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
-    }
 }
 
 template <int EPI>
@@ -96,14 +86,10 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
             if (EPI != kDots && p == 0) {
                 const float d = half_bits_to_float(v.x);
                 const float dmin = half_bits_to_float(v.x >> 16);
-                uint8_t s[12];
-                *reinterpret_cast<uint32_t*>(s) = v.y;
-                *reinterpret_cast<uint32_t*>(s + 4) = v.z;
-                *reinterpret_cast<uint32_t*>(s + 8) = v.w;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     int sc, mn;
-                    scale_min(s, j, sc, mn);
+                    scale_min(v.y, v.z, v.w, j, sc, mn);
                     sDsc[j][r] = d * (float)sc;
                     sNdm[j][r] = -(dmin * (float)mn);
                 }

@@ -36,6 +36,7 @@
 // the next super-block's copied during the current one), and take every
 // field from there as aligned dwords shifted into place.
 #include "internal.h"
+#include "kquant_device.h"
 #include "q6k_device.h"
 
 namespace mmq {
@@ -50,9 +51,7 @@ constexpr int CT = 512;          // consumer threads (8 waves of 64 rows x 32 to
 constexpr int PT = 512;          // producer threads (8 waves)
 constexpr int NT = CT + PT;
 constexpr int CS = 2;            // chunks per stage (64 k)
-constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer resource on gfx950
 // s_waitcnt operand: at most n vector-memory operations outstanding.
-constexpr int kWaitVmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // One (token tile, 128-k stage) block of the q8 operand tiles (bytes).
 constexpr int kQtBlockBytes = 16 * BN * 16;
 
@@ -396,11 +395,18 @@ __device__ __forceinline__ void settle(const RawPieces& rp) {
         asm volatile("" ::"v"(rp.v[j].x), "v"(rp.v[j].y), "v"(rp.v[j].z), "v"(rp.v[j].w));
 }
 
+// Super-blocks per float32 partial of the output (BIG kernels only, k above
+// kGroup * 256): every kGroup super-blocks the consumers add their partial
+// into a second accumulator and restart it, so that no float32 sum runs over
+// more than kGroup super-blocks (the serial rounding error grows with the
+// square root of the term count).
+constexpr int kGroup = 256;
+
 // Waves 0-7 consume (MFMA + fold), waves 8-15 produce (load, convert).  Two
 // LDS stages alternate: while the consumers work on stage s, the producers
 // fill stage s+1, their loads running one stage further ahead in registers.
 // One workgroup barrier per stage.
-template <bool H, bool QT>
+template <bool H, bool QT, bool BIG>
 __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restrict__ w,
                                                          const int8_t* __restrict__ q,
                                                          const uint32_t* __restrict__ ds,
@@ -461,11 +467,11 @@ __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restri
     const int wm = wave & 1, wn = wave >> 1;
     const int g = lane >> 5, l32 = lane & 31;
 
-    v16f acc[2], accb[2];
+    v16f acc[2], accb[2], acc2[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][v] = accb[a][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) acc[a][v] = accb[a][v] = acc2[a][v] = 0.0f;
 
     // Four stages per super-block: (first, -, -, last) on stages 0,1,0,1.
     __syncthreads();   // the producers' raw copy 0
@@ -479,7 +485,17 @@ __global__ __launch_bounds__(NT) void mmq_q6k_f16_kernel(const uint8_t* __restri
         __syncthreads();
         consume_stage<false, true>(stage[1], stage_b[1], wm, wn, g, l32, acc, accb);
         __syncthreads();
+        if (BIG && (((st >> 2) + 1) & (kGroup - 1)) == 0) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                acc2[a] += acc[a];
+                acc[a] = v16f{};
+            }
+        }
     }
+    if (BIG)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[a] += acc2[a];
 
     const bool vec = (M & 3) == 0;
 #pragma unroll
@@ -510,7 +526,11 @@ hipError_t launch_q6k_f16(const uint8_t* w, int m, int k, const int8_t* q, const
     const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    const void* f = half_out ? (const void*)mmq_q6k_f16_kernel<true, false> : (const void*)mmq_q6k_f16_kernel<false, false>;
+    const bool big = (k >> 8) > kGroup;
+    const void* f = half_out ? (big ? (const void*)mmq_q6k_f16_kernel<true, false, true>
+                                    : (const void*)mmq_q6k_f16_kernel<true, false, false>)
+                             : (big ? (const void*)mmq_q6k_f16_kernel<false, false, true>
+                                    : (const void*)mmq_q6k_f16_kernel<false, false, false>);
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 
@@ -521,8 +541,9 @@ hipError_t launch_q6k_f16_tiles(const uint8_t* w, int m, int k, const uint16_t* 
     const int8_t* q = reinterpret_cast<const int8_t*>(qt);
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
                     (void*)&tiles_m, (void*)&out};
-    return hipLaunchKernel((const void*)mmq_q6k_f16_kernel<false, true>, dim3((unsigned)tiles), dim3(NT), args,
-                           0, stream);
+    const void* f = (k >> 8) > kGroup ? (const void*)mmq_q6k_f16_kernel<false, true, true>
+                                      : (const void*)mmq_q6k_f16_kernel<false, true, false>;
+    return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
 }
 
 }  // namespace mmq

@@ -29,6 +29,7 @@
 //     partial sums are added in a fixed order (the four quarter lanes of a
 //     row by a butterfly, then the waves in index order).
 #include "internal.h"
+#include "kquant_device.h"
 #include "q6k_device.h"
 
 namespace mmq {
@@ -108,7 +109,6 @@ struct Seg {
     static constexpr int kLoads = (16 * kSlots + 63) / 64;               // load instructions per step
 };
 
-constexpr int kBufferFlags = 0x00020000;   // word 3 of a raw buffer resource on gfx950
 // s_waitcnt operand: no vector-memory operation outstanding, the other
 // counters untouched
 constexpr int kWaitVmcnt0 = 0x0F70;

@@ -35,6 +35,7 @@
 //     49 / 50 us).  With 2-4 tiles its per-wave token copies cost more LDS
 //     than they save, so this kernel keeps 17-64 tokens.
 #include "internal.h"
+#include "kquant_device.h"
 
 namespace mmq {
 namespace {
@@ -47,17 +48,6 @@ constexpr int NT = 64 * WAVES;
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
-// 6-bit (sc, m) of sub-block j from the scale bytes in three dwords (GGUF
-// k-quant packing; see mmq_f16.hip).
-__device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
-                                          int& sc, int& mn) {
-    const int sh = 8 * (j & 3);
-    const int by = (s03 >> sh) & 0xFF, bz = (s47 >> sh) & 0xFF, bw = (s811 >> sh) & 0xFF;
-    const bool hi = j >= 4;
-    sc = hi ? ((bw & 15) | ((by >> 6) << 4)) : (by & 63);
-    mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
 }
 
 // LDS of a workgroup: the staging areas of the main loop, reused after it
@@ -302,7 +292,6 @@ hipError_t launch_t(const uint8_t* w, int m, int k, const int8_t* q, const uint3
 // a step computes.
 constexpr int kFewWaves = 4;
 constexpr int kFewNT = 64 * kFewWaves;
-constexpr int kBufferFlags = 0x00020000;   // word 3 of a raw buffer resource on gfx950
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0), other counters untouched
 
 // Copies are made by buffer loads that write LDS directly: lane i of a load

@@ -14,21 +14,10 @@
 // producers likewise read a chunk pair's (sc, m) as one dword.  148 bytes per
 // row and super-block against 144.
 #include "internal.h"
+#include "kquant_device.h"
 
 namespace mmq {
 namespace {
-
-// 6-bit (sc, m) of sub-block j from the scale bytes in three dwords (GGUF
-// k-quant packing: j < 4 keeps the low 6 bits of bytes j and j+4; j >= 4
-// takes the nibbles of byte j+4 and the top 2 bits of bytes j-4 and j).
-__device__ __forceinline__ void scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
-                                          uint32_t& sc, uint32_t& mn) {
-    const int sh = 8 * (j & 3);
-    const uint32_t by = (s03 >> sh) & 0xFF, bz = (s47 >> sh) & 0xFF, bw = (s811 >> sh) & 0xFF;
-    const bool hi = j >= 4;
-    sc = hi ? ((bw & 15) | ((by >> 6) << 4)) : (by & 63);
-    mn = hi ? ((bw >> 4) | ((bz >> 6) << 4)) : (bz & 63);
-}
 
 // One record per 64 lanes: lane 16p + r takes row r's header and its qs
 // bytes 32p .. 32p+31.
@@ -49,10 +38,11 @@ __global__ __launch_bounds__(256) void q4k_repack_kernel(const uint8_t* __restri
     }
     uint8_t* out = wr + rec * kRepackRecordBytes;
     if (p == 0) *reinterpret_cast<uint32_t*>(out + 4 * r) = hdr.x;
-    uint32_t sc0, m0, sc1, m1;
+    int sc0, m0, sc1, m1;
     scale_min(hdr.y, hdr.z, hdr.w, 2 * p, sc0, m0);
     scale_min(hdr.y, hdr.z, hdr.w, 2 * p + 1, sc1, m1);
-    *reinterpret_cast<uint32_t*>(out + 64 + 4 * (16 * p + r)) = sc0 | (sc1 << 8) | (m0 << 16) | (m1 << 24);
+    *reinterpret_cast<uint32_t*>(out + 64 + 4 * (16 * p + r)) =
+        (uint32_t)sc0 | ((uint32_t)sc1 << 8) | ((uint32_t)m0 << 16) | ((uint32_t)m1 << 24);
     *reinterpret_cast<uint4*>(out + 320 + 512 * p + 16 * r) = qa;
     *reinterpret_cast<uint4*>(out + 320 + 512 * p + 256 + 16 * r) = qb;
 }

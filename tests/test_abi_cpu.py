@@ -192,3 +192,159 @@ def test_q6k_weight_bytes_limit(lib):
 def test_binding_raises_on_error_status(lib):
     with pytest.raises(binding.MMQError):
         binding._check("q8_quantize_rows", SHAPE)
+
+
+KERNEL = -7
+K_AUTO, K_DOT4, K_FEW, K_F16, K_I8 = 0, 1, 2, 3, 4
+
+
+@pytest.mark.parametrize("fn", ["mmq_q4k_q8_fold", "mmq_q6k_q8_fold"])
+@pytest.mark.parametrize("args,want", [
+    ((A, 8, 512, A, A, -3, A, 0, K_AUTO), SHAPE),
+    ((A, 8, 288, A, A, 3, A, 0, K_F16), SHAPE),
+    ((A, 8, 1 << 25, A, A, 3, A, 0, K_F16), OVERFLOW),
+    ((0, 8, 512, A, A, 3, A, 0, K_F16), NULL),
+    ((A, 8, 512, A, 0, 3, A, 0, K_F16), NULL),
+    ((A, 8, 512, A, A, 3, MIS, 1, K_F16), ALIGN),
+    ((A, 8, 512, A, A, 3, A, 0, 9), KERNEL),          # unknown kernel id
+    ((A, 8, 512, A, A, 3, A, 0, -1), KERNEL),
+    ((A, 8, 512, A, A, 9, A, 0, K_DOT4), KERNEL),     # dot4 takes at most 8 tokens
+    ((A, 8, 512, A, A, 0, A, 0, 9), OK),              # empty calls succeed before the kernel check
+])
+def test_fold_kernel_validation(lib, fn, args, want):
+    assert getattr(lib, fn)(*args, None) == want
+
+
+def test_fold_kernel_token_ranges(lib):
+    # the few-token MFMA kernel takes at most 64 tokens, and has no q6_K form
+    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 65, A, 0, K_FEW, None) == KERNEL
+    assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_FEW, None) == KERNEL
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a HIP device")
+def test_fold_kernel_valid_arguments_reach_device_check(lib):
+    for k in (K_AUTO, K_DOT4, K_FEW, K_F16, K_I8):
+        assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 3, A, 0, k, None) == DEVICE
+    for k in (K_AUTO, K_DOT4, K_F16, K_I8):
+        assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 3, A, 1, k, None) == DEVICE
+
+
+def test_grid_limits_are_overflow_errors(lib):
+    """Sizes inside the element limits whose launch would exceed HIP's 2^32
+    work-items per grid are MMQ_ERR_OVERFLOW, before any HIP call."""
+    # quantizer: 4 lanes per 32-block, n*k/8 work-items
+    n, k = 1 << 20, 1 << 15
+    assert n * k < 1 << 40 and n * k // 8 >= 1 << 32
+    assert lib.q8_quantize_rows(A, n, k, A, A, None) == OVERFLOW
+    assert lib.q8_quantize_silu_mul(A, A, n, k, A, A, None) == OVERFLOW
+    assert lib.q8_quantize_rows_tiled(A, n, k, A, A, None) == OVERFLOW
+    assert lib.q8_quantize_silu_mul_tiled(A, A, n, k, A, A, None) == OVERFLOW
+    # binary16-MFMA kernel: 1024 work-items per 128 x 64 tile
+    m, n, k = 1 << 19, 1 << 16, 256
+    assert n * m < 1 << 40 and (m // 128) * (n // 64) * 1024 >= 1 << 32
+    for fn in ("mmq_q4k_q8_fp32out", "mmq_q4k_q8_f16out", "mmq_q4kr_q8_fp32out", "mmq_q4k_q8t_fp32out",
+               "mmq_q4kr_q8t_fp32out"):
+        assert getattr(lib, fn)(A, m, k, A, A, n, A, None) == OVERFLOW, fn
+    # the q6_K binary16 kernel: 1024 work-items per 128 x 128 tile
+    n = 1 << 17
+    assert (m // 128) * (n // 128) * 1024 >= 1 << 32
+    for fn in ("mmq_q6k_q8_fp32out", "mmq_q6k_q8t_fp32out"):
+        assert getattr(lib, fn)(A, m, k, A, A, n, A, None) == OVERFLOW, fn
+    # dot4 kernel at one token: 256 work-items per 16 rows
+    m = 1 << 28
+    assert lib.mmq_q4k_q8_fp32out(A, m, 256, A, A, 1, A, None) == OVERFLOW
+    assert lib.mmq_q6k_q8_fp32out(A, m, 256, A, A, 1, A, None) == OVERFLOW
+    assert lib.mmq_q4kr_q8_fp32out(A, m, 256, A, A, 1, A, None) == OVERFLOW
+    # repack: 64 work-items per record of 16 rows
+    assert lib.q4k_repack(A, (1 << 31) - 1, 256, A, None) == OVERFLOW
+
+
+@pytest.mark.parametrize("m,n,want", [
+    (4096, 1, K_DOT4), (4096, 8, K_DOT4), (4096, 9, K_FEW), (28672, 32, K_FEW),
+    (28672, 33, K_F16),            # 224 x 1 tiles of 128 x 128: enough for the chip
+    (20480, 33, K_F16),            # 160 tiles: the threshold
+    (20352, 33, K_FEW),            # 159 tiles
+    (8192, 33, K_FEW), (8192, 64, K_FEW), (8192, 65, K_F16), (4096, 2630, K_F16),
+])
+def test_kernel_choice_q4k(lib, m, n, want):
+    assert lib.mmq_kernel_choice(0, m, 4096, n) == want
+
+
+@pytest.mark.parametrize("m,n,want", [
+    (4096, 8, K_DOT4), (4096, 16, K_DOT4), (28672, 17, K_F16), (8192, 17, K_DOT4),
+    (8192, 40, K_DOT4), (8192, 41, K_F16), (4096, 2630, K_F16),
+])
+def test_kernel_choice_repacked(lib, m, n, want):
+    assert lib.mmq_kernel_choice(1, m, 4096, n) == want
+
+
+def test_kernel_choice_other_formats(lib):
+    assert [lib.mmq_kernel_choice(2, 4096, 4096, n) for n in (1, 8, 9, 2630)] == [K_DOT4, K_DOT4, K_F16, K_F16]
+    for fmt in (3, 4, 5):
+        assert lib.mmq_kernel_choice(fmt, 4096, 4096, 1) == K_F16
+    assert lib.mmq_kernel_choice(6, 4096, 4096, 1) == KERNEL
+    assert lib.mmq_kernel_choice(0, 4096, 300, 1) == SHAPE
+    assert lib.mmq_kernel_choice(0, -1, 4096, 1) == SHAPE
+    assert binding.mmq_kernel_choice(binding.FORMAT_Q4K, 4096, 4096, 2630) == binding.KERNEL_F16
+    with pytest.raises(binding.MMQError):
+        binding.mmq_kernel_choice(0, 4096, 300, 1)
+
+
+# ------------------------------------------------ binding size checks (no GPU)
+# The C ABI sees only pointers; the binding checks every tensor's size (and
+# that all tensors share a device) against m, k, n before the call, so a
+# wrong size raises ValueError instead of reaching a kernel.  CPU tensors
+# stand in for device tensors here: the checks run before any library call.
+def _t(nbytes, dtype=torch.uint8, device="cpu"):
+    item = torch.empty((), dtype=dtype).element_size()
+    return torch.empty((nbytes + item - 1) // item, dtype=dtype, device=device)
+
+
+M_, K_, N_ = 40, 512, 3
+GOOD = dict(w=M_ * (K_ // 256) * 144, q=N_ * K_, ds=N_ * (K_ // 32) * 4, out=N_ * M_ * 4)
+
+
+@pytest.mark.parametrize("short", ["w", "q", "ds", "out"])
+def test_binding_rejects_short_tensors(short):
+    sizes = dict(GOOD)
+    sizes[short] -= 1
+    w, q, ds, out = _t(sizes["w"]), _t(sizes["q"], torch.int8), _t(sizes["ds"]), _t(sizes["out"])
+    with pytest.raises(ValueError, match=short):
+        binding.mmq_q4k_q8_fp32out(w, M_, K_, q, ds, N_, out)
+
+
+def test_binding_size_checks_cover_every_fold_call():
+    w, q, ds = _t(GOOD["w"]), _t(GOOD["q"], torch.int8), _t(GOOD["ds"])
+    small = _t(16)
+    calls = [
+        lambda: binding.mmq_q4k_q8(w, M_, K_, q, ds, N_, small),
+        lambda: binding.mmq_q4k_q8_f16out(w, M_, K_, q, ds, N_, small),
+        lambda: binding.mmq_q4k_q8_fold(w, M_, K_, q, ds, N_, small, 0, 0),
+        lambda: binding.mmq_q4kr_q8_fp32out(w, M_, K_, q, ds, N_, _t(GOOD["out"])),   # records are larger
+        lambda: binding.mmq_q4k_q8t_fp32out(w, M_, K_, q, ds, N_, _t(GOOD["out"])),   # tiles are 128 tokens
+        lambda: binding.mmq_q6k_q8_fp32out(w, M_, K_, q, ds, N_, _t(GOOD["out"])),    # q6_K blocks are 210 B
+        lambda: binding.mmq_q6k_q8(w, M_, K_, q, ds, N_, small),
+        lambda: binding.q4k_repack(w, M_, K_, small),
+        lambda: binding.q8_quantize_rows(_t(N_ * K_ * 4 - 4), N_, K_, q, ds),
+        lambda: binding.q8_quantize_rows_tiled(_t(N_ * K_ * 4), N_, K_, small, ds),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError):
+            call()
+
+
+def test_binding_rejects_mixed_devices():
+    w, q, ds = _t(GOOD["w"]), _t(GOOD["q"], torch.int8), _t(GOOD["ds"])
+    out = _t(GOOD["out"], device="meta")
+    with pytest.raises(ValueError, match="one device"):
+        binding.mmq_q4k_q8_fp32out(w, M_, K_, q, ds, N_, out)
+
+
+def test_binding_tensor_shape_helpers():
+    with pytest.raises(ValueError):
+        binding._tokens(torch.empty((3, 256), dtype=torch.int8), 512)
+    with pytest.raises(ValueError):
+        binding._scale_words(torch.empty((3, 8), dtype=torch.int32), 3, 512)
+    with pytest.raises(ValueError):
+        binding._mmq_sizes(4, 300, 1)
+    assert binding._tokens(torch.empty((3, 512), dtype=torch.int8), 512) == 3

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import MAX_ABS_ROW, gpu_quantize, note, to_dev
+from gpu_helpers import MAX_ABS_ROW, gpu_quantize, note, sample_tokens, to_dev
 from q4_q8_integer_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,16 @@ def test_f16out_subnormal_outputs(n):
 
 
 def test_f16out_qproj_full_size():
+    """The full 7B q-proj (2630 tokens): bit for bit the rounded float32
+    output everywhere, and on sampled tokens within one binary16 ulp of the
+    float64 oracle plus the row bar."""
     f, x = synth.qproj_inputs()
     note("f16out q-proj full size")
-    _, o32, o16 = _both(f, x)
+    w, o32, o16 = _both(f, x)
     assert np.array_equal(o16.view(np.uint16), o32.astype(np.float16).view(np.uint16))
+    toks = sample_tokens(x.shape[0], 32)
+    rq, rds = oracle.quantize(x[toks])
+    ref = oracle.out_f64(w, f.m, f.k, rq, rds)
+    rowscale = np.abs(ref).max(axis=1, keepdims=True)
+    err = np.abs(o16[toks].astype(np.float64) - ref)
+    assert np.all(err <= _ulp16(ref) + MAX_ABS_ROW * rowscale)

@@ -146,14 +146,13 @@ def test_ffn_full(which):
 def test_layer_set(n):
     inputs = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in",
               "gate": "ffn_in", "up": "ffn_in", "down": "down_in"}
-    names = ("q", "down") if n == 8192 else ("q", "k", "v", "o", "gate", "up", "down")
     cache = {}
-    for name in names:
+    for name in ("q", "k", "v", "o", "gate", "up", "down"):
         src = inputs[name]
         if src not in cache:
             cache[src] = synth.layer_activation(src, n)
         sampled_check(synth.layer_weights(name), cache[src], "layer %s N=%d" % (name, n),
-                      count=32, dots_rows=96 if name in ("q", "down") else 0)
+                      count=24 if n == 8192 else 32, dots_rows=96 if name in ("q", "down") else 0)
 
 
 @pytest.mark.parametrize("name", ["wide_in", "wide_out"])

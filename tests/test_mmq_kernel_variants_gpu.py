@@ -1,67 +1,96 @@
-"""Every float32 kernel meets the same bar on shapes outside its default
-range: MMQ_FP32_KERNEL=i8 (int8-MFMA kernel, kept for comparison), f16 (the
-binary16-MFMA kernel, default above 64 tokens and from 49 where the matrix
-gives it enough tiles, here also on few tokens), small (the few-token
-int8-MFMA kernels, one-tile up to 16 tokens and multi-tile above, default
-from 9 tokens, here also on fewer), pair (the
-chunk-pair int8-MFMA kernel, kept for comparison) and gemv (the vector-ALU
-dot4 kernel, default up to 8 tokens).  Each forced kernel's binary16 output
-must equal its float32 output rounded to nearest-even, bit for bit.  The
-switch is read once per process, so each runs in one child process."""
-import os
-import subprocess
-import sys
-
+"""Every q4_K float32 kernel meets the same bar on shapes outside its
+default range, named through mmq_q4k_q8_fold: i8 (the int8-MFMA kernel with a
+three-operation fold, kept for comparison), f16 (the binary16-MFMA kernel,
+default above 64 tokens and from 33 where the matrix gives it enough tiles,
+here also on few tokens), few (the few-token int8-MFMA kernels, one tile up
+to 16 tokens and more above, default from 9 tokens, here also on fewer) and
+dot4 (the vector-ALU kernel, default up to 8 tokens).  Each kernel's binary16
+output must equal its float32 output rounded to nearest-even, bit for bit,
+and the automatic choice must equal the kernel mmq_kernel_choice names."""
+import numpy as np
 import pytest
+import torch
+
+import oracle
+from gpu_helpers import check_fp32, gpu_quantize, note, to_dev
+from q4_q8_integer_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-
-CHILD = r"""
-import sys
-sys.path.insert(0, %(root)r)
-sys.path.insert(0, %(tests)r)
-import numpy as np
-import oracle
-from gpu_helpers import check_fp32, gpu_quantize, to_dev
-from q4_q8_integer_amd import binding, synth
-import torch
-for seed, (n, m, k) in enumerate(%(shapes)s):
-    f = synth.random_fields(500 + seed, m, k, sc_zero_frac=0.1)
-    x = synth.random_activations(500 + seed, n, k, "outliers")
-    w = synth.pack_q4k(f)
-    q, ds = gpu_quantize(x)
-    wd = to_dev(w)
-    got = binding.fp32(wd, m, k, q, ds)
-    got16 = binding.fp16(wd, m, k, q, ds)
-    torch.cuda.synchronize()
-    assert np.array_equal(got16.cpu().numpy().view(np.uint16),
-                          got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16out != rounded fp32out"
-    rq, rds = oracle.quantize(x)
-    rel, worst = check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "forced kernel")
-    print("case", n, m, k, "rel %%.2e" %% rel, flush=True)
-print("ok")
-"""
-
-
 SHAPES = {
-    "i8": [(64, 256, 512), (77, 200, 768), (130, 129, 512), (5, 131, 2304)],
-    "f16": [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304)],
-    "small": [(1, 1, 256), (7, 31, 1280), (16, 17, 2304), (17, 200, 768), (48, 129, 512),
-              (64, 256, 11008)],
-    "gemv": [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
-             (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
-    "pair": [(1, 1, 256), (2, 17, 2304), (4, 33, 512), (5, 200, 768), (7, 129, 4352),
-             (8, 16, 256), (9, 131, 2304), (12, 64, 1280), (16, 256, 11008)],
+    binding.KERNEL_I8: [(64, 256, 512), (77, 200, 768), (130, 129, 512), (5, 131, 2304)],
+    binding.KERNEL_F16: [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304)],
+    binding.KERNEL_FEW: [(1, 1, 256), (7, 31, 1280), (16, 17, 2304), (17, 200, 768), (48, 129, 512),
+                         (64, 256, 11008)],
+    binding.KERNEL_DOT4: [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
+                          (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
 }
 
 
-@pytest.mark.parametrize("kernel", sorted(SHAPES))
-def test_forced_fp32_kernel_matches_oracle(kernel):
-    env = dict(os.environ, MMQ_FP32_KERNEL=kernel)
-    code = CHILD % {"root": ROOT, "tests": os.path.join(ROOT, "tests"), "shapes": repr(SHAPES[kernel])}
-    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                       timeout=300)
-    print(r.stdout, r.stderr[-2000:])
-    assert r.returncode == 0 and r.stdout.strip().endswith("ok")
+@pytest.mark.parametrize("kernel", sorted(SHAPES), ids=lambda k: binding.KERNEL_NAMES[k])
+def test_named_fp32_kernel_matches_oracle(kernel):
+    for seed, (n, m, k) in enumerate(SHAPES[kernel]):
+        note("named kernel %s n=%d m=%d k=%d" % (binding.KERNEL_NAMES[kernel], n, m, k))
+        f = synth.random_fields(500 + seed, m, k, sc_zero_frac=0.1)
+        x = synth.random_activations(500 + seed, n, k, "outliers")
+        w = synth.pack_q4k(f)
+        q, ds = gpu_quantize(x)
+        wd = to_dev(w)
+        got = binding.fold_kernel(wd, m, k, q, ds, kernel)
+        got16 = binding.fold_kernel(wd, m, k, q, ds, kernel, f16=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(got16.cpu().numpy().view(np.uint16),
+                              got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16 != rounded fp32"
+        rq, rds = oracle.quantize(x)
+        check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "named kernel")
+
+
+@pytest.mark.parametrize("n,m", [(1, 64), (8, 300), (9, 64), (33, 129), (33, 20480), (48, 20352), (65, 96)])
+def test_auto_equals_the_named_choice(n, m):
+    """The entry point's own choice is bitwise the kernel mmq_kernel_choice
+    names for the shape (the 33-token rows at 20480 take the binary16 kernel
+    at its 160-tile threshold; 20352 rows stay on the few-token kernel)."""
+    k = 512
+    note("auto choice n=%d m=%d" % (n, m))
+    f = synth.random_fields(530 + n, m, k)
+    x = synth.random_activations(530 + n, n, k)
+    wd = to_dev(synth.pack_q4k(f))
+    q, ds = gpu_quantize(x)
+    choice = binding.mmq_kernel_choice(binding.FORMAT_Q4K, m, k, n)
+    a = binding.fp32(wd, m, k, q, ds)
+    b = binding.fold_kernel(wd, m, k, q, ds, choice)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_named_kernel_outside_its_range_raises():
+    wd = torch.zeros(256 * 144 // 256 * 4, dtype=torch.uint8, device="cuda:0")
+    q = torch.zeros((9, 256), dtype=torch.int8, device="cuda:0")
+    ds = torch.zeros((9, 8), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(binding.MMQError):
+        binding.fold_kernel(wd, 4, 256, q, ds, binding.KERNEL_DOT4)
+
+
+def test_tensor_wrappers_check_sizes_on_device():
+    """The tensor wrappers refuse tensors whose sizes disagree with m, k and
+    the token count, before anything is launched."""
+    m, k, n = 40, 512, 3
+    dev = "cuda:0"
+    w = torch.zeros(m * (k // 256) * 144, dtype=torch.uint8, device=dev)
+    q = torch.zeros((n, k), dtype=torch.int8, device=dev)
+    ds = torch.zeros((n, k // 32), dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        binding.fp32(w[:-1], m, k, q, ds)
+    with pytest.raises(ValueError):
+        binding.fp32(w, m, k, q[:, :256].contiguous(), ds)
+    with pytest.raises(ValueError):
+        binding.fp32(w, m, k, q, ds[:2].contiguous())
+    with pytest.raises(ValueError):
+        binding.fp32(w, m, k, q, ds, out=torch.empty((n, m - 1), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        binding.fp32_repacked(w, m, k, q, ds)          # records are 2368 bytes per 16 rows
+    with pytest.raises(ValueError):
+        binding.q6k_fp32(w, m, k, q, ds)                # q6_K blocks are 210 bytes
+    qt = torch.zeros(binding.tiles_elems(n, k) - 8, dtype=torch.int16, device=dev)
+    with pytest.raises(ValueError):
+        binding.fp32_tiles(w, m, k, qt, ds)

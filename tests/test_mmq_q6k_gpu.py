@@ -3,13 +3,9 @@ against the oracle: bit-exact group dots, the float32 bar, binary16 output
 equal to the rounded float32 output bit for bit, ragged shapes (odd
 super-block counts put blocks at both 2- and 4-byte alignments), both
 kernels (the dot4 kernel by default up to 8 tokens, the binary16-MFMA kernel
-above that, the int8-MFMA tile kernel behind the dots entry; each also forced
-outside its range in a child process), the hand-worked
+above that, the int8-MFMA tile kernel behind the dots entry; each also named
+outside its range through mmq_q6k_q8_fold), the hand-worked
 super-block, full-size workloads, and metamorphic properties."""
-import os
-import subprocess
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -21,7 +17,6 @@ from q4_q8_integer_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def run_case(f, x, what, dots=True):
@@ -146,50 +141,32 @@ def test_q6k_qproj_full_sampled():
     assert np.array_equal(dg.cpu().numpy(), oracle.q6k_dots(wwin, r1 - r0, k, rq))
 
 
-CHILD = r"""
-import sys
-sys.path.insert(0, %(root)r)
-sys.path.insert(0, %(tests)r)
-import numpy as np
-import oracle
-from gpu_helpers import check_fp32, gpu_quantize, to_dev
-from q4_q8_integer_amd import binding, synth
-import torch
-for seed, (n, m, k) in enumerate(%(shapes)s):
-    f = synth.random_q6k_fields(900 + seed, m, k, sc_zero_frac=0.1)
-    x = synth.random_activations(900 + seed, n, k, "outliers")
-    w = synth.pack_q6k(f)
-    q, ds = gpu_quantize(x)
-    wd = to_dev(w)
-    got = binding.q6k_fp32(wd, m, k, q, ds)
-    got16 = binding.q6k_fp16(wd, m, k, q, ds)
-    torch.cuda.synchronize()
-    assert np.array_equal(got16.cpu().numpy().view(np.uint16),
-                          got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16out != rounded fp32out"
-    rq, rds = oracle.quantize(x)
-    rel, worst = check_fp32(got.cpu().numpy(), oracle.q6k_out_f64(w, m, k, rq, rds), "forced q6k kernel")
-    print("case", n, m, k, "rel %%.2e" %% rel, flush=True)
-print("ok")
-"""
-
-
 FORCED = {
-    "i8": [(1, 1, 256), (3, 33, 768), (5, 131, 2304), (8, 200, 1280), (40, 96, 512), (130, 129, 768)],
-    "f16": [(1, 1, 256), (3, 33, 768), (8, 200, 1280), (9, 17, 512), (64, 127, 256), (200, 300, 1280)],
-    "gemv": [(1, 40, 512), (4, 16, 256), (8, 129, 2304)],
+    binding.KERNEL_I8: [(1, 1, 256), (3, 33, 768), (5, 131, 2304), (8, 200, 1280), (40, 96, 512), (130, 129, 768)],
+    binding.KERNEL_F16: [(1, 1, 256), (3, 33, 768), (8, 200, 1280), (9, 17, 512), (64, 127, 256), (200, 300, 1280)],
+    binding.KERNEL_DOT4: [(1, 40, 512), (4, 16, 256), (8, 129, 2304)],
 }
 
 
-@pytest.mark.parametrize("kernel", sorted(FORCED))
-def test_q6k_forced_kernel(kernel):
-    """Every q6_K fold kernel meets the bar outside its default range
-    (MMQ_Q6K_KERNEL is read once per process, so each runs in a child)."""
-    env = dict(os.environ, MMQ_Q6K_KERNEL=kernel)
-    code = CHILD % {"root": ROOT, "tests": os.path.join(ROOT, "tests"), "shapes": repr(FORCED[kernel])}
-    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                       timeout=300)
-    print(r.stdout, r.stderr[-2000:])
-    assert r.returncode == 0 and r.stdout.strip().endswith("ok")
+@pytest.mark.parametrize("kernel", sorted(FORCED), ids=lambda k: binding.KERNEL_NAMES[k])
+def test_q6k_named_kernel(kernel):
+    """Every q6_K fold kernel meets the bar outside its default range (named
+    through mmq_q6k_q8_fold), and its binary16 output is its float32 output
+    rounded to nearest-even."""
+    for seed, (n, m, k) in enumerate(FORCED[kernel]):
+        note("q6k named kernel %s n=%d m=%d k=%d" % (binding.KERNEL_NAMES[kernel], n, m, k))
+        f = synth.random_q6k_fields(600 + seed, m, k, sc_zero_frac=0.1)
+        x = synth.random_activations(600 + seed, n, k, "outliers")
+        w = synth.pack_q6k(f)
+        q, ds = gpu_quantize(x)
+        wd = to_dev(w)
+        got = binding.q6k_fold_kernel(wd, m, k, q, ds, kernel)
+        got16 = binding.q6k_fold_kernel(wd, m, k, q, ds, kernel, f16=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(got16.cpu().numpy().view(np.uint16),
+                              got.cpu().numpy().astype(np.float16).view(np.uint16))
+        rq, rds = oracle.quantize(x)
+        check_fp32(got.cpu().numpy(), oracle.q6k_out_f64(w, m, k, rq, rds), "named q6k kernel")
 
 
 # ------------------------------------------------------------- metamorphic
