@@ -7,13 +7,16 @@ resident in HBM before timing starts; several copies of the weights and
 activations are rotated so that the 256 MB last-level cache cannot hold a
 step's working set.
 
-Default workload: the 7B q-projection prefill, W[4096 x 4096] q4_K times
-X[2630 x 4096], with the same step on the library's fastest calls (weights
-repacked at load time, activations quantized to binary16 operand tiles)
-measured beside it under "fastest_path".  Prints one JSON line (see the keys
-in ``main``).
+Default workload: the 7B layer projection set at N = 2048 tokens (q, k, v, o
+4096 x 4096; gate, up 11008 x 4096; down 4096 x 11008; 4 quantizes and 7
+MMQs per step), the configuration the metric's "prefill tok/s over 7B
+projections" is quoted on: tok/s = N / (32 * t_step) for 32 layers.  Beside
+it: the same set at N = 512 and 8192, and the N = 2048 step on the
+library's fastest calls (weights repacked at load time, activations
+quantized to binary16 operand tiles) under "fastest_path".  Prints one JSON
+line (see the keys in ``main``).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload qproj]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload layer2048]
 """
 from __future__ import annotations
 
@@ -32,8 +35,10 @@ if ROOT not in sys.path:
 METRIC = "MMQ int8 TOPS (+% MFMA peak) and prefill tok/s over 7B projections"
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, published
 F16_PEAK_TFLOPS = 2500.0   # MI355X dense binary16 MFMA, published
-DEFAULT_WORKLOAD = "qproj"
-FASTEST = "t_r_qproj"      # the default workload on the fastest calls
+DEFAULT_WORKLOAD = "layer2048"
+FASTEST = "t_r_layer2048"  # the default workload on the fastest calls
+BESIDE = ("layer512", "layer8192")   # the other token counts of the layer set
+LAYERS = 32                # layers of a 7B model (the pages do not state it)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 
 
@@ -94,19 +99,19 @@ def build_workload(name: str):
 
 
 def compute_dtype(desc, f, n):
-    """Arithmetic type of the kernel the library runs for this call (the
-    entry points' dispatch rules, repeated here for labelling): "f16" for the
-    binary16-MFMA kernels (exact integer operands in binary16, float32
-    accumulation), "int8" for the int8 dot4 and int8-MFMA kernels."""
-    from q4_q8_integer_amd import synth
-    tiles128 = ((f.m + 127) // 128) * ((n + 127) // 128)
+    """Arithmetic type of the kernel the library runs for this call, from the
+    library's own dispatch (mmq_kernel_choice): "f16" for the binary16-MFMA
+    kernels (exact integer operands in binary16, float32 accumulation),
+    "int8" for the dot4, few-token and int8-MFMA kernels."""
+    from q4_q8_integer_amd import binding, synth
+    q6 = isinstance(f, synth.Q6KFields)
     if desc.get("tiles"):
-        return "f16"
-    if isinstance(f, synth.Q6KFields):
-        return "f16" if n > 8 else "int8"
-    if desc.get("repacked"):
-        return "f16" if n > 16 and (tiles128 >= 160 or n > 40) else "int8"
-    return "f16" if n > 64 or (n > 48 and tiles128 >= 160) else "int8"
+        fmt = binding.FORMAT_Q6K_TILES if q6 else (
+            binding.FORMAT_Q4K_REPACKED_TILES if desc.get("repacked") else binding.FORMAT_Q4K_TILES)
+    else:
+        fmt = binding.FORMAT_Q6K if q6 else (
+            binding.FORMAT_Q4K_REPACKED if desc.get("repacked") else binding.FORMAT_Q4K)
+    return "f16" if binding.mmq_kernel_choice(fmt, f.m, f.k, n) == binding.KERNEL_F16 else "int8"
 
 
 def weight_format(f):
@@ -134,11 +139,31 @@ def measured_traffic(key: str):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
-def cpu_baseline(mats, inputs, budget_s: float = 12.0):
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(mats, inputs, budget_s: float = 10.0):
     """Time the oracle (as it stands) on a bounded token sample of the same
-    workload: quantize + float64 fold for every projection."""
+    workload: quantize + float64 fold for every projection, with all host
+    threads and with one thread.  Its cost is exactly linear in the tokens,
+    so the rate extends to the whole workload."""
     import oracle
-    from q4_q8_integer_amd import synth
 
     packed = [(weight_format(f)[0](f), f.m, f.k, src, getattr(oracle, weight_format(f)[3]))
               for _, f, src in mats]
@@ -152,13 +177,25 @@ def cpu_baseline(mats, inputs, budget_s: float = 12.0):
             out_f64(w, m, k, q, ds)
         return time.perf_counter() - t0
 
-    probe = min(4, n_full)
-    t = run(probe)
-    nt = int(max(probe, min(n_full, probe * budget_s / max(t, 1e-6))))
-    t = run(nt)
-    ops = sum(2.0 * nt * m * k for _, m, k, _, _ in packed)
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.get_threads(),
+    def timed(budget):
+        probe = min(2, n_full)
+        t = run(probe)
+        nt = int(max(probe, min(n_full, probe * budget / max(t, 1e-6))))
+        return nt, run(nt)
+
+    all_threads = oracle.get_threads()
+    nt, t = timed(budget_s)
+    oracle.set_threads(1)
+    try:
+        nt1, t1 = timed(budget_s / 2)
+    finally:
+        oracle.set_threads(all_threads)
+    flops = sum(2.0 * m * k for _, m, k, _, _ in packed)   # per token
+    return {"value": flops * nt / t / 1e12, "unit": "TOPS", "cores": all_threads,
             "kind": "oracle", "tok_per_s": nt / t,
+            "one_thread": {"value": flops * nt1 / t1 / 1e12, "tok_per_s": nt1 / t1, "cores": 1,
+                           "sample": "first %d tokens (%.1f s)" % (nt1, t1)},
+            "cpu_model": cpu_model(),
             "sample": "first %d tokens of every input, all rows, quantize + float64 fold "
                       "(%.1f s)" % (nt, t)}
 
@@ -266,7 +303,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
-                    help="default: qproj, with the fastest path (%s) measured beside it" % FASTEST)
+                    help="default: %s, with %s and the fastest path (%s) measured beside it"
+                         % (DEFAULT_WORKLOAD, ", ".join(BESIDE), FASTEST))
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--f16-out", action="store_true",
@@ -283,6 +321,7 @@ def main():
     default_run = args.workload is None
     if default_run:
         args.workload = DEFAULT_WORKLOAD
+    host_cpu = cpu_model()   # before the GPU is touched (lscpu runs as a child process)
     if args.workload == "silu_q8":
         return run_silu_q8(args)
 
@@ -297,19 +336,30 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = 2 * src.numel() * 4
     if default_run and not args.f16_out:
-        # The same prefill step through the library's fastest calls: weights
-        # repacked at load time, activations quantized to the binary16
-        # operand tiles (same codes, scale words and output as the headline
-        # calls).  Reported beside the headline, which stays on the
-        # int8-code calls.
+        # The layer set at the other token counts, and the same N = 2048 step
+        # through the library's fastest calls: weights repacked at load time,
+        # activations quantized to the binary16 operand tiles (same codes,
+        # scale words and output as the headline calls).  Reported beside the
+        # headline, which stays on the calls the boundary names.
+        res["layer_set"] = {str(res["config"]["n"]): summary(res)}
+        for wl in BESIDE:
+            alt, _, _ = measure(args, wl)
+            res["layer_set"][str(alt["config"]["n"])] = summary(alt)
         alt, _, _ = measure(args, FASTEST)
-        res["fastest_path"] = {"workload": FASTEST, "step": alt["config"]["step"],
-                               "value": alt["value"], "unit": alt["unit"],
-                               "ms_per_step": alt["ms_per_step"], "tok_per_s": alt["tok_per_s"],
-                               "pct_int8_peak": alt["pct_int8_peak"], "roofline": alt["roofline"]}
+        res["fastest_path"] = dict(summary(alt), workload=FASTEST, step=alt["config"]["step"],
+                                   roofline=alt["roofline"])
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(mats, inputs)
+        res["cpu_baseline"] = dict(cpu_baseline(mats, inputs), cpu_model=host_cpu)
     print(json.dumps(res), flush=True)
+
+
+def summary(r):
+    """The figures of one measured workload that the default line repeats."""
+    keys = ("value", "unit", "ms_per_step", "tok_per_s", "tok_per_s_7b_projections", "pct_int8_peak", "dtype")
+    out = {k: r[k] for k in keys if k in r}
+    out["mmq_us_per_projection"] = r["roofline"]["avg_launch_us"]
+    out["mmq_int8_tops"] = r["roofline"]["int8_tops"]
+    return out
 
 
 def measure(args, workload):
@@ -411,24 +461,18 @@ def measure(args, workload):
     few_tokens = n_tok <= 64
     dtypes = sorted({compute_dtype(desc, f, inputs[src].shape[0]) for _, f, src in mats})
     dtype = "+".join(dtypes)
+    kernels = {lbl: compute_dtype(desc, f, inputs[src].shape[0]) for lbl, f, src in mats}
     if few_tokens:   # weights streamed once: HBM roofline
         roof = {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg_gbs / HBM_PEAK_GBS, 4)}
     else:
-        # the contraction's own dtype: binary16 MFMA above 64 tokens on every
-        # path; the int8-peak fraction (the method's int8 MACs against the
-        # int8 peak) is reported beside it
-        roof = {"bound": "mfma", "achieved": round(achieved_tops, 2), "peak": F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tops / F16_PEAK_TFLOPS, 4),
-                "int8_peak_frac": round(achieved_tops / INT8_PEAK_TOPS, 4)}
-    roof.update({
-        "kernel": mmq_name,
-        "traffic": measured_traffic(mmq_name + "|" + workload),
-        "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
-        "launches_timed": rounds * len(mats),
-        "alg_bytes_per_step": mmq_alg_bytes,
-        "alg_gbs": round(alg_gbs, 1),
-        "int8_tops": round(achieved_tops, 2)})
+        # the method's int8 MACs (2 N M K ops) against the dense int8 MFMA
+        # peak; above 64 tokens the contraction runs on binary16 MFMA with
+        # exact integer operands, whose own peak is half that: its fraction
+        # is reported beside it
+        roof = {"bound": "mfma", "achieved": round(achieved_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
+                "f16_peak_frac": round(achieved_tops / F16_PEAK_TFLOPS, 4)}
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -438,8 +482,16 @@ def measure(args, workload):
                        copies=len(sets)),
         "tok_per_s": round(n_tok / (ms_step * 1e-3), 1),
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "kernels": kernels,
         "roofline": roof,
     }
+    base = workload
+    while base[:2] in ("t_", "r_"):
+        base = base[2:]
+    if base.startswith("layer"):
+        # prefill tok/s over the projections of a 7B model: N tokens through
+        # 32 layers' steps
+        res["tok_per_s_7b_projections"] = round(n_tok / (LAYERS * ms_step * 1e-3), 1)
     del sets
     torch.cuda.empty_cache()
     return res, mats, inputs
