@@ -473,6 +473,14 @@ def measure(args, workload):
         roof = {"bound": "mfma", "achieved": round(achieved_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
                 "f16_peak_frac": round(achieved_tops / F16_PEAK_TFLOPS, 4)}
+    roof.update({
+        "kernel": mmq_name,
+        "traffic": measured_traffic(mmq_name + "|" + workload),
+        "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
+        "launches_timed": rounds * len(mats),
+        "alg_bytes_per_step": mmq_alg_bytes,
+        "alg_gbs": round(alg_gbs, 1),
+        "int8_tops": round(achieved_tops, 2)})
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
