@@ -98,11 +98,9 @@ def build_workload(name: str):
     raise SystemExit("unknown workload %r" % name)
 
 
-def compute_dtype(desc, f, n):
-    """Arithmetic type of the kernel the library runs for this call, from the
-    library's own dispatch (mmq_kernel_choice): "f16" for the binary16-MFMA
-    kernels (exact integer operands in binary16, float32 accumulation),
-    "int8" for the dot4, few-token and int8-MFMA kernels."""
+def kernel_choice(desc, f, n):
+    """(format, kernel id) the library's own dispatch (mmq_kernel_choice)
+    runs for this call."""
     from q4_q8_integer_amd import binding, synth
     q6 = isinstance(f, synth.Q6KFields)
     if desc.get("tiles"):
@@ -111,7 +109,29 @@ def compute_dtype(desc, f, n):
     else:
         fmt = binding.FORMAT_Q6K if q6 else (
             binding.FORMAT_Q4K_REPACKED if desc.get("repacked") else binding.FORMAT_Q4K)
-    return "f16" if binding.mmq_kernel_choice(fmt, f.m, f.k, n) == binding.KERNEL_F16 else "int8"
+    return fmt, binding.mmq_kernel_choice(fmt, f.m, f.k, n)
+
+
+def compute_dtype(desc, f, n):
+    """Arithmetic type of the kernel the library runs for this call: "f16"
+    for the binary16-MFMA kernels (exact integer operands in binary16,
+    float32 accumulation), "int8" for the dot4, narrow, few-token and
+    int8-MFMA kernels."""
+    from q4_q8_integer_amd import binding
+    return "f16" if kernel_choice(desc, f, n)[1] == binding.KERNEL_F16 else "int8"
+
+
+def kernel_source(desc, f, n):
+    """The csrc file of the kernel the library runs for this call."""
+    from q4_q8_integer_amd import binding
+    fmt, kid = kernel_choice(desc, f, n)
+    q6 = fmt in (binding.FORMAT_Q6K, binding.FORMAT_Q6K_TILES)
+    names = ({binding.KERNEL_DOT4: "mmq_q6k_gemv.hip", binding.KERNEL_F16: "mmq_q6k_f16.hip",
+              binding.KERNEL_I8: "mmq_q6k_i8.hip"} if q6 else
+             {binding.KERNEL_DOT4: "mmq_gemv.hip", binding.KERNEL_NARROW: "mmq_narrow.hip",
+              binding.KERNEL_FEW: "mmq_small.hip", binding.KERNEL_F16: "mmq_f16.hip",
+              binding.KERNEL_I8: "mmq_i8.hip"})
+    return "q4_q8_integer_amd/csrc/" + names[kid]
 
 
 def weight_format(f):
@@ -123,18 +143,18 @@ def weight_format(f):
     return synth.pack_q4k, 144.0 / 256.0, "mmq_q4k_q8", "out_f64"
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, src: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record (profiles/traffic.txt), already scaled by the copy-probe factors;
-    None unless the record was taken on the kernel source (its "src") as it
-    is now."""
+    None unless the record was taken on the kernel the library runs now
+    (src, its csrc file) with that source as it is now."""
     import hashlib
     try:
         rec = json.loads(open(os.path.join(ROOT, "profiles", "traffic.txt")).read())[key]
         sha = hashlib.sha256(open(os.path.join(ROOT, rec["src"]), "rb").read()).hexdigest()[:16]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("sha256_16") != sha:
+    if rec.get("src") != src or rec.get("sha256_16") != sha:
         return None
     return int(rec["read_bytes"] + rec["write_bytes"])
 
@@ -269,7 +289,7 @@ def run_silu_q8(args):
                    "n": n, "k": k, "copies": len(sets)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "q8_quantize_silu_mul",
-                     "traffic": measured_traffic("q8_quantize_silu_mul|silu_q8"),
+                     "traffic": measured_traffic("q8_quantize_silu_mul|silu_q8", "q4_q8_integer_amd/csrc/quantize.hip"),
                      "avg_launch_us": round(fused_ms * 1e3, 2), "launches_timed": rounds,
                      "alg_bytes_per_step": alg},
         "unfused_us": round(unfused_ms * 1e3, 2),
@@ -462,6 +482,7 @@ def measure(args, workload):
     dtypes = sorted({compute_dtype(desc, f, inputs[src].shape[0]) for _, f, src in mats})
     dtype = "+".join(dtypes)
     kernels = {lbl: compute_dtype(desc, f, inputs[src].shape[0]) for lbl, f, src in mats}
+    srcs = sorted({kernel_source(desc, f, inputs[src].shape[0]) for _, f, src in mats})
     if few_tokens:   # weights streamed once: HBM roofline
         roof = {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg_gbs / HBM_PEAK_GBS, 4)}
@@ -475,7 +496,7 @@ def measure(args, workload):
                 "f16_peak_frac": round(achieved_tops / F16_PEAK_TFLOPS, 4)}
     roof.update({
         "kernel": mmq_name,
-        "traffic": measured_traffic(mmq_name + "|" + workload),
+        "traffic": measured_traffic(mmq_name + "|" + workload, srcs[0]) if len(srcs) == 1 else None,
         "avg_launch_us": round(mmq_ms * 1e3 / len(mats), 2),
         "launches_timed": rounds * len(mats),
         "alg_bytes_per_step": mmq_alg_bytes,

@@ -104,6 +104,13 @@ hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const 
 // Largest token count the few-token kernel takes.
 constexpr int kSmallMaxN = 64;
 
+// Two-term fold, out[t][o], for 1 <= n <= kNarrowMaxN tokens: 4x4x4 int8
+// MFMA with one weight row and super-block per lane (mmq_narrow.hip).
+hipError_t launch_mmq_fp32_narrow(const uint8_t* w, int m, int k, const int8_t* q,
+                                  const uint32_t* ds, int n, void* out, bool half_out,
+                                  hipStream_t stream);
+constexpr int kNarrowMaxN = 8;
+
 // q6_K weights (210-byte super-blocks, one int8 scale per 16 weights).
 // Exact int32 group dots, dots[t][o][g] (g = k/16 groups).
 hipError_t launch_q6k_dots(const uint8_t* w, int m, int k, const int8_t* q, int n,

@@ -64,9 +64,12 @@ using FoldLaunch = hipError_t (*)(const uint8_t*, int, int, const int8_t*, const
 bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block < (1LL << 32); }
 
 // Kernel behind the q4_K fold entry points for MMQ_KERNEL_AUTO, by token
-// count (measured on the 28672 x 8192 and 8192 x 28672 matrices across
-// n = 9..64):
-//   n <= 8:   the vector-ALU dot4 kernel;
+// count (measured on the 28672 x 8192 and 8192 x 28672 matrices):
+//   n <= 6:   the vector-ALU dot4 kernel (at 2-6 tokens 25-37 us against
+//             30-37 us for the narrow kernel);
+//   n <= 8:   the narrow 4x4x4 int8-MFMA kernel (at 7 / 8 tokens 39.1 / 39.0
+//             us against 39.6 / 42.7 us for dot4 on 28672 x 8192, 38.0 /
+//             38.4 against 39.2 / 41.6 on 8192 x 28672);
 //   n <= 32:  the few-token int8-MFMA kernels (one 16-token tile up to
 //             16 tokens, two tiles up to 32: 74-77 us against 87-89 us for
 //             the binary16 kernel on 28672 x 8192);
@@ -77,7 +80,8 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 //   n > 64:   the binary16-MFMA kernel.
 int q4k_auto_kernel(int64_t m, int64_t n) {
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    return n <= mmq::kGemvMaxN                        ? MMQ_KERNEL_DOT4
+    return n <= 6                                     ? MMQ_KERNEL_DOT4
+           : n <= mmq::kNarrowMaxN                    ? MMQ_KERNEL_NARROW
            : n <= 32                                  ? MMQ_KERNEL_FEW
            : n <= mmq::kSmallMaxN && f16_tiles < 160  ? MMQ_KERNEL_FEW
                                                       : MMQ_KERNEL_F16;
@@ -112,6 +116,10 @@ int q4k_fold_launcher(int kernel, int64_t m, int64_t n, FoldLaunch* f) {
         case MMQ_KERNEL_I8:
             *f = mmq::launch_mmq_fp32;
             return threads_ok((m + 127) / 128 * ((n + 127) / 128), 256) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_NARROW:
+            if (n > mmq::kNarrowMaxN) return MMQ_ERR_KERNEL;
+            *f = mmq::launch_mmq_fp32_narrow;
+            return threads_ok((m + 15) / 16, 512) ? MMQ_OK : MMQ_ERR_OVERFLOW;
         default:
             return MMQ_ERR_KERNEL;
     }

@@ -195,7 +195,7 @@ def test_binding_raises_on_error_status(lib):
 
 
 KERNEL = -7
-K_AUTO, K_DOT4, K_FEW, K_F16, K_I8 = 0, 1, 2, 3, 4
+K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW = 0, 1, 2, 3, 4, 5
 
 
 @pytest.mark.parametrize("fn", ["mmq_q4k_q8_fold", "mmq_q6k_q8_fold"])
@@ -216,14 +216,17 @@ def test_fold_kernel_validation(lib, fn, args, want):
 
 
 def test_fold_kernel_token_ranges(lib):
-    # the few-token MFMA kernel takes at most 64 tokens, and has no q6_K form
+    # the few-token MFMA kernel takes at most 64 tokens, the narrow kernel at
+    # most 8, and neither has a q6_K form
     assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 65, A, 0, K_FEW, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_FEW, None) == KERNEL
+    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 9, A, 0, K_NARROW, None) == KERNEL
+    assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_NARROW, None) == KERNEL
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a HIP device")
 def test_fold_kernel_valid_arguments_reach_device_check(lib):
-    for k in (K_AUTO, K_DOT4, K_FEW, K_F16, K_I8):
+    for k in (K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW):
         assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 3, A, 0, k, None) == DEVICE
     for k in (K_AUTO, K_DOT4, K_F16, K_I8):
         assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 3, A, 1, k, None) == DEVICE
@@ -260,7 +263,8 @@ def test_grid_limits_are_overflow_errors(lib):
 
 
 @pytest.mark.parametrize("m,n,want", [
-    (4096, 1, K_DOT4), (4096, 8, K_DOT4), (4096, 9, K_FEW), (28672, 32, K_FEW),
+    (4096, 1, K_DOT4), (4096, 6, K_DOT4), (4096, 7, K_NARROW), (4096, 8, K_NARROW), (4096, 9, K_FEW),
+    (28672, 32, K_FEW),
     (28672, 33, K_F16),            # 224 x 1 tiles of 128 x 128: enough for the chip
     (20480, 33, K_F16),            # 160 tiles: the threshold
     (20352, 33, K_FEW),            # 159 tiles

@@ -64,8 +64,10 @@ def test_few_token_weight_layouts(n, k):
     to 5 tokens, loaded into registers from 6) and 65 (staged with the next
     step in flight up to 6 tokens: 4 waves of 16-17 super-blocks, so each
     wave's last step runs past its range and the last row's past the
-    matrix).  40 rows leave a half tile.  The result also equals the
-    repacked-layout path bit for bit (same summation order)."""
+    matrix).  40 rows leave a half tile.  The dot4 result also equals the
+    repacked-layout path bit for bit (same summation order); the entry
+    point's own choice (the narrow kernel at 7-8 tokens) meets the same
+    bar."""
     m = 40
     note("few-token layouts n=%d m=%d k=%d" % (n, m, k))
     f = synth.random_fields(700 + 10 * n + k % 7, m, k, sc_zero_frac=0.1)
@@ -73,13 +75,16 @@ def test_few_token_weight_layouts(n, k):
     w = synth.pack_q4k(f)
     wd = to_dev(w)
     q, ds = gpu_quantize(x)
-    got = binding.fp32(wd, m, k, q, ds)
+    dot4 = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_DOT4)
+    auto = binding.fp32(wd, m, k, q, ds)
     rep = binding.fp32_repacked(binding.repack(wd, m, k), m, k, q, ds)
     torch.cuda.synchronize()
-    got = got.cpu().numpy()
-    assert np.array_equal(got.view(np.uint32), rep.cpu().numpy().view(np.uint32))
+    dot4 = dot4.cpu().numpy()
+    assert np.array_equal(dot4.view(np.uint32), rep.cpu().numpy().view(np.uint32))
     rq, rds = oracle.quantize(x)
-    check_fp32(got, oracle.out_f64(w, m, k, rq, rds), "few-token layouts")
+    ref = oracle.out_f64(w, m, k, rq, rds)
+    check_fp32(dot4, ref, "few-token layouts")
+    check_fp32(auto.cpu().numpy(), ref, "few-token auto choice")
 
 
 @pytest.mark.parametrize("k", [2304, 16640])

@@ -3,8 +3,9 @@ default range, named through mmq_q4k_q8_fold: i8 (the int8-MFMA kernel with a
 three-operation fold, kept for comparison), f16 (the binary16-MFMA kernel,
 default above 64 tokens and from 33 where the matrix gives it enough tiles,
 here also on few tokens), few (the few-token int8-MFMA kernels, one tile up
-to 16 tokens and more above, default from 9 tokens, here also on fewer) and
-dot4 (the vector-ALU kernel, default up to 8 tokens).  Each kernel's binary16
+to 16 tokens and more above, default from 9 tokens, here also on fewer),
+dot4 (the vector-ALU kernel, default up to 8 tokens) and narrow (the 4x4x4
+int8-MFMA kernel with one weight row per lane, up to 8 tokens).  Each kernel's binary16
 output must equal its float32 output rounded to nearest-even, bit for bit,
 and the automatic choice must equal the kernel mmq_kernel_choice names."""
 import numpy as np
@@ -24,6 +25,8 @@ SHAPES = {
                          (64, 256, 11008)],
     binding.KERNEL_DOT4: [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
                           (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
+    binding.KERNEL_NARROW: [(1, 1, 256), (2, 65, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
+                            (6, 17, 1280), (7, 131, 2304), (8, 256, 11008), (8, 48, 3584)],
 }
 
 
@@ -45,7 +48,8 @@ def test_named_fp32_kernel_matches_oracle(kernel):
         check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "named kernel")
 
 
-@pytest.mark.parametrize("n,m", [(1, 64), (8, 300), (9, 64), (33, 129), (33, 20480), (48, 20352), (65, 96)])
+@pytest.mark.parametrize("n,m", [(1, 64), (6, 64), (7, 300), (8, 300), (9, 64), (33, 129), (33, 20480), (48, 20352),
+                                 (65, 96)])
 def test_auto_equals_the_named_choice(n, m):
     """The entry point's own choice is bitwise the kernel mmq_kernel_choice
     names for the shape (the 33-token rows at 20480 take the binary16 kernel
@@ -94,3 +98,24 @@ def test_tensor_wrappers_check_sizes_on_device():
     qt = torch.zeros(binding.tiles_elems(n, k) - 8, dtype=torch.int16, device=dev)
     with pytest.raises(ValueError):
         binding.fp32_tiles(w, m, k, qt, ds)
+
+
+@pytest.mark.parametrize("kernel", [binding.KERNEL_DOT4, binding.KERNEL_NARROW, binding.KERNEL_FEW],
+                         ids=lambda k: binding.KERNEL_NAMES[k])
+def test_weight_streaming_kernels_run_to_run_and_token_slice_bitwise(kernel):
+    """The weight-streaming kernels sum every output in an order fixed by m
+    and k alone (waves, steps and partial sums in index order): a repeated
+    call, and a call on a slice of the tokens, give the same bits."""
+    m, k, n = 300, 9216, 8
+    note("run-to-run %s n=%d m=%d k=%d" % (binding.KERNEL_NAMES[kernel], n, m, k))
+    f = synth.random_fields(541, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(541, n, k, "outliers")
+    wd = to_dev(synth.pack_q4k(f))
+    q, ds = gpu_quantize(x)
+    a = binding.fold_kernel(wd, m, k, q, ds, kernel)
+    b = binding.fold_kernel(wd, m, k, q, ds, kernel)
+    s = binding.fold_kernel(wd, m, k, q[3:8].contiguous(), ds[3:8].contiguous(), kernel)
+    torch.cuda.synchronize()
+    a, b, s = (t.cpu().numpy().view(np.uint32) for t in (a, b, s))
+    assert np.array_equal(a, b)
+    assert np.array_equal(a[3:8], s)

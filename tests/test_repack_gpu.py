@@ -39,7 +39,10 @@ def test_repacked_mmq(n, m, k):
     q, ds = gpu_quantize(x)
     wr = binding.repack(wd, m, k)
     got = binding.fp32_repacked(wr, m, k, q, ds)
-    base = binding.fp32(wd, m, k, q, ds)
+    # the repacked records run the dot4 kernel up to 8 tokens and the
+    # binary16 kernel above 64: the same summation order as those kernels on
+    # the q4_K rows
+    base = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_DOT4 if n <= 8 else binding.KERNEL_F16)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
     if n <= 8 or n > 64:
@@ -59,7 +62,7 @@ def test_repacked_wide_in_full(n):
     q, ds = binding.quantize(to_dev(x))
     wr = binding.repack(wd, m, k)
     got = binding.fp32_repacked(wr, m, k, q, ds)
-    base = binding.fp32(wd, m, k, q, ds)
+    base = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_DOT4)   # the records' kernel, on q4_K rows
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy().view(np.uint32), base.cpu().numpy().view(np.uint32))
     assert np.array_equal(wr.cpu().numpy()[:4 * 2368 * 32], oracle.q4k_repack(w[:64], 64, k))
