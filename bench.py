@@ -178,11 +178,14 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(mats, inputs, budget_s: float = 10.0):
+def cpu_baseline(mats, inputs, budget_s: float = 12.0):
     """Time the oracle (as it stands) on a bounded token sample of the same
     workload: quantize + float64 fold for every projection, with all host
-    threads and with one thread.  Its cost is exactly linear in the tokens,
-    so the rate extends to the whole workload."""
+    threads (about budget_s seconds) and with one thread (about 2/3 of
+    that).  Its cost is a fixed part per call (the weight decode) plus a
+    part linear in the tokens; two short probes fit both, and the sample is
+    sized from the fit.  The rate at the sample extends to the whole
+    workload (the fixed part only shrinks with more tokens)."""
     import oracle
 
     packed = [(weight_format(f)[0](f), f.m, f.k, src, getattr(oracle, weight_format(f)[3]))
@@ -198,16 +201,18 @@ def cpu_baseline(mats, inputs, budget_s: float = 10.0):
         return time.perf_counter() - t0
 
     def timed(budget):
-        probe = min(2, n_full)
-        t = run(probe)
-        nt = int(max(probe, min(n_full, probe * budget / max(t, 1e-6))))
+        n0, n1 = min(2, n_full), min(10, n_full)
+        t0, t1 = run(n0), run(n1)
+        per_tok = max((t1 - t0) / max(n1 - n0, 1), 1e-6)
+        fixed = max(t0 - n0 * per_tok, 0.0)
+        nt = int(max(n1, min(n_full, (budget - fixed) / per_tok)))
         return nt, run(nt)
 
     all_threads = oracle.get_threads()
     nt, t = timed(budget_s)
     oracle.set_threads(1)
     try:
-        nt1, t1 = timed(budget_s / 2)
+        nt1, t1 = timed(budget_s * 2 / 3)
     finally:
         oracle.set_threads(all_threads)
     flops = sum(2.0 * m * k for _, m, k, _, _ in packed)   # per token
