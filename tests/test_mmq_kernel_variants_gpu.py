@@ -4,7 +4,7 @@ three-operation fold, kept for comparison), f16 (the binary16-MFMA kernel,
 default above 64 tokens and from 33 where the matrix gives it enough tiles,
 here also on few tokens), few (the few-token int8-MFMA kernels, one tile up
 to 16 tokens and more above, default from 9 tokens, here also on fewer),
-dot4 (the vector-ALU kernel, default up to 8 tokens) and narrow (the 4x4x4
+dot4 (the vector-ALU kernel, default up to 6 tokens) and narrow (the 4x4x4
 int8-MFMA kernel with one weight row per lane, up to 8 tokens).  Each kernel's binary16
 output must equal its float32 output rounded to nearest-even, bit for bit,
 and the automatic choice must equal the kernel mmq_kernel_choice names."""
