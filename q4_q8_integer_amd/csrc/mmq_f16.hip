@@ -39,6 +39,7 @@
 // already binary16 and already in the B slot order: the producers copy each
 // stage's 32 KiB block into LDS with buffer_load ... lds and convert weights
 // only.
+#include "f16_operand.h"
 #include "internal.h"
 #include "kquant_device.h"
 
@@ -61,22 +62,6 @@ constexpr int NTW = 1;  // 32-token tiles per consumer wave
 // tokens x 8 binary16 values.
 constexpr int kQtBlockBytes = 16 * BN * 16;
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
-__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 r = __builtin_elementwise_fma(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b),
-                                     __builtin_bit_cast(h2, c));
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) + __builtin_bit_cast(h2, b));
-}
-
 // 4 qs bytes x = [b0 b1 b2 b3] -> binary16 pairs of sc*nibble, exactly:
 //   low nibbles (chunk 2p):   (x & 0x000F000F) | 0x64006400 = (1024 + n, 1024 + n')
 //                             fma(1024 + n, sc, -1024 sc) = sc*n
@@ -84,13 +69,6 @@ __device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
 //                             fma(1024 + 16n, sc/16, -64 sc) = sc*n
 // and the same on x >> 8 for bytes b1, b3.  Pair order: [b0,b2], [b1,b3].
 // sc, sc/16, -1024 sc and -64 sc are exact binary16 for sc <= 63.
-// (x & mask) | bits in one VALU instruction (the compiler otherwise emits two).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
-    return r;
-}
-
 __device__ __forceinline__ void unpack_word(uint32_t x, uint32_t sclo, uint32_t nblo, uint32_t schi,
                                             uint32_t nbhi, uint32_t& lo02, uint32_t& lo13,
                                             uint32_t& hi02, uint32_t& hi13) {
@@ -99,20 +77,6 @@ __device__ __forceinline__ void unpack_word(uint32_t x, uint32_t sclo, uint32_t 
     lo13 = pk_fma_f16(and_or(y, 0x000F000Fu, 0x64006400u), sclo, nblo);
     hi02 = pk_fma_f16(and_or(x, 0x00F000F0u, 0x64006400u), schi, nbhi);
     hi13 = pk_fma_f16(and_or(y, 0x00F000F0u, 0x64006400u), schi, nbhi);
-}
-
-// 4 int8 -> packed binary16 pairs [b0,b2], [b1,b3] (exact): byte ^ 0x80 =
-// q + 128, placed under exponent 0x64 gives 1152 + q, minus 1152.
-__device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13) {
-    const uint32_t z = y ^ 0x80808080u;
-    const uint32_t m1152 = 0xE480E480u;  // (-1152, -1152)
-    p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
-    p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
-}
-
-__device__ __forceinline__ uint32_t f16x2_splat(float v) {
-    const unsigned short h = __builtin_bit_cast(unsigned short, (_Float16)v);
-    return (uint32_t)h | ((uint32_t)h << 16);
 }
 
 // One stage of operands (128 k = 4 chunks) in LDS.  The q8 operands are an

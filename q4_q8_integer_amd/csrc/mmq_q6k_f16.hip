@@ -35,6 +35,7 @@
 // 210 bytes into LDS with aligned 16-byte loads (two raw areas alternate,
 // the next super-block's copied during the current one), and take every
 // field from there as aligned dwords shifted into place.
+#include "f16_operand.h"
 #include "internal.h"
 #include "kquant_device.h"
 #include "q6k_device.h"
@@ -54,42 +55,6 @@ constexpr int CS = 2;            // chunks per stage (64 k)
 // s_waitcnt operand: at most n vector-memory operations outstanding.
 // One (token tile, 128-k stage) block of the q8 operand tiles (bytes).
 constexpr int kQtBlockBytes = 16 * BN * 16;
-
-__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, a),
-                                                                   __builtin_bit_cast(h2, b),
-                                                                   __builtin_bit_cast(h2, c)));
-}
-
-__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) + __builtin_bit_cast(h2, b));
-}
-
-__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) * __builtin_bit_cast(h2, b));
-}
-
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
-    return r;
-}
-
-__device__ __forceinline__ uint32_t f16x2_splat(float v) {
-    const unsigned short h = __builtin_bit_cast(unsigned short, (_Float16)v);
-    return (uint32_t)h | ((uint32_t)h << 16);
-}
-
-// 4 int8 -> binary16 pairs [b0,b2], [b1,b3] (exact).
-__device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13) {
-    const uint32_t z = y ^ 0x80808080u;
-    const uint32_t m1152 = 0xE480E480u;  // (-1152, -1152)
-    p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
-    p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
-}
 
 // One stage (64 k = 2 chunks) of operands.  Slots of 8 halves laid out
 // [chunk][part][j][lane-half][row or token]: MFMA j of a chunk takes, in
