@@ -1,6 +1,7 @@
-// f16_operand.h - packed binary16 helpers of the binary16-MFMA kernels
-// (mmq_f16.hip, mmq_q6k_f16.hip): exact integer operands built from bit
-// patterns, two values per register.
+// f16_operand.h - shared pieces of the binary16-MFMA kernels (mmq_f16.hip,
+// mmq_q6k_f16.hip): packed binary16 helpers that build exact integer
+// operands from bit patterns, two values per register, and the
+// direct-to-LDS copy of operand-tile blocks.
 //
 //   * A nibble or small code n placed under the exponent bits 0x6400 is the
 //     binary16 value 1024 + n (the exponent's unit is 1 there), so
@@ -17,10 +18,6 @@
 #include <stdint.h>
 
 namespace mmq {
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
 
 __device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -59,5 +56,22 @@ __device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13
     p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
     p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
 }
+
+// One 16-byte direct-to-LDS copy per lane (buffer_load_dwordx4 ... lds):
+// lane i writes 16 bytes at LDS address lds + 16 i, from byte voff of the
+// buffer rsrc.  Inline asm, outside the compiler's wait bookkeeping: the
+// callers place the vmcnt waits that complete these copies themselves.
+// M0 is a reserved register; in the kernels using this nothing else sets or
+// reads it, so the clobber only tells the compiler what the asm does.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace mmq

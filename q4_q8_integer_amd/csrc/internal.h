@@ -43,6 +43,11 @@ struct OutElem<true> {
     typedef _Float16 T;
 };
 
+// The low 16 bits of h as a binary16 value, widened to float32 (exact).
+__device__ __forceinline__ float half_lo(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
 template <bool H>
 __device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
     reinterpret_cast<typename OutElem<H>::T*>(out)[i] = (typename OutElem<H>::T)v;

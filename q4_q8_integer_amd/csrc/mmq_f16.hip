@@ -244,8 +244,8 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, StageB& s
         // scale of the stage's chunk j, and all four write d (same value).
         // No branch here, so the loop body stays straight-line.
         {
-            const float d = half_bits_to_float(hdr.x);
-            const float dmin = half_bits_to_float(hdr.x >> 16);
+            const float d = half_lo(hdr.x);
+            const float dmin = half_lo(hdr.x >> 16);
             int sc, m;
             if (REP)
                 m = (hdr.y >> (16 + 8 * gg)) & 0xFF;   // chunk 4 hs + j = c0 + gg
@@ -273,7 +273,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, StageB& s
     for (int rr = 0; rr < SPC; ++rr) {
         const int i = pt + rr * PT;
         const int tok = i % TB, cl = i / TB;
-        const float da = half_bits_to_float(r.word[rr]);
+        const float da = half_lo(r.word[rr]);
         if (TB == BN || i < TB * 4) {
             sg.Da[cl][tok] = da;
             sg.Dass[cl][tok] = da * (float)(int16_t)(uint16_t)(r.word[rr] >> 16);  // exact
@@ -300,20 +300,6 @@ constexpr int stage_loads() { return WPC * (REP ? 3 : 2) + SPC + (QT ? 0 : APC);
 // are issued, and a vmcnt that leaves only the next stage's loads in flight
 // completes them before the barrier.  The compiler's own waits can then only
 // be stricter than needed, never looser.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// M0 is a reserved register; in these kernels nothing else sets or reads it
-// (the compiler's own direct-to-LDS and LDS-bounds uses are absent), so the
-// clobber only tells the compiler what the asm does.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // An empty asm that reads a stage's raw registers: the compiler completes
 // their loads here (nothing newer is in flight yet), so that no later use

@@ -63,10 +63,6 @@ constexpr int kStagedArea = 16 * kStagedRow;        // LDS bytes of one step's c
 // and across load instructions (40 -> 52 us at 7 tokens with it).
 constexpr int kStreamAux = 2;
 
-__device__ __forceinline__ float half_lo(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
 __device__ __forceinline__ v4u ld16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
 // repacked weight loads: non-temporal (kStreamAux)
 __device__ __forceinline__ v4u ld16w(const void* p) {

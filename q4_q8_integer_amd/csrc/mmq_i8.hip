@@ -42,10 +42,6 @@ constexpr int X_STRIDE = 272;      // LDS bytes per token row (256 q8 + pad)
 
 enum { kDots = 0, kFp32 = 1, kF16 = 2 };
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
 template <int EPI>
 __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ w,
                                                     const int8_t* __restrict__ q,
@@ -84,8 +80,8 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
                 w + ((int64_t)row * S + sb) * kBlockBytes + p * 16);
             *reinterpret_cast<uint4*>(sW + r * W_STRIDE + p * 16) = v;
             if (EPI != kDots && p == 0) {
-                const float d = half_bits_to_float(v.x);
-                const float dmin = half_bits_to_float(v.x >> 16);
+                const float d = half_lo(v.x);
+                const float dmin = half_lo(v.x >> 16);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     int sc, mn;
@@ -107,7 +103,7 @@ __global__ __launch_bounds__(NT) void mmq_i8_kernel(const uint8_t* __restrict__ 
                 const int t = i >> 3, j = i & 7;
                 const int tok = min(tok0 + t, N - 1);
                 const uint32_t word = ds[(int64_t)tok * C + sb * 8 + j];
-                const float da = half_bits_to_float(word);
+                const float da = half_lo(word);
                 const float ss = (float)(int16_t)(uint16_t)(word >> 16);
                 sXs[j][t] = make_float2(da, da * ss);  // exact: 11 x 13 significant bits
             }

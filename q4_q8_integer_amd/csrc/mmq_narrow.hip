@@ -83,10 +83,6 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t src, uint32_t
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ float half_lo(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
 // The value of x in lane 4*(lane/4) + v of the lane's quad.
 template <int V>
 __device__ __forceinline__ float quad_bcast(float x) {

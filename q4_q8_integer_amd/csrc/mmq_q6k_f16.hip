@@ -244,7 +244,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, St
     if (gi == 0 && kh == 0) {
         const int od = lo + 208;   // 2-aligned: d lies in the dword at od & ~3
         const uint32_t dw = *reinterpret_cast<const uint32_t*>(row_raw + (od & ~3)) >> (8 * (od & 3));
-        sg.D[row] = 64.0f * q6k::half_to_float(dw);
+        sg.D[row] = 64.0f * half_lo(dw);
     }
     // q8 piece: token pt & 127, k 16*(pt >> 7) .. +15 of the stage (QT: copied
     // by dma_stage instead)
@@ -258,7 +258,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, const Raw16& raw, St
         sgb.B[cc][0][kk][tok] = make_uint4(pp[0], pp[1], pp[2], pp[3]);
         sgb.B[cc][1][kk][tok] = make_uint4(pp[4], pp[5], pp[6], pp[7]);
     }
-    if (pt < 2 * BN) sg.Da[pt >> 7][pt & (BN - 1)] = q6k::half_to_float(r.word);
+    if (pt < 2 * BN) sg.Da[pt >> 7][pt & (BN - 1)] = half_lo(r.word);
 }
 
 // One stage for one consumer wave (64 rows x 32 tokens as 2 tiles of 32x32).
@@ -328,20 +328,6 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb,
 // in the q4_K kernel, the copies are inline asm outside the compiler's wait
 // bookkeeping, and the producer loop completes older loads before issuing
 // them and waits for everything before the stage barrier.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// M0 is a reserved register; in this kernel nothing else sets or reads it,
-// so the clobber only tells the compiler what the asm does.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 __device__ __forceinline__ void dma_stage(StageB& sb, const Src& p, int st, int pw, int lane) {
     const uint64_t a = reinterpret_cast<uint64_t>(p.qt + (int64_t)(st >> 1) * (kQtBlockBytes / 2));
     const u32x4 rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)kQtBlockBytes,

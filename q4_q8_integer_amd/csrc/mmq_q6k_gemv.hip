@@ -221,7 +221,7 @@ __device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, const uint8_
         lds_run(row_lds, off + 192, sc);
         const uint32_t dword = *reinterpret_cast<const uint32_t*>(row_lds + ((off + 208) & ~3));
         q6k::quarter_codes(ql0, ql1, qh, sh, cw);
-        const float d = s + j <= last ? q6k::half_to_float(dword >> (8 * sh)) : 0.0f;
+        const float d = s + j <= last ? half_lo(dword >> (8 * sh)) : 0.0f;
         // scales of groups 8h + 2g + e: byte 2(g & 1) + e of scale word 2h + (g >> 1)
         const uint32_t w0 = q6k::run_word(sc, 0, sh), w1 = q6k::run_word(sc, 1, sh);
         const uint32_t w2 = q6k::run_word(sc, 2, sh), w3 = q6k::run_word(sc, 3, sh);
@@ -238,7 +238,7 @@ __device__ __forceinline__ void compute_step(const Fetch<N, SW>& f, const uint8_
             group_dots(Df, f.tq[t][j], cw);
 #pragma unroll
             for (int g = 0; g < 4; ++g) y[g] = fmaf(dsc[g], Df[g], kn[g]);
-            fold4(acc[t], q6k::half_to_float(f.tw[t][j]), y);
+            fold4(acc[t], half_lo(f.tw[t][j]), y);
         }
     }
 }

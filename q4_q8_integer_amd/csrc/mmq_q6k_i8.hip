@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT, 2) void mmq_q6k_i8_kernel(const uint8_t* __rest
 #pragma unroll
                     for (int b = 0; b < 4; ++b) sSc[4 * j + b][r] = (short)(int8_t)(word >> (8 * b));
                 }
-                sD[r] = q6k::half_to_float(*reinterpret_cast<const uint16_t*>(w + B + 208));
+                sD[r] = half_lo(*reinterpret_cast<const uint16_t*>(w + B + 208));
             }
         }
         // ---- q8 tile: BN tokens x 16 x 16 B
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NT, 2) void mmq_q6k_i8_kernel(const uint8_t* __rest
             for (int i = tid; i < BN * 8; i += NT) {
                 const int t = i >> 3, j = i & 7;
                 const int tok = min(tok0 + t, N - 1);
-                sDa[j][t] = q6k::half_to_float(ds[(int64_t)tok * C + sb * 8 + j]);
+                sDa[j][t] = half_lo(ds[(int64_t)tok * C + sb * 8 + j]);
             }
         }
         __syncthreads();

@@ -46,10 +46,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int WAVES = 8;
 constexpr int NT = 64 * WAVES;
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
-}
-
 // LDS of a workgroup: the staging areas of the main loop, reused after it
 // for the partial sums of the 8 waves (reduced in a fixed order).
 template <int T, int RB>
@@ -139,7 +135,7 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t word = f.word[tt][h];
-                const float da = half_bits_to_float(word);
+                const float da = half_lo(word);
                 L.m.da[wv][kg + 4 * h][16 * tt + r] = da;
                 L.m.dass[wv][kg + 4 * h][16 * tt + r] = da * (float)(int16_t)(uint16_t)(word >> 16);
             }
@@ -208,7 +204,7 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float dmin = half_bits_to_float(f.hdr[rb].x >> 16);
+            const float dmin = half_lo(f.hdr[rb].x >> 16);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 int sc, mn;
@@ -219,7 +215,7 @@ __global__ __launch_bounds__(NT) void mmq_small_kernel(const uint8_t* __restrict
                     acc[rb][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(L.m.dass[wv][4 * j + kg][16 * tt + r], bneg,
                                                                        acc[rb][tt], 0, 0, 0);
             }
-            const float d = half_bits_to_float(f.hdr[rb].x);
+            const float d = half_lo(f.hdr[rb].x);
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
 #pragma unroll
@@ -418,7 +414,7 @@ __global__ __launch_bounds__(kFewNT) void mmq_few_kernel(const uint8_t* __restri
         for (int tt = 0; tt < T; ++tt)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const float da = half_bits_to_float(wd[tt][h]);
+                const float da = half_lo(wd[tt][h]);
                 my.da[kg + 4 * h][16 * tt + r] = da;
                 my.dass[kg + 4 * h][16 * tt + r] = da * (float)(int16_t)(uint16_t)(wd[tt][h] >> 16);
             }
@@ -468,7 +464,7 @@ __global__ __launch_bounds__(kFewNT) void mmq_few_kernel(const uint8_t* __restri
             }
         }
         // min term, 4 chunks per MFMA: A = da*ssum (token x chunk), B = -dmin*m (chunk x row)
-        const float dmin = half_bits_to_float(hdr.x >> 16);
+        const float dmin = half_lo(hdr.x >> 16);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             int sc, mn;
@@ -478,7 +474,7 @@ __global__ __launch_bounds__(kFewNT) void mmq_few_kernel(const uint8_t* __restri
             for (int tt = 0; tt < T; ++tt)
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(my.dass[4 * j + kg][16 * tt + r], bneg, acc[tt], 0, 0, 0);
         }
-        const float d = half_bits_to_float(hdr.x);
+        const float d = half_lo(hdr.x);
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
 #pragma unroll

@@ -75,9 +75,5 @@ __device__ __forceinline__ void quarter_codes(const uint32_t (&ql0)[5], const ui
     }
 }
 
-__device__ __forceinline__ float half_to_float(uint32_t bits) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
-}
-
 }  // namespace q6k
 }  // namespace mmq
