@@ -100,9 +100,12 @@ def build_workload(name: str):
 
 def kernel_choice(desc, f, n):
     """(format, kernel id) the library's own dispatch (mmq_kernel_choice)
-    runs for this call."""
+    runs for this call, or the kernel named with --kernel."""
     from q4_q8_integer_amd import binding, synth
     q6 = isinstance(f, synth.Q6KFields)
+    if desc.get("kernel"):
+        ids = {v: k for k, v in binding.KERNEL_NAMES.items()}
+        return (binding.FORMAT_Q6K if q6 else binding.FORMAT_Q4K), ids[desc["kernel"]]
     if desc.get("tiles"):
         fmt = binding.FORMAT_Q6K_TILES if q6 else (
             binding.FORMAT_Q4K_REPACKED_TILES if desc.get("repacked") else binding.FORMAT_Q4K_TILES)
@@ -334,6 +337,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--f16-out", action="store_true",
                     help="time the binary16-output entry point (mmq_*_f16out) instead of the float32 one")
+    ap.add_argument("--kernel", default=None,
+                    help="run the MMQ on this named kernel through the fold entry point "
+                         "(mmq_q4k_q8_fold / mmq_q6k_q8_fold: dot4, narrow, few, f16 or i8) instead "
+                         "of the library's own choice; GGUF-layout, int8-code workloads only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (known bytes) so that "
                          "profiler byte counters can be calibrated against it")
@@ -393,6 +400,12 @@ def measure(args, workload):
     from q4_q8_integer_amd import binding, synth
 
     desc, inputs, mats = build_workload(workload)
+    if getattr(args, "kernel", None):
+        if desc.get("repacked") or desc.get("tiles"):
+            raise SystemExit("--kernel applies to GGUF-layout workloads with int8 codes")
+        if args.kernel not in binding.KERNEL_NAMES.values():
+            raise SystemExit("--kernel: one of %s" % ", ".join(sorted(binding.KERNEL_NAMES.values())))
+        desc = dict(desc, kernel=args.kernel)
     dev = torch.device("cuda:0")
     binding.load_library()
 
@@ -440,6 +453,14 @@ def measure(args, workload):
     calls = [getattr(binding, names[0] if desc.get("repacked") or desc.get("tiles")
                      else weight_format(f)[2] + suffix)
              for _, f, _ in mats]
+    if desc.get("kernel"):   # the named kernel through the fold entry point
+        kid = {v: k for k, v in binding.KERNEL_NAMES.items()}[desc["kernel"]]
+
+        def named(fold):
+            return lambda w, m, k, q, ds, n, out: fold(w, m, k, q, ds, kid, f16=args.f16_out, out=out)
+        calls = [named(binding.q6k_fold_kernel if isinstance(f, synth.Q6KFields) else binding.fold_kernel)
+                 for _, f, _ in mats]
+        mmq_name = "+".join(sorted({weight_format(f)[2] + "_fold" for _, f, _ in mats})) + ":" + desc["kernel"]
     quantize = binding.q8_quantize_rows_tiled if desc.get("tiles") else binding.q8_quantize_rows
     quantize_name = "q8_quantize_rows_tiled" if desc.get("tiles") else "q8_quantize_rows"
 
