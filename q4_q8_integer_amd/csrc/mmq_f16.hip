@@ -173,10 +173,12 @@ __device__ __forceinline__ void init_src(Src& p, const uint8_t* __restrict__ w,
     }
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr) {
-        // with TB < BN only the first TB * 4 producer threads hold a word
-        // (the others re-read the last one and store nothing)
+        // thread i loads chunk i & 3 of token i >> 2, so that the four lanes
+        // of a token read one 16-byte run (one cache line per 16 lanes rather
+        // than per lane); with TB < BN only the first TB * 4 producer threads
+        // hold a word (the others re-read the last one and store nothing)
         const int i = TB == BN ? pt + rr * PT : min(pt + rr * PT, TB * 4 - 1);
-        const int tok = i % TB, cl = i / TB;
+        const int tok = i >> 2, cl = i & 3;
         p.word[rr] = (min(tok, toks - 1) * C + cl) * 4;
     }
 }
@@ -272,7 +274,7 @@ __device__ __forceinline__ void convert_stage(const Raw& r, Stage& sg, StageB& s
 #pragma unroll
     for (int rr = 0; rr < SPC; ++rr) {
         const int i = pt + rr * PT;
-        const int tok = i % TB, cl = i / TB;
+        const int tok = i >> 2, cl = i & 3;
         const float da = half_lo(r.word[rr]);
         if (TB == BN || i < TB * 4) {
             sg.Da[cl][tok] = da;
@@ -430,7 +432,8 @@ constexpr int kGroup = 256;
 // binary16 operand slots, or with QT copy the tile block straight into LDS).
 // Two LDS stages alternate: while the consumers
 // work on stage s, the producers fill stage s+1 (their global loads run one
-// stage further ahead, in registers).  One workgroup barrier per stage.
+// stage further ahead in registers, two with int8 codes).  One workgroup
+// barrier per stage.
 template <int TB, bool H, bool REP, bool QT, bool BIG>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
@@ -447,39 +450,69 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 
     if (tid >= CT) {
         // ------------------------------------------------------- producer
-        // Two raw register sets alternate, so the loads for stage s+1 stay in
-        // flight while stage s is converted (a register copy would force a
-        // wait on them).
+        // Raw register sets rotate, so that the loads of later stages stay
+        // in flight while stage s is converted (a register copy would force a
+        // wait on them).  k is a multiple of 256, so the stage count is even.
+        // Every load is unconditional (prefetches past the end re-read the
+        // final stage), which lets the compiler wait only for the oldest set.
         const int pt = tid - CT;
         Src src;
         init_src<TB, REP, QT>(src, w, q, ds, pt, row0, tok0, M, N, K);
-        const int pw = __builtin_amdgcn_readfirstlane(pt >> 6), lane = pt & 63;
         Raw ra, rb;
-        load_stage<TB, REP, QT>(ra, src, 0);
-        // k is a multiple of 256, so the stage count is even and the loop
-        // runs whole (even, odd) pairs.  Every load is unconditional (the
-        // last prefetch re-reads the final stage), which lets the compiler
-        // wait only for the older register set.
-        for (int it = 0; it < stages; it += 2) {
-            // QT: everything older completes first (loads issued a half-step
+        if constexpr (!QT) {
+            // Three sets: loads run two stages ahead of the conversion (the
+            // loads, not the conversions, bound the producers with one stage
+            // of prefetch: measured 151 -> 132 us for the producers alone on
+            // q-proj, 4-7% for the whole kernel; a fourth set gained
+            // nothing).  Stage s uses set s % 3 and LDS stage s % 2, so the
+            // loop body covers 6 stages.
+            Raw rc;
+            load_stage<TB, REP, QT>(ra, src, 0);
+            load_stage<TB, REP, QT>(rb, src, min(1, stages - 1));
+            for (int it = 0; it < stages; it += 6) {
+                load_stage<TB, REP, QT>(rc, src, min(it + 2, stages - 1));
+                convert_stage<TB, REP, QT>(ra, stage[0], stage_b[0], pt, it);
+                __syncthreads();
+                load_stage<TB, REP, QT>(ra, src, min(it + 3, stages - 1));
+                convert_stage<TB, REP, QT>(rb, stage[1], stage_b[1], pt, it + 1);
+                __syncthreads();
+                if (it + 2 >= stages) break;
+                load_stage<TB, REP, QT>(rb, src, min(it + 4, stages - 1));
+                convert_stage<TB, REP, QT>(rc, stage[0], stage_b[0], pt, it + 2);
+                __syncthreads();
+                load_stage<TB, REP, QT>(rc, src, min(it + 5, stages - 1));
+                convert_stage<TB, REP, QT>(ra, stage[1], stage_b[1], pt, it + 3);
+                __syncthreads();
+                if (it + 4 >= stages) break;
+                load_stage<TB, REP, QT>(ra, src, min(it + 6, stages - 1));
+                convert_stage<TB, REP, QT>(rb, stage[0], stage_b[0], pt, it + 4);
+                __syncthreads();
+                load_stage<TB, REP, QT>(rb, src, min(it + 7, stages - 1));
+                convert_stage<TB, REP, QT>(rc, stage[1], stage_b[1], pt, it + 5);
+                __syncthreads();
+            }
+        } else {
+            // Operand tiles: two sets (the weights only; the q8 operands are
+            // direct-to-LDS copies whose waits the loop places itself).
+            // Everything older completes first (loads issued a half-step
             // ago), then the stage's q8 copies, so that waiting for them
             // before the barrier leaves only the next stage's loads in flight.
-            if (QT) {
+            const int pw = __builtin_amdgcn_readfirstlane(pt >> 6), lane = pt & 63;
+            load_stage<TB, REP, QT>(ra, src, 0);
+            for (int it = 0; it < stages; it += 2) {
                 settle<REP>(ra);
                 dma_stage<TB>(stage_b[0], src, it, pw, lane);
-            }
-            load_stage<TB, REP, QT>(rb, src, it + 1);
-            convert_stage<TB, REP, QT>(ra, stage[0], stage_b[0], pt, it);
-            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
-            __syncthreads();
-            if (QT) {
+                load_stage<TB, REP, QT>(rb, src, it + 1);
+                convert_stage<TB, REP, QT>(ra, stage[0], stage_b[0], pt, it);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
+                __syncthreads();
                 settle<REP>(rb);
                 dma_stage<TB>(stage_b[1], src, it + 1, pw, lane);
+                load_stage<TB, REP, QT>(ra, src, min(it + 2, stages - 1));
+                convert_stage<TB, REP, QT>(rb, stage[1], stage_b[1], pt, it + 1);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
+                __syncthreads();
             }
-            load_stage<TB, REP, QT>(ra, src, min(it + 2, stages - 1));
-            convert_stage<TB, REP, QT>(rb, stage[1], stage_b[1], pt, it + 1);
-            if (QT) __builtin_amdgcn_s_waitcnt(kWaitVmcnt(stage_loads<REP, QT>()));
-            __syncthreads();
         }
         __syncthreads();  // the consumers' last stage
         return;
