@@ -91,8 +91,11 @@ struct Stage {
     uint4 A[CS][2][2][BM];   // sc*q4 binary16 operand slots [chunk][k-half][lane-half][row]
     float D[BM];             // d of the stage's super-block
     float CA[CS][BM];        // -dmin*m per (chunk, row)
-    float Da[CS][BN];        // da per (chunk, token)
-    float Dass[CS][BN];      // da*ssum per (chunk, token)
+    // da and da*ssum per (chunk, token).  Rows padded by 8 floats: the
+    // producers store a token's 4 chunks from 4 neighbouring lanes, which
+    // rows 128 floats apart would put in one bank.
+    float Da[CS][BN + 8];
+    float Dass[CS][BN + 8];
 };
 
 // Raw global data of one stage, as one producer thread loads it.
