@@ -350,6 +350,24 @@ __device__ __forceinline__ void dma_stage(StageB& sb, const Src& p, int st, int 
 template <int HS, int RT>
 __device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb, int wm, int wn, int g, int l32,
                                               v16f (&acc)[2][NTW], v16f (&accb)[2][NTW]) {
+    // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA.  First in
+    // the stage: its scalar operands arrive quickly, and its MFMAs cover the
+    // LDS latency of the first chunk's operand reads, which every consumer
+    // wave issues at once after the stage barrier (acc sees the same updates
+    // in the same order as with the min term last).
+#pragma unroll
+    for (int cp = 0; cp < CS / 2; ++cp) {
+        float ca[2], cb[NTW];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 32 * RT + rt * 32 + l32];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 32 * NTW + nt * 32 + l32];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+                acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
+    }
 #pragma unroll
     for (int cl = 0; cl < CS; ++cl) {
         v8h a0[2], a1[2], b0[NTW], b1[NTW];
@@ -390,20 +408,6 @@ __device__ __forceinline__ void consume_stage(const Stage& sg, const StageB& sb,
                     for (int v = 0; v < 16; ++v)
                         accb[rt][nt][v] = fmaf(da[nt], pr[rt][nt][v], accb[rt][nt][v]);
             }
-    }
-    // min term: out += (-dmin*m) x (da*ssum), two chunks per MFMA
-#pragma unroll
-    for (int cp = 0; cp < CS / 2; ++cp) {
-        float ca[2], cb[NTW];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) ca[rt] = sg.CA[2 * cp + g][wm * 32 * RT + rt * 32 + l32];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) cb[nt] = sg.Dass[2 * cp + g][wn * 32 * NTW + nt * 32 + l32];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                acc[rt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[rt], cb[nt], acc[rt][nt], 0, 0, 0);
     }
     // end of a super-block: out += d * acc_b
     if (HS == 1) {
