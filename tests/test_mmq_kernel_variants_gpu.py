@@ -20,7 +20,10 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = {
     binding.KERNEL_I8: [(64, 256, 512), (77, 200, 768), (130, 129, 512), (5, 131, 2304)],
-    binding.KERNEL_F16: [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304)],
+    # k = 256 .. 2304: the producers' three-set loop leaves after 2, 4, 6 (whole), 10 and 18
+    # (whole) stages of 128 k
+    binding.KERNEL_F16: [(1, 256, 512), (7, 200, 768), (33, 129, 512), (64, 131, 2304), (65, 130, 256),
+                         (80, 96, 1280)],
     binding.KERNEL_FEW: [(1, 1, 256), (7, 31, 1280), (16, 17, 2304), (17, 200, 768), (48, 129, 512),
                          (64, 256, 11008)],
     binding.KERNEL_DOT4: [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
