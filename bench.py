@@ -265,8 +265,10 @@ def run_silu_q8(args):
     rounds = max(args.steps, 10)
 
     def event_time(fn):
+        # behind untimed rounds of the same work, as for the MMQ below
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(50_000_000)
+        for i in range(rounds):
+            fn(i)
         e0.record(stream)
         for i in range(rounds):
             fn(i)
@@ -329,7 +331,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the GPU reaches its working clocks over some tens of ms)")
     ap.add_argument("--workload", default=None,
                     help="default: %s, with %s and the fastest path (%s) measured beside it"
                          % (DEFAULT_WORKLOAD, ", ".join(BESIDE), FASTEST))
@@ -484,18 +487,26 @@ def measure(args, workload):
 
     # Duration of the dominant kernel (the MMQ entry point) with HIP events on
     # the stream it runs on: R rounds of every projection's MMQ, back to back,
-    # behind a GPU spin long enough for the host to enqueue them all, so that
-    # host launch latency is not counted.
+    # enqueued behind R untimed rounds of the same launches.  The GPU stays
+    # busy at its working clocks (a spin on one wave before the events let
+    # the clocks fall, and the timed launches then ran slower than in the
+    # steps), and the host, which enqueues a launch faster than the GPU runs
+    # one, stays ahead of the events, so host launch latency is not counted.
     rounds = max(args.steps, 10)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(50_000_000)
-    e0.record(stream)
-    for i in range(rounds):
+
+    def mmq_round(i):
         xs, ws, qs, outs = sets[i % len(sets)]
         for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
             q, ds = qs[src]
             mmq(w, m, k, q, ds, ds.shape[0], out)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(rounds):
+        mmq_round(i)
+    e0.record(stream)
+    for i in range(rounds):
+        mmq_round(i)
     e1.record(stream)
     torch.cuda.synchronize()
     mmq_ms = e0.elapsed_time(e1) / rounds          # all projections of one step
