@@ -21,6 +21,7 @@ line (see the keys in ``main``).
 from __future__ import annotations
 
 import argparse
+import math
 import json
 import os
 import sys
@@ -135,6 +136,26 @@ def kernel_source(desc, f, n):
               binding.KERNEL_FEW: "mmq_small.hip", binding.KERNEL_F16: "mmq_f16.hip",
               binding.KERNEL_I8: "mmq_i8.hip"})
     return "q4_q8_integer_amd/csrc/" + names[kid]
+
+
+def raw_call(name, args):
+    """The C-ABI entry point `name` with its arguments marshalled once (tensors
+    to device pointers, the current stream appended): a callable that repeats
+    the call with no per-call Python work, for the event-timed loop, where the
+    host must enqueue launches faster than the GPU runs them.  The arguments
+    were checked by the binding's own wrapper in the timed steps before."""
+    import ctypes
+    import torch
+    from q4_q8_integer_amd import binding
+    fn = getattr(binding.load_library(), name)
+    cargs = tuple(ctypes.c_void_p(a.data_ptr()) if isinstance(a, torch.Tensor) else a for a in args)
+    cargs += (ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),)
+
+    def call():
+        status = fn(*cargs)
+        if status != 0:
+            raise RuntimeError("%s: %s" % (name, binding.status_string(status)))
+    return call
 
 
 def weight_format(f):
@@ -262,7 +283,8 @@ def run_silu_q8(args):
     wall = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
-    rounds = max(args.steps, 10)
+    # about 25 ms of GPU time each way, as for the MMQ below
+    rounds = int(min(4000, max(args.steps, 10, math.ceil(25.0 / max(wall * 1e3 / args.steps, 1e-3)))))
 
     def event_time(fn):
         # behind untimed rounds of the same work, as for the MMQ below
@@ -456,8 +478,13 @@ def measure(args, workload):
     calls = [getattr(binding, names[0] if desc.get("repacked") or desc.get("tiles")
                      else weight_format(f)[2] + suffix)
              for _, f, _ in mats]
+    raw_names = [names[0] if desc.get("repacked") or desc.get("tiles") else weight_format(f)[2] + suffix
+                 for _, f, _ in mats]
+    raw_extra = [() for _ in mats]
     if desc.get("kernel"):   # the named kernel through the fold entry point
         kid = {v: k for k, v in binding.KERNEL_NAMES.items()}[desc["kernel"]]
+        raw_names = [weight_format(f)[2] + "_fold" for _, f, _ in mats]
+        raw_extra = [(int(args.f16_out), kid) for _ in mats]
 
         def named(fold):
             return lambda w, m, k, q, ds, n, out: fold(w, m, k, q, ds, kid, f16=args.f16_out, out=out)
@@ -487,19 +514,25 @@ def measure(args, workload):
 
     # Duration of the dominant kernel (the MMQ entry point) with HIP events on
     # the stream it runs on: R rounds of every projection's MMQ, back to back,
-    # enqueued behind R untimed rounds of the same launches.  The GPU stays
-    # busy at its working clocks (a spin on one wave before the events let
-    # the clocks fall, and the timed launches then ran slower than in the
-    # steps), and the host, which enqueues a launch faster than the GPU runs
-    # one, stays ahead of the events, so host launch latency is not counted.
-    rounds = max(args.steps, 10)
+    # enqueued behind R untimed rounds of the same launches, R sized to about
+    # 25 ms of GPU time each way.  The clocks settle over some 10-20 ms of
+    # sustained load after an idle gap (a one-wave spin before the events, or
+    # too few rounds, measured the ramp: q-proj 206-209 us per launch over
+    # 20 rounds after a spin, 175-177 us after 200 warm rounds).  The calls
+    # are marshalled once, so the host enqueues a launch faster than the GPU
+    # runs one and host launch latency is not counted.
+    ms_step = wall * 1e3 / args.steps
+    rounds = int(min(4000, max(args.steps, 10, math.ceil(25.0 / max(ms_step, 1e-3)))))
     stream = torch.cuda.current_stream()
 
+    raw = []
+    for xs, ws, qs, outs in sets:
+        raw.append([raw_call(nm, (w, m, k, qs[src][0], qs[src][1], qs[src][1].shape[0], out) + ex)
+                    for (lbl, w, m, k, src), out, nm, ex in zip(ws, outs, raw_names, raw_extra)])
+
     def mmq_round(i):
-        xs, ws, qs, outs = sets[i % len(sets)]
-        for (lbl, w, m, k, src), out, mmq in zip(ws, outs, calls):
-            q, ds = qs[src]
-            mmq(w, m, k, q, ds, ds.shape[0], out)
+        for call in raw[i % len(raw)]:
+            call()
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(rounds):
@@ -511,7 +544,6 @@ def measure(args, workload):
     torch.cuda.synchronize()
     mmq_ms = e0.elapsed_time(e1) / rounds          # all projections of one step
 
-    ms_step = wall * 1e3 / args.steps
     value = mmq_ops / (ms_step * 1e-3) / 1e12
     achieved_tops = mmq_ops / (mmq_ms * 1e-3) / 1e12
     alg_gbs = mmq_alg_bytes / (mmq_ms * 1e-3) / 1e9
