@@ -184,13 +184,22 @@ def measured_traffic(key: str, src: str):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    """The host CPU's model name (lscpu, else /proc/cpuinfo), with the CPU
+    family, model and the cores lscpu reports (virtual machines often give
+    only a generic name)."""
     import subprocess
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = {}
         for line in out.splitlines():
-            if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = line.split(":", 1)
+                f[key.strip()] = val.strip()
+        if "Model name" in f:
+            extra = ", ".join("%s %s" % (lbl, f[key]) for key, lbl in
+                              (("CPU family", "family"), ("Model", "model"), ("Core(s) per socket", "cores/socket"),
+                               ("Socket(s)", "sockets"), ("Thread(s) per core", "threads/core")) if key in f)
+            return "%s (%s)" % (f["Model name"], extra) if extra else f["Model name"]
     except (OSError, subprocess.SubprocessError):
         pass
     try:
