@@ -9,8 +9,10 @@
 //     values in one instruction; a fused multiply-add with exact constants
 //     then removes the 1024 and applies a scale, rounding nothing when the
 //     result is an integer (or a multiple of a power of two) below 2048.
-//   * An int8 code q: byte ^ 0x80 = q + 128, under 0x64 that is 1152 + q,
-//     minus 1152.
+//   * An int8 code q: the vector unit's sub-dword operand select picks one
+//     byte, sign-extends it and converts it to binary16 (exact, |q| <= 128),
+//     writing either half of the destination and keeping the other, so four
+//     codes become two pairs in four instructions.
 //   * Pairs are (byte 0, byte 2) and (byte 1, byte 3) of a dword, on the
 //     weight side and the activation side alike, so both sides agree on k.
 #pragma once
@@ -51,10 +53,14 @@ __device__ __forceinline__ uint32_t f16x2_splat(float v) {
 
 // 4 int8 codes -> binary16 pairs [b0, b2], [b1, b3], exactly.
 __device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13) {
-    const uint32_t z = y ^ 0x80808080u;
-    const uint32_t m1152 = 0xE480E480u;  // (-1152, -1152)
-    p02 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04020400u), m1152);
-    p13 = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, z, 0x04030401u), m1152);
+    uint32_t a, b;
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2"
+        : "=&v"(a) : "v"(y));
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "=&v"(b) : "v"(y));
+    p02 = a; p13 = b;
 }
 
 // One 16-byte direct-to-LDS copy per lane (buffer_load_dwordx4 ... lds):
