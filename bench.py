@@ -167,18 +167,44 @@ def weight_format(f):
     return synth.pack_q4k, 144.0 / 256.0, "mmq_q4k_q8", "out_f64"
 
 
+def source_digest(src: str) -> str:
+    """sha256 prefix (16 hex digits) over a kernel source file and, depth
+    first in include order, every local header it includes with
+    `#include "..."`, each file once: a change in a shared header changes
+    the digest of every source that includes it."""
+    import hashlib
+    import re
+    files = []
+
+    def walk(path):
+        path = os.path.normpath(path)
+        if path in files:
+            return
+        files.append(path)
+        for line in open(path, encoding="utf-8", errors="replace"):
+            m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+            if m:
+                walk(os.path.join(os.path.dirname(path), m.group(1)))
+
+    walk(os.path.join(ROOT, src))
+    h = hashlib.sha256()
+    for path in files:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(key: str, src: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record (profiles/traffic.txt), already scaled by the copy-probe factors;
     None unless the record was taken on the kernel the library runs now
-    (src, its csrc file) with that source as it is now."""
-    import hashlib
+    (src, its csrc file) with that source and the headers it includes as
+    they are now (source_digest)."""
     try:
         rec = json.loads(open(os.path.join(ROOT, "profiles", "traffic.txt")).read())[key]
-        sha = hashlib.sha256(open(os.path.join(ROOT, rec["src"]), "rb").read()).hexdigest()[:16]
+        digest = source_digest(rec["src"])
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("src") != src or rec.get("sha256_16") != sha:
+    if rec.get("src") != src or rec.get("sha256_16") != digest:
         return None
     return int(rec["read_bytes"] + rec["write_bytes"])
 
