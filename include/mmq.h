@@ -150,12 +150,12 @@ int mmq_q4k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
  * chip, and each meets the same accuracy bar on every shape it accepts.
  */
 enum mmq_kernel {
-    MMQ_KERNEL_AUTO = 0,  /* the entry point's own choice, by m and n (mmq_kernel_choice) */
+    MMQ_KERNEL_AUTO = 0,  /* the entry point's own choice, by m, k and n (mmq_kernel_choice) */
     MMQ_KERNEL_DOT4 = 1,  /* vector-ALU 4-way int8 dots, weights streamed once; n <= 8 */
     MMQ_KERNEL_FEW = 2,   /* int8 MFMA on 16-token tiles, weights streamed once; n <= 64 (q4_K) */
     MMQ_KERNEL_F16 = 3,   /* binary16 MFMA on exact sc*q4 and q8 operands, 128-row tiles; any n */
     MMQ_KERNEL_I8 = 4,    /* int8 MFMA on 128 x 128 tiles with a three-operation fold; any n */
-    MMQ_KERNEL_NARROW = 5 /* int8 4x4x4 MFMA, one weight row per lane, weights streamed once; n <= 8 */
+    MMQ_KERNEL_NARROW = 5 /* int8 4x4x4 MFMA, weights staged through LDS, streamed once; n <= 16 */
 };
 
 /*
@@ -163,7 +163,7 @@ enum mmq_kernel {
  * (out_f16 != 0) on a kernel the caller names, for comparisons, benchmarks
  * and validation of every kernel on any shape.  With MMQ_KERNEL_AUTO it is
  * exactly that entry point.  A kernel outside its token range (DOT4 above 8
- * tokens, NARROW above 8, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
+ * tokens, NARROW above 16, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
  * HIP call; other arguments, errors and empty calls as for
  * mmq_q4k_q8_fp32out.
  */

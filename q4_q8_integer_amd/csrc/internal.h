@@ -110,11 +110,22 @@ hipError_t launch_mmq_fp32_gemv_repacked(const uint8_t* wr, int m, int k, const 
 constexpr int kSmallMaxN = 64;
 
 // Two-term fold, out[t][o], for 1 <= n <= kNarrowMaxN tokens: 4x4x4 int8
-// MFMA with one weight row and super-block per lane (mmq_narrow.hip).
+// MFMA on weights and tokens staged through LDS, one (row, super-block,
+// chunk half) per lane (mmq_narrow.hip).
 hipError_t launch_mmq_fp32_narrow(const uint8_t* w, int m, int k, const int8_t* q,
                                   const uint32_t* ds, int n, void* out, bool half_out,
                                   hipStream_t stream);
-constexpr int kNarrowMaxN = 8;
+constexpr int kNarrowMaxN = 16;
+
+// The narrow kernel's layout for an m x k weight: 32-row tiles where they
+// fill the 256 CUs (at least 256 tiles) with at least 8 super-blocks per
+// wave, run by 4 waves per workgroup from 512 tiles on (two workgroups per
+// CU) and by 8 below; the return value is that wave count, or 0 for 16-row
+// tiles.
+inline int narrow_waves32(int64_t m, int64_t k) {
+    const int64_t tiles = (m + 31) / 32, w = tiles >= 512 ? 4 : 8;
+    return tiles >= 256 && (k >> 8) >= 8 * w ? (int)w : 0;
+}
 
 // q6_K weights (210-byte super-blocks, one int8 scale per 16 weights).
 // Exact int32 group dots, dots[t][o][g] (g = k/16 groups).

@@ -65,11 +65,16 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 
 // Kernel behind the q4_K fold entry points for MMQ_KERNEL_AUTO, by token
 // count (measured on the 28672 x 8192 and 8192 x 28672 matrices):
-//   n <= 6:   the vector-ALU dot4 kernel (at 2-6 tokens 25-37 us against
-//             30-37 us for the narrow kernel);
-//   n <= 8:   the narrow 4x4x4 int8-MFMA kernel (at 7 / 8 tokens 39.1 / 39.0
-//             us against 39.6 / 42.7 us for dot4 on 28672 x 8192, 38.0 /
-//             38.4 against 39.2 / 41.6 on 8192 x 28672);
+//   n <= 5:   the vector-ALU dot4 kernel (at 5 tokens 30.0 / 31.2 us against
+//             34.8 / 30.7 us for the narrow kernel);
+//   n <= 8:   the narrow 4x4x4 int8-MFMA kernel (at 6 tokens 35.1 / 31.2 us
+//             against 36.1 / 32.7 for dot4; at 7 / 8 tokens 36.5 / 32 us
+//             against 38.6-40 / 38-42 us for dot4);
+//   n <= 16:  the narrow kernel where its 32-row tiles give each wave at
+//             least 12 super-blocks (8192 x 28672 at 9 / 12 / 16 tokens
+//             36.7 / 37.1 / 43.5 us against 45.1 / 45.5 / 47.1 us for the
+//             few-token kernel; with 8 super-blocks per wave, on 28672 x
+//             8192, the two are level or the few-token kernel leads);
 //   n <= 32:  the few-token int8-MFMA kernels (one 16-token tile up to
 //             16 tokens, two tiles up to 32: 74-77 us against 87-89 us for
 //             the binary16 kernel on 28672 x 8192);
@@ -78,13 +83,16 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 //             rows at 33 / 48 tokens 90.7 / 92.5 us against 97 / 101.5 us;
 //             with 64 tiles, on 8192 rows, it is three times slower);
 //   n > 64:   the binary16-MFMA kernel.
-int q4k_auto_kernel(int64_t m, int64_t n) {
+int q4k_auto_kernel(int64_t m, int64_t k, int64_t n) {
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    return n <= 6                                     ? MMQ_KERNEL_DOT4
-           : n <= mmq::kNarrowMaxN                    ? MMQ_KERNEL_NARROW
-           : n <= 32                                  ? MMQ_KERNEL_FEW
-           : n <= mmq::kSmallMaxN && f16_tiles < 160  ? MMQ_KERNEL_FEW
-                                                      : MMQ_KERNEL_F16;
+    const int w32 = mmq::narrow_waves32(m, k);
+    const bool narrow_long = w32 > 0 && (k >> 8) / w32 >= 12;
+    return n <= 5                                      ? MMQ_KERNEL_DOT4
+           : n <= 8                                    ? MMQ_KERNEL_NARROW
+           : n <= mmq::kNarrowMaxN && narrow_long      ? MMQ_KERNEL_NARROW
+           : n <= 32                                   ? MMQ_KERNEL_FEW
+           : n <= mmq::kSmallMaxN && f16_tiles < 160   ? MMQ_KERNEL_FEW
+                                                       : MMQ_KERNEL_F16;
 }
 
 // The repacked-weight entry: above 16 tokens the binary16-MFMA kernel on the
@@ -99,8 +107,8 @@ int q4kr_auto_kernel(int64_t m, int64_t n) {
 }
 
 // The launcher of a q4_K fold kernel choice, and whether its grid fits.
-int q4k_fold_launcher(int kernel, int64_t m, int64_t n, FoldLaunch* f) {
-    if (kernel == MMQ_KERNEL_AUTO) kernel = q4k_auto_kernel(m, n);
+int q4k_fold_launcher(int kernel, int64_t m, int64_t k, int64_t n, FoldLaunch* f) {
+    if (kernel == MMQ_KERNEL_AUTO) kernel = q4k_auto_kernel(m, k, n);
     switch (kernel) {
         case MMQ_KERNEL_DOT4:
             if (n > mmq::kGemvMaxN) return MMQ_ERR_KERNEL;
@@ -141,7 +149,7 @@ int fold_entry(const void* w, int64_t m, int64_t k, const int8_t* q, const uint3
     if (!ds) return MMQ_ERR_NULL;
     if (!aligned16(ds)) return MMQ_ERR_ALIGN;
     FoldLaunch launch = nullptr;
-    rc = q4k_fold_launcher(kernel, m, n, &launch);
+    rc = q4k_fold_launcher(kernel, m, k, n, &launch);
     if (rc != MMQ_OK) return rc;
     rc = check_device();
     if (rc != MMQ_OK) return rc;
@@ -325,7 +333,7 @@ int mmq_q6k_q8_fold(const void* w, int64_t m, int64_t k, const int8_t* q, const 
 int mmq_kernel_choice(int format, int64_t m, int64_t k, int64_t n) {
     if (n < 0 || m < 0 || k <= 0 || (k & 255) != 0) return MMQ_ERR_SHAPE;
     switch (format) {
-        case MMQ_FORMAT_Q4K: return q4k_auto_kernel(m, n);
+        case MMQ_FORMAT_Q4K: return q4k_auto_kernel(m, k, n);
         case MMQ_FORMAT_Q4K_REPACKED: return q4kr_auto_kernel(m, n);
         case MMQ_FORMAT_Q6K: return q6k_auto_kernel(n);
         case MMQ_FORMAT_Q4K_TILES:

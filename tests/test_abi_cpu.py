@@ -217,10 +217,10 @@ def test_fold_kernel_validation(lib, fn, args, want):
 
 def test_fold_kernel_token_ranges(lib):
     # the few-token MFMA kernel takes at most 64 tokens, the narrow kernel at
-    # most 8, and neither has a q6_K form
+    # most 16, and neither has a q6_K form
     assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 65, A, 0, K_FEW, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_FEW, None) == KERNEL
-    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 9, A, 0, K_NARROW, None) == KERNEL
+    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 17, A, 0, K_NARROW, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_NARROW, None) == KERNEL
 
 
@@ -263,7 +263,7 @@ def test_grid_limits_are_overflow_errors(lib):
 
 
 @pytest.mark.parametrize("m,n,want", [
-    (4096, 1, K_DOT4), (4096, 6, K_DOT4), (4096, 7, K_NARROW), (4096, 8, K_NARROW), (4096, 9, K_FEW),
+    (4096, 1, K_DOT4), (4096, 5, K_DOT4), (4096, 6, K_NARROW), (4096, 8, K_NARROW), (4096, 9, K_FEW),
     (28672, 32, K_FEW),
     (28672, 33, K_F16),            # 224 x 1 tiles of 128 x 128: enough for the chip
     (20480, 33, K_F16),            # 160 tiles: the threshold
@@ -272,6 +272,22 @@ def test_grid_limits_are_overflow_errors(lib):
 ])
 def test_kernel_choice_q4k(lib, m, n, want):
     assert lib.mmq_kernel_choice(0, m, 4096, n) == want
+
+
+@pytest.mark.parametrize("m,k,n,want", [
+    # 9-16 tokens: the narrow kernel where its 32-row tiles (at least 256 of
+    # them, 4 waves each from 512 on, else 8) give each wave at least 12
+    # super-blocks of 256
+    (8192, 28672, 9, K_NARROW), (8192, 28672, 16, K_NARROW), (8192, 28672, 17, K_FEW),
+    (8160, 28672, 12, K_FEW),       # 255 tiles of 32 rows
+    (28672, 8192, 7, K_NARROW), (28672, 8192, 9, K_FEW),   # 4 waves x 8 super-blocks
+    (16384, 16384, 16, K_NARROW),   # 512 tiles: 4 waves x 16 super-blocks
+    (8192, 8192, 12, K_FEW),        # 256 tiles but 8 waves x 4 super-blocks
+    (8192, 24576, 12, K_NARROW),    # 8 waves x 12
+    (8192, 22528, 12, K_FEW),       # 8 waves x 11
+])
+def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
+    assert lib.mmq_kernel_choice(0, m, k, n) == want
 
 
 @pytest.mark.parametrize("m,n,want", [

@@ -4,8 +4,8 @@ three-operation fold, kept for comparison), f16 (the binary16-MFMA kernel,
 default above 64 tokens and from 33 where the matrix gives it enough tiles,
 here also on few tokens), few (the few-token int8-MFMA kernels, one tile up
 to 16 tokens and more above, default from 9 tokens, here also on fewer),
-dot4 (the vector-ALU kernel, default up to 6 tokens) and narrow (the 4x4x4
-int8-MFMA kernel with one weight row per lane, up to 8 tokens).  Each kernel's binary16
+dot4 (the vector-ALU kernel, default up to 5 tokens) and narrow (the 4x4x4
+int8-MFMA kernel on LDS-staged weights, up to 16 tokens, default from 6).  Each kernel's binary16
 output must equal its float32 output rounded to nearest-even, bit for bit,
 and the automatic choice must equal the kernel mmq_kernel_choice names."""
 import numpy as np
@@ -29,7 +29,8 @@ SHAPES = {
     binding.KERNEL_DOT4: [(1, 1, 256), (2, 17, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
                           (6, 16, 256), (7, 131, 2304), (8, 256, 11008)],
     binding.KERNEL_NARROW: [(1, 1, 256), (2, 65, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
-                            (6, 17, 1280), (7, 131, 2304), (8, 256, 11008), (8, 48, 3584)],
+                            (6, 17, 1280), (7, 131, 2304), (8, 256, 11008), (8, 48, 3584), (9, 70, 1280),
+                            (12, 33, 2304), (13, 17, 4352), (16, 130, 768)],
 }
 
 
@@ -51,14 +52,15 @@ def test_named_fp32_kernel_matches_oracle(kernel):
         check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "named kernel")
 
 
-@pytest.mark.parametrize("n,m", [(1, 64), (6, 64), (7, 300), (8, 300), (9, 64), (33, 129), (33, 20480), (48, 20352),
-                                 (65, 96)])
-def test_auto_equals_the_named_choice(n, m):
+@pytest.mark.parametrize("n,m,k", [(1, 64, 512), (5, 64, 512), (6, 64, 512), (7, 300, 512), (8, 300, 512),
+                                   (9, 64, 512), (12, 8200, 16384), (33, 129, 512), (33, 20480, 512),
+                                   (48, 20352, 512), (65, 96, 512)])
+def test_auto_equals_the_named_choice(n, m, k):
     """The entry point's own choice is bitwise the kernel mmq_kernel_choice
     names for the shape (the 33-token rows at 20480 take the binary16 kernel
-    at its 160-tile threshold; 20352 rows stay on the few-token kernel)."""
-    k = 512
-    note("auto choice n=%d m=%d" % (n, m))
+    at its 160-tile threshold; 20352 rows stay on the few-token kernel; 12
+    tokens on 8200 x 16384 take the narrow kernel's 32-row tiles)."""
+    note("auto choice n=%d m=%d k=%d" % (n, m, k))
     f = synth.random_fields(530 + n, m, k)
     x = synth.random_activations(530 + n, n, k)
     wd = to_dev(synth.pack_q4k(f))
@@ -122,3 +124,45 @@ def test_weight_streaming_kernels_run_to_run_and_token_slice_bitwise(kernel):
     a, b, s = (t.cpu().numpy().view(np.uint32) for t in (a, b, s))
     assert np.array_equal(a, b)
     assert np.array_equal(a[3:8], s)
+
+
+@pytest.mark.parametrize("n,m,k", [(7, 8200, 16384), (16, 8200, 16384), (9, 16400, 8192), (6, 16400, 8192)])
+def test_narrow_32_row_tiles(n, m, k):
+    """The narrow kernel's 32-row tiles, run by 8 waves per workgroup (257
+    tiles, 64 super-blocks per row) and by 4 (513 tiles, 32 super-blocks),
+    the last tile ragged: every output against the oracle, and the binary16
+    output bitwise the rounded float32 one."""
+    note("narrow 32-row tiles n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(560 + n, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(560 + n, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    q, ds = gpu_quantize(x)
+    wd = to_dev(w)
+    got = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_NARROW)
+    got16 = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_NARROW, f16=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got16.cpu().numpy().view(np.uint16),
+                          got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16 != rounded fp32"
+    rq, rds = oracle.quantize(x)
+    check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "narrow 32-row tiles")
+
+
+def test_narrow_32_row_tiles_run_to_run_and_token_slice_bitwise():
+    """The 32-row tiles sum in an order fixed by m and k alone too: a repeated
+    call and calls on token slices (other token-group counts) give the same
+    bits."""
+    m, k, n = 8200, 16384, 12
+    note("run-to-run narrow 32-row tiles n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(561, m, k)
+    x = synth.random_activations(561, n, k, "outliers")
+    wd = to_dev(synth.pack_q4k(f))
+    q, ds = gpu_quantize(x)
+    a = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_NARROW)
+    b = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_NARROW)
+    s1 = binding.fold_kernel(wd, m, k, q[2:12].contiguous(), ds[2:12].contiguous(), binding.KERNEL_NARROW)
+    s2 = binding.fold_kernel(wd, m, k, q[5:8].contiguous(), ds[5:8].contiguous(), binding.KERNEL_NARROW)
+    torch.cuda.synchronize()
+    a, b, s1, s2 = (t.cpu().numpy().view(np.uint32) for t in (a, b, s1, s2))
+    assert np.array_equal(a, b)
+    assert np.array_equal(a[2:12], s1)
+    assert np.array_equal(a[5:8], s2)
