@@ -68,12 +68,15 @@ __device__ __forceinline__ void q8_word(uint32_t y, uint32_t& p02, uint32_t& p13
 // buffer rsrc.  Inline asm, outside the compiler's wait bookkeeping: the
 // callers place the vmcnt waits that complete these copies themselves.
 // M0 is a reserved register; in the kernels using this nothing else sets or
-// reads it, so the clobber only tells the compiler what the asm does.
+// reads it, so the clobber only tells the compiler what the asm does.  A
+// load that writes LDS reads M0 and needs one wait state after an SALU
+// write of it (the compiler inserts the same s_nop 0 before its own such
+// loads; inside asm it does not).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
