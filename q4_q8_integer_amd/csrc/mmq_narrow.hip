@@ -41,11 +41,13 @@
 //     lane's block) into an accumulator of its own.
 //   * n <= 4G tokens run as G groups of 4; every weight operand serves all
 //     groups.
-//   * A workgroup is W waves on the same RT rows, each over a contiguous
-//     range of steps.  A step slot past the wave's range computes with
-//     d = dmin = 0 (adding exactly 0) on valid data.  The partial sums (W
-//     waves x 64/RT lanes per row) are added in LDS in a fixed order, so
-//     results do not depend on timing.  Within a wave the chunk sums are
+//   * A workgroup is W waves on the same RT rows, wave w taking the steps
+//     w, w + W, w + 2W, ...: the waves read W adjacent blocks of every row at
+//     about the same time, runs that a single wave's step is too short for
+//     (contiguous step ranges per wave were 2-8% slower).  A step slot past
+//     k computes with d = dmin = 0 (adding exactly 0) on valid data.  The
+//     partial sums (W waves x 64/RT lanes per row) are added in LDS in a
+//     fixed order, so results do not depend on timing.  Within a wave the chunk sums are
 //     added into a float32 accumulator that is moved (with the min-term
 //     accumulator) into a second one every 32 super-blocks, which keeps the
 //     rounding error of very long rows (k up to 2^24) within the float32 bar.
@@ -216,9 +218,10 @@ __global__ __launch_bounds__(64 * WM) void mmq_narrow_kernel(const uint8_t* __re
     const int row0 = blockIdx.x * RT;
     const int rows = min(RT, M - row0);
     const int S = K >> 8, C = K >> 5;
-    const int steps = (S + kS - 1) / kS;
-    const int sb0 = kS * (int)((int64_t)steps * wv / W);
-    const int sb1 = min(S, kS * (int)((int64_t)steps * (wv + 1) / W));
+    // Interleaved: wave wv takes the steps wv, wv + W, wv + 2W, ..., so the
+    // W waves on these rows read W adjacent blocks of every row together.
+    const int D = kS * W;          // super-blocks between a wave's steps
+    const int sb0 = kS * wv, sb1 = S;
 
     // Copy sources.  Weight instruction c: lane u fills slot i = 64c + u of
     // row i / kRowPieces, whose piece p has wslot(row, p) = i % kRowPieces
@@ -281,19 +284,19 @@ __global__ __launch_bounds__(64 * WM) void mmq_narrow_kernel(const uint8_t* __re
     // before a step is computed; one wait for everything at the top of each
     // step.
     if (sb0 < sb1) issue_step<G, RT>(cp, sb0, S, area0[wv]);
-    for (int st = sb0, n_st = 0; st < sb1; st += 2 * kS, n_st += 2) {
+    for (int st = sb0, n_st = 0; st < sb1; st += 2 * D, n_st += 2) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
         __builtin_amdgcn_sched_barrier(0);
-        if (st + kS < sb1) issue_step<G, RT>(cp, st + kS, S, area1[wv]);
+        if (st + D < sb1) issue_step<G, RT>(cp, st + D, S, area1[wv]);
         __builtin_amdgcn_sched_barrier(0);
         compute_step<G, RT>(area0[wv], st + s < sb1, r, s, h, ti, acc, accm);
         flush(n_st);
-        if (st + kS >= sb1) break;
+        if (st + D >= sb1) break;
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
         __builtin_amdgcn_sched_barrier(0);
-        if (st + 2 * kS < sb1) issue_step<G, RT>(cp, st + 2 * kS, S, area0[wv]);
+        if (st + 2 * D < sb1) issue_step<G, RT>(cp, st + 2 * D, S, area0[wv]);
         __builtin_amdgcn_sched_barrier(0);
-        compute_step<G, RT>(area1[wv], st + kS + s < sb1, r, s, h, ti, acc, accm);
+        compute_step<G, RT>(area1[wv], st + D + s < sb1, r, s, h, ti, acc, accm);
         flush(n_st + 1);
     }
 
