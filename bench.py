@@ -119,8 +119,8 @@ def kernel_choice(desc, f, n):
 def compute_dtype(desc, f, n):
     """Arithmetic type of the kernel the library runs for this call: "f16"
     for the binary16-MFMA kernels (exact integer operands in binary16,
-    float32 accumulation), "int8" for the dot4, narrow, few-token and
-    int8-MFMA kernels."""
+    float32 accumulation), "int8" for the dot4, narrow, stream, few-token
+    and int8-MFMA kernels."""
     from q4_q8_integer_amd import binding
     return "f16" if kernel_choice(desc, f, n)[1] == binding.KERNEL_F16 else "int8"
 
@@ -133,7 +133,7 @@ def kernel_source(desc, f, n):
     names = ({binding.KERNEL_DOT4: "mmq_q6k_gemv.hip", binding.KERNEL_F16: "mmq_q6k_f16.hip",
               binding.KERNEL_I8: "mmq_q6k_i8.hip"} if q6 else
              {binding.KERNEL_DOT4: "mmq_gemv.hip", binding.KERNEL_NARROW: "mmq_narrow.hip",
-              binding.KERNEL_FEW: "mmq_small.hip", binding.KERNEL_F16: "mmq_f16.hip",
+              binding.KERNEL_STREAM: "mmq_stream.hip", binding.KERNEL_FEW: "mmq_small.hip", binding.KERNEL_F16: "mmq_f16.hip",
               binding.KERNEL_I8: "mmq_i8.hip"})
     return "q4_q8_integer_amd/csrc/" + names[kid]
 
@@ -399,7 +399,7 @@ def main():
                     help="time the binary16-output entry point (mmq_*_f16out) instead of the float32 one")
     ap.add_argument("--kernel", default=None,
                     help="run the MMQ on this named kernel through the fold entry point "
-                         "(mmq_q4k_q8_fold / mmq_q6k_q8_fold: dot4, narrow, few, f16 or i8) instead "
+                         "(mmq_q4k_q8_fold / mmq_q6k_q8_fold: dot4, narrow, stream, few, f16 or i8) instead "
                          "of the library's own choice; GGUF-layout, int8-code workloads only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (known bytes) so that "

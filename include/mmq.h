@@ -155,7 +155,9 @@ enum mmq_kernel {
     MMQ_KERNEL_FEW = 2,   /* int8 MFMA on 16-token tiles, weights streamed once; n <= 64 (q4_K) */
     MMQ_KERNEL_F16 = 3,   /* binary16 MFMA on exact sc*q4 and q8 operands, 128-row tiles; any n */
     MMQ_KERNEL_I8 = 4,    /* int8 MFMA on 128 x 128 tiles with a three-operation fold; any n */
-    MMQ_KERNEL_NARROW = 5 /* int8 4x4x4 MFMA, weights staged through LDS, streamed once; n <= 16 */
+    MMQ_KERNEL_NARROW = 5, /* int8 4x4x4 MFMA, weights staged through LDS, streamed once; n <= 16 */
+    MMQ_KERNEL_STREAM = 6  /* the narrow kernel's arithmetic, tokens held in LDS per workgroup of many
+                              row tiles, weights streamed in 576-byte runs; n <= 8 */
 };
 
 /*
@@ -163,7 +165,7 @@ enum mmq_kernel {
  * (out_f16 != 0) on a kernel the caller names, for comparisons, benchmarks
  * and validation of every kernel on any shape.  With MMQ_KERNEL_AUTO it is
  * exactly that entry point.  A kernel outside its token range (DOT4 above 8
- * tokens, NARROW above 16, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
+ * tokens, NARROW above 16, STREAM above 8, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
  * HIP call; other arguments, errors and empty calls as for
  * mmq_q4k_q8_fp32out.
  */
@@ -222,8 +224,8 @@ int mmq_q6k_q8_f16out(const void *w, int64_t m, int64_t k, const int8_t *q,
 
 /*
  * mmq_q6k_q8_fold - mmq_q4k_q8_fold for q6_K weights: MMQ_KERNEL_AUTO,
- * MMQ_KERNEL_DOT4 (n <= 8), MMQ_KERNEL_F16 or MMQ_KERNEL_I8 (MMQ_KERNEL_FEW
- * and MMQ_KERNEL_NARROW return MMQ_ERR_KERNEL).
+ * MMQ_KERNEL_DOT4 (n <= 8), MMQ_KERNEL_F16 or MMQ_KERNEL_I8 (MMQ_KERNEL_FEW,
+ * MMQ_KERNEL_NARROW and MMQ_KERNEL_STREAM return MMQ_ERR_KERNEL).
  */
 int mmq_q6k_q8_fold(const void *w, int64_t m, int64_t k, const int8_t *q, const uint32_t *ds,
                     int64_t n, void *out, int out_f16, int kernel, hipStream_t stream);

@@ -21,9 +21,9 @@ EXPORTS = ("q8_quantize_rows", "q8_quantize_silu_mul", "mmq_q4k_q8", "mmq_q4k_q8
            "mmq_kernel_choice", "mmq_status_string")
 
 # enum mmq_kernel / enum mmq_format of include/mmq.h
-KERNEL_AUTO, KERNEL_DOT4, KERNEL_FEW, KERNEL_F16, KERNEL_I8, KERNEL_NARROW = 0, 1, 2, 3, 4, 5
+KERNEL_AUTO, KERNEL_DOT4, KERNEL_FEW, KERNEL_F16, KERNEL_I8, KERNEL_NARROW, KERNEL_STREAM = 0, 1, 2, 3, 4, 5, 6
 KERNEL_NAMES = {KERNEL_DOT4: "dot4", KERNEL_FEW: "few", KERNEL_F16: "f16", KERNEL_I8: "i8",
-                KERNEL_NARROW: "narrow"}
+                KERNEL_NARROW: "narrow", KERNEL_STREAM: "stream"}
 (FORMAT_Q4K, FORMAT_Q4K_REPACKED, FORMAT_Q6K, FORMAT_Q4K_TILES, FORMAT_Q4K_REPACKED_TILES,
  FORMAT_Q6K_TILES) = range(6)
 Q4K_BLOCK_BYTES, Q6K_BLOCK_BYTES, REPACK_RECORD_BYTES = 144, 210, 2368

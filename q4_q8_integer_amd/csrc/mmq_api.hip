@@ -8,6 +8,7 @@
 
 #include "../../include/mmq.h"
 #include "internal.h"
+#include "stream.h"
 #include "q6k_device.h"
 
 namespace {
@@ -66,10 +67,19 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 // Kernel behind the q4_K fold entry points for MMQ_KERNEL_AUTO, by token
 // count (measured on the 28672 x 8192 and 8192 x 28672 matrices):
 //   n <= 5:   the vector-ALU dot4 kernel (at 5 tokens 30.0 / 31.2 us against
-//             34.8 / 30.7 us for the narrow kernel);
+//             34.8 / 30.7 us for the narrow kernel), except the stream kernel
+//             at 3-4 tokens where it fits (below);
 //   n <= 8:   the narrow 4x4x4 int8-MFMA kernel (at 6 tokens 35.1 / 31.2 us
 //             against 36.1 / 32.7 for dot4; at 7 / 8 tokens 36.5 / 32 us
-//             against 38.6-40 / 38-42 us for dot4);
+//             against 38.6-40 / 38-42 us for dot4), except the stream kernel
+//             where it fits: at least 7 x 256 tiles of 8 rows (7 or more per
+//             workgroup, so that its LDS token copy serves many rows) and
+//             k <= 8192 (at most two token phases).  Swept with weights
+//             streamed from HBM: 28672 x 8192 at 4 tokens 26.7 us against
+//             28.4 for dot4, at 6 / 7 / 8 tokens 31.1-31.2 us against
+//             34.1-34.8 us for the narrow kernel; 14336 x 4096 ahead from 3
+//             tokens; on 8192 x 28672 and the 4096-row shapes the narrow
+//             kernel stays ahead, at 1-2 tokens dot4;
 //   n <= 16:  the narrow kernel where its 32-row tiles give each wave at
 //             least 12 super-blocks (8192 x 28672 at 9 / 12 / 16 tokens
 //             36.7 / 37.1 / 43.5 us against 45.1 / 45.5 / 47.1 us for the
@@ -87,7 +97,11 @@ int q4k_auto_kernel(int64_t m, int64_t k, int64_t n) {
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
     const int w32 = mmq::narrow_waves32(m, k);
     const bool narrow_long = w32 > 0 && (k >> 8) / w32 >= 12;
-    return n <= 5                                      ? MMQ_KERNEL_DOT4
+    const bool stream = mmq::stream_fits(m, k);
+    return n <= 2                                      ? MMQ_KERNEL_DOT4
+           : n <= 4 && stream                          ? MMQ_KERNEL_STREAM
+           : n <= 5                                    ? MMQ_KERNEL_DOT4
+           : n <= 8 && stream                          ? MMQ_KERNEL_STREAM
            : n <= 8                                    ? MMQ_KERNEL_NARROW
            : n <= mmq::kNarrowMaxN && narrow_long      ? MMQ_KERNEL_NARROW
            : n <= 32                                   ? MMQ_KERNEL_FEW
@@ -128,6 +142,10 @@ int q4k_fold_launcher(int kernel, int64_t m, int64_t k, int64_t n, FoldLaunch* f
             if (n > mmq::kNarrowMaxN) return MMQ_ERR_KERNEL;
             *f = mmq::launch_mmq_fp32_narrow;
             return threads_ok((m + 15) / 16, 512) ? MMQ_OK : MMQ_ERR_OVERFLOW;
+        case MMQ_KERNEL_STREAM:
+            if (n > mmq::kStreamMaxN) return MMQ_ERR_KERNEL;
+            *f = mmq::launch_mmq_fp32_stream;
+            return threads_ok((m + 7) / 8, 512) ? MMQ_OK : MMQ_ERR_OVERFLOW;
         default:
             return MMQ_ERR_KERNEL;
     }

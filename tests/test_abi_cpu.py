@@ -195,7 +195,7 @@ def test_binding_raises_on_error_status(lib):
 
 
 KERNEL = -7
-K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW = 0, 1, 2, 3, 4, 5
+K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW, K_STREAM = 0, 1, 2, 3, 4, 5, 6
 
 
 @pytest.mark.parametrize("fn", ["mmq_q4k_q8_fold", "mmq_q6k_q8_fold"])
@@ -207,6 +207,7 @@ K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW = 0, 1, 2, 3, 4, 5
     ((A, 8, 512, A, 0, 3, A, 0, K_F16), NULL),
     ((A, 8, 512, A, A, 3, MIS, 1, K_F16), ALIGN),
     ((A, 8, 512, A, A, 3, A, 0, 9), KERNEL),          # unknown kernel id
+    ((A, 8, 512, A, A, 3, A, 0, 7), KERNEL),
     ((A, 8, 512, A, A, 3, A, 0, -1), KERNEL),
     ((A, 8, 512, A, A, 9, A, 0, K_DOT4), KERNEL),     # dot4 takes at most 8 tokens
     ((A, 8, 512, A, A, 0, A, 0, 9), OK),              # empty calls succeed before the kernel check
@@ -222,11 +223,14 @@ def test_fold_kernel_token_ranges(lib):
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_FEW, None) == KERNEL
     assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 17, A, 0, K_NARROW, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_NARROW, None) == KERNEL
+    # the stream kernel takes at most 8 tokens, q4_K only
+    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 9, A, 0, K_STREAM, None) == KERNEL
+    assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_STREAM, None) == KERNEL
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a HIP device")
 def test_fold_kernel_valid_arguments_reach_device_check(lib):
-    for k in (K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW):
+    for k in (K_AUTO, K_DOT4, K_FEW, K_F16, K_I8, K_NARROW, K_STREAM):
         assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 3, A, 0, k, None) == DEVICE
     for k in (K_AUTO, K_DOT4, K_F16, K_I8):
         assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 3, A, 1, k, None) == DEVICE
@@ -280,13 +284,29 @@ def test_kernel_choice_q4k(lib, m, n, want):
     # super-blocks of 256
     (8192, 28672, 9, K_NARROW), (8192, 28672, 16, K_NARROW), (8192, 28672, 17, K_FEW),
     (8160, 28672, 12, K_FEW),       # 255 tiles of 32 rows
-    (28672, 8192, 7, K_NARROW), (28672, 8192, 9, K_FEW),   # 4 waves x 8 super-blocks
+    (28672, 8192, 9, K_FEW),        # 4 waves x 8 super-blocks
+    (16384, 16384, 7, K_NARROW),
     (16384, 16384, 16, K_NARROW),   # 512 tiles: 4 waves x 16 super-blocks
     (8192, 8192, 12, K_FEW),        # 256 tiles but 8 waves x 4 super-blocks
     (8192, 24576, 12, K_NARROW),    # 8 waves x 12
     (8192, 22528, 12, K_FEW),       # 8 waves x 11
 ])
 def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
+    assert lib.mmq_kernel_choice(0, m, k, n) == want
+
+
+@pytest.mark.parametrize("m,k,n,want", [
+    # 3-4 and 6-8 tokens: the stream kernel where it has at least 7 x 256
+    # tiles of 8 rows and k <= 8192; dot4 at 1-2 and 5 tokens; the narrow
+    # kernel at 6-8 elsewhere
+    (28672, 8192, 1, K_DOT4), (28672, 8192, 2, K_DOT4), (28672, 8192, 3, K_STREAM),
+    (28672, 8192, 4, K_STREAM), (28672, 8192, 5, K_DOT4), (28672, 8192, 6, K_STREAM),
+    (28672, 8192, 8, K_STREAM), (14336, 4096, 7, K_STREAM), (14329, 4096, 7, K_STREAM),
+    (14328, 4096, 7, K_NARROW),     # 1791 tiles of 8
+    (28672, 8448, 7, K_NARROW),     # 33 super-blocks: three token phases
+    (8192, 28672, 7, K_NARROW), (8192, 28672, 4, K_DOT4),
+])
+def test_kernel_choice_stream(lib, m, k, n, want):
     assert lib.mmq_kernel_choice(0, m, k, n) == want
 
 

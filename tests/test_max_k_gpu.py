@@ -7,8 +7,9 @@ output row is checked against the oracle row of its token.
 
 The accuracy bar is the workloads' one (relative L2 <= 1e-5, max-abs <=
 1e-3 x row scale) for every kernel.  The dot4 and few-token kernels split k
-over several waves; the narrow kernel (7 tokens here) moves its float32
-partial into a second accumulator every 32 super-blocks; the binary16-MFMA
+over several waves; the narrow kernel (7 tokens here) and the stream kernel
+(named, 7 tokens) move their float32 partials into a second accumulator
+every 32 super-blocks; the binary16-MFMA
 kernels (more than 64 tokens) restart their
 float32 partial every 256 super-blocks into a second accumulator, so no
 float32 sum runs over more than 256 terms (one sum over all S = k/256 =
@@ -71,6 +72,25 @@ def test_max_k_q4k(n):
 @pytest.mark.parametrize("n", [1, 128])
 def test_max_k_q6k(n):
     run_max_k("q6k", n)
+
+
+def test_max_k_stream_kernel():
+    """The stream kernel (named: its automatic range has k <= 8192) at the
+    largest k: 4096 token phases of 16 super-blocks, 7 tokens, 20 rows (three
+    tiles of 8, the last partial, one per workgroup, four waves per tile each
+    taking every fourth step)."""
+    n = 7
+    note("max k: stream kernel n=%d" % n)
+    w, base, rq, rds, ref = case_inputs("q4k")
+    idx = np.arange(n) % 3
+    x = to_dev(base)[torch.from_numpy(idx).to("cuda:0")]
+    q, ds = binding.quantize(x)
+    del x
+    out = binding.fold_kernel(to_dev(w), M, K, q, ds, binding.KERNEL_STREAM)
+    torch.cuda.synchronize()
+    check_fp32(out.cpu().numpy(), ref[idx], "max k stream")
+    del q, ds, out
+    torch.cuda.empty_cache()
 
 
 def test_max_k_operand_tiles():

@@ -66,8 +66,8 @@ def test_few_token_weight_layouts(n, k):
     wave's last step runs past its range and the last row's past the
     matrix).  40 rows leave a half tile.  The dot4 result also equals the
     repacked-layout path bit for bit (same summation order); the entry
-    point's own choice (the narrow kernel at 7-8 tokens) meets the same
-    bar."""
+    point's own choice (the narrow kernel at 6-8 tokens on these 40 rows)
+    meets the same bar."""
     m = 40
     note("few-token layouts n=%d m=%d k=%d" % (n, m, k))
     f = synth.random_fields(700 + 10 * n + k % 7, m, k, sc_zero_frac=0.1)

@@ -4,8 +4,10 @@ three-operation fold, kept for comparison), f16 (the binary16-MFMA kernel,
 default above 64 tokens and from 33 where the matrix gives it enough tiles,
 here also on few tokens), few (the few-token int8-MFMA kernels, one tile up
 to 16 tokens and more above, default from 9 tokens, here also on fewer),
-dot4 (the vector-ALU kernel, default up to 5 tokens) and narrow (the 4x4x4
-int8-MFMA kernel on LDS-staged weights, up to 16 tokens, default from 6).  Each kernel's binary16
+dot4 (the vector-ALU kernel, default up to 5 tokens), narrow (the 4x4x4
+int8-MFMA kernel on LDS-staged weights, up to 16 tokens, default from 6) and
+stream (the narrow kernel's arithmetic with token operands shared in LDS by a
+workgroup of many 8-row tiles, up to 8 tokens).  Each kernel's binary16
 output must equal its float32 output rounded to nearest-even, bit for bit,
 and the automatic choice must equal the kernel mmq_kernel_choice names."""
 import numpy as np
@@ -31,6 +33,11 @@ SHAPES = {
     binding.KERNEL_NARROW: [(1, 1, 256), (2, 65, 2304), (3, 33, 512), (4, 200, 768), (5, 129, 4352),
                             (6, 17, 1280), (7, 131, 2304), (8, 256, 11008), (8, 48, 3584), (9, 70, 1280),
                             (12, 33, 2304), (13, 17, 4352), (16, 130, 768)],
+    # k of 1, 2 and 3 token phases of 16 super-blocks (the last ragged), 1-8 tokens; rows
+    # giving 4 waves per tile (1 or 2 tiles per workgroup), 2 (3 tiles) and 1 (5 tiles)
+    binding.KERNEL_STREAM: [(1, 1, 256), (2, 9, 2304), (3, 33, 4352), (4, 200, 768), (5, 131, 11008),
+                            (6, 17, 8192), (3, 2100, 1280), (7, 4111, 4352), (8, 5121, 1280),
+                            (4, 9000, 2304), (8, 64, 4096)],
 }
 
 
@@ -105,8 +112,8 @@ def test_tensor_wrappers_check_sizes_on_device():
         binding.fp32_tiles(w, m, k, qt, ds)
 
 
-@pytest.mark.parametrize("kernel", [binding.KERNEL_DOT4, binding.KERNEL_NARROW, binding.KERNEL_FEW],
-                         ids=lambda k: binding.KERNEL_NAMES[k])
+@pytest.mark.parametrize("kernel", [binding.KERNEL_DOT4, binding.KERNEL_NARROW, binding.KERNEL_STREAM,
+                                    binding.KERNEL_FEW], ids=lambda k: binding.KERNEL_NAMES[k])
 def test_weight_streaming_kernels_run_to_run_and_token_slice_bitwise(kernel):
     """The weight-streaming kernels sum every output in an order fixed by m
     and k alone (waves, steps and partial sums in index order): a repeated
@@ -166,3 +173,24 @@ def test_narrow_32_row_tiles_run_to_run_and_token_slice_bitwise():
     assert np.array_equal(a, b)
     assert np.array_equal(a[2:12], s1)
     assert np.array_equal(a[5:8], s2)
+
+
+@pytest.mark.parametrize("n,m,k", [(7, 16392, 4352), (5, 20000, 512), (8, 24583, 8448)])
+def test_stream_two_tiles_per_wave(n, m, k):
+    """The stream kernel with two 8-row tiles per wave (from 2049 tiles on:
+    10 to 16 tiles per workgroup), ragged in rows and in the last phase:
+    every output against the oracle, and the binary16 output bitwise the
+    rounded float32 one."""
+    note("stream two tiles per wave n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(570 + n, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(570 + n, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    q, ds = gpu_quantize(x)
+    wd = to_dev(w)
+    got = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_STREAM)
+    got16 = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_STREAM, f16=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got16.cpu().numpy().view(np.uint16),
+                          got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16 != rounded fp32"
+    rq, rds = oracle.quantize(x)
+    check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "stream two tiles per wave")
