@@ -157,7 +157,7 @@ enum mmq_kernel {
     MMQ_KERNEL_I8 = 4,    /* int8 MFMA on 128 x 128 tiles with a three-operation fold; any n */
     MMQ_KERNEL_NARROW = 5, /* int8 4x4x4 MFMA, weights staged through LDS, streamed once; n <= 16 */
     MMQ_KERNEL_STREAM = 6  /* the narrow kernel's arithmetic, tokens held in LDS per workgroup of many
-                              row tiles, weights streamed in 576-byte runs; n <= 8 */
+                              row tiles, weights streamed in 576-byte runs; n <= 16 */
 };
 
 /*
@@ -165,7 +165,7 @@ enum mmq_kernel {
  * (out_f16 != 0) on a kernel the caller names, for comparisons, benchmarks
  * and validation of every kernel on any shape.  With MMQ_KERNEL_AUTO it is
  * exactly that entry point.  A kernel outside its token range (DOT4 above 8
- * tokens, NARROW above 16, STREAM above 8, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
+ * tokens, NARROW and STREAM above 16, FEW above 64) or an unknown id returns MMQ_ERR_KERNEL before any
  * HIP call; other arguments, errors and empty calls as for
  * mmq_q4k_q8_fp32out.
  */

@@ -80,7 +80,12 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 //             34.1-34.8 us for the narrow kernel; 14336 x 4096 ahead from 3
 //             tokens; on 8192 x 28672 and the 4096-row shapes the narrow
 //             kernel stays ahead, at 1-2 tokens dot4;
-//   n <= 16:  the narrow kernel where its 32-row tiles give each wave at
+//   n <= 16:  the stream kernel at 9-12 tokens where it fits and k > 4096
+//             (28672 x 8192 at 9 / 12 tokens 39.4-39.6 / 39.3-39.9 us
+//             against 41.5-41.7 / 45.0-45.1 us for the few-token kernel; at
+//             16 tokens the two are level, 47.2-48.5 against 47.5-47.6 us;
+//             on 14336 x 4096 the few-token kernel leads);
+//             the narrow kernel where its 32-row tiles give each wave at
 //             least 12 super-blocks (8192 x 28672 at 9 / 12 / 16 tokens
 //             36.7 / 37.1 / 43.5 us against 45.1 / 45.5 / 47.1 us for the
 //             few-token kernel; with 8 super-blocks per wave, on 28672 x
@@ -104,6 +109,7 @@ int q4k_auto_kernel(int64_t m, int64_t k, int64_t n) {
            : n <= 8 && stream                          ? MMQ_KERNEL_STREAM
            : n <= 8                                    ? MMQ_KERNEL_NARROW
            : n <= mmq::kNarrowMaxN && narrow_long      ? MMQ_KERNEL_NARROW
+           : n <= 12 && stream && (k >> 8) > 16        ? MMQ_KERNEL_STREAM
            : n <= 32                                   ? MMQ_KERNEL_FEW
            : n <= mmq::kSmallMaxN && f16_tiles < 160   ? MMQ_KERNEL_FEW
                                                        : MMQ_KERNEL_F16;

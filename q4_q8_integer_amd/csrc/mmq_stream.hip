@@ -1,4 +1,4 @@
-// mmq_stream.hip - q4_K x q8 matmul for a few tokens (1 <= n <= 8), float32
+// mmq_stream.hip - q4_K x q8 matmul for a few tokens (1 <= n <= 16), float32
 // or binary16 result: weights streamed in long runs past token operands that
 // a workgroup holds in LDS.
 //
@@ -11,8 +11,9 @@
 //
 //   * Token operands are shared.  A workgroup owns many 8-row tiles (one
 //     workgroup per CU), and its waves read the tokens' q8 rows and scale
-//     words from one copy in LDS: k is cut into phases of 16 super-blocks,
-//     the workgroup copies a phase's token rows (4G x 4 KiB) and words once,
+//     words from one copy in LDS: k is cut into phases of 16 super-blocks (8
+//     with more than 8 tokens), the workgroup copies a phase's token rows and
+//     words once,
 //     double-buffered, with one workgroup barrier per phase.  Each token byte
 //     is then read from L2 once per workgroup instead of once per few rows.
 //   * Weights stream in long runs.  A wave's step is 8 rows x 4 consecutive
@@ -33,11 +34,11 @@
 //   * weight area of a step: row r's 36 pieces (4 blocks x 9) in slots
 //     40r .. 40r + 39, piece p at slot 40r + (p ^ r): the 16 lanes of a
 //     half-wave (8 rows, 2 slots, one piece) read 16 distinct 4-bank groups;
-//   * token phase: token t's 16 super-blocks in slots 256t + 16u + .., piece
+//   * token phase: token t's kP super-blocks in slots 16 kP t + 16u + .., piece
 //     q of super-block u at 16u + (q ^ x), x = 2 (t & 3) + (u & 1): the
 //     eight (token, super-block) pairs that a half-wave's read touches fall
 //     in eight different 4-bank groups;
-//   * scale words of a phase: token t's 128 words at dword 129t + 8u + c;
+//   * scale words of a phase: token t's 8 kP words at dword (8 kP + 1) t + 8u + c;
 //     the odd row length puts the 32 words of one read in 32 banks.
 #include <algorithm>
 
@@ -56,18 +57,23 @@ constexpr int kRT = 8;                      // rows per tile
 constexpr int kSlots = 4;                   // super-blocks per step
 constexpr int kRowSlots = 40;               // 36 weight pieces of a row's run, padded
 constexpr int kAreaBytes = kRT * kRowSlots * 16;   // 5 KiB: five copy instructions
-constexpr int kPhase = 16;                  // super-blocks per token phase
-constexpr int kWordRow = 8 * kPhase + 1;    // dwords per token in a phase's word area
 constexpr int kMaxWaves = 8;
 constexpr int kFlushSteps = 32 / kSlots;    // a tile's steps between accumulator moves
 
+// A token phase for G groups of 4 tokens: kP super-blocks (16 with one or
+// two groups, 8 with three or four, so that the two buffers stay within
+// 64 KiB of token rows).
 template <int G>
 struct Phase {
+    static constexpr int kP = G <= 2 ? 16 : 8;                // super-blocks per phase
     static constexpr int kTok = 4 * G;                       // token rows (4 per group)
-    static constexpr int kTokSlots = kTok * 16 * kPhase;     // 16-byte slots
-    static constexpr int kTokLoads = kTokSlots / 64;         // 1 KiB copies (4 per token)
+    static constexpr int kTokSlots = kTok * 16 * kP;         // 16-byte slots
+    static constexpr int kTokLoads = kTokSlots / 64;         // 1 KiB copies (kP / 4 per token)
+    static constexpr int kWordRow = 8 * kP + 1;              // dwords per token's words (odd)
     static constexpr int kWords = kTok * kWordRow;           // dwords
-    static constexpr int kWordLoads = kTok * kPhase * 8 / 64;   // 256-byte copies (2 per token)
+    static constexpr int kWordLoads = kTok * kP * 8 / 64;    // 256-byte copies (kP / 8 per token)
+    static constexpr int kGroupBytes = 4 * 16 * kP * 16;     // token rows of one group
+    static constexpr int kGroupWordBytes = 4 * kWordRow * 4;  // words of one group
 };
 
 // One 16-byte direct-to-LDS copy per lane (the weight steps): lane i writes
@@ -119,7 +125,7 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
 }
 
-// Copy the token rows and scale words of phase ph (super-blocks 16ph ..)
+// Copy the token rows and scale words of phase ph (super-blocks kP ph ..)
 // into one phase buffer.  The copy instructions are dealt to the W waves;
 // every instruction runs on a whole wave.
 template <int G>
@@ -129,18 +135,20 @@ __device__ __forceinline__ void issue_phase(u32x4 qr, u32x4 dr, int ph, int S, i
     const int C = S * 8;
     for (int c = wv; c < P::kTokLoads + P::kWordLoads; c += W) {
         if (c < P::kTokLoads) {
-            // token t = c / 4, super-blocks 4 (c % 4) .. +3 of the phase
-            const int t = c >> 2, u = 4 * (c & 3) + (lane >> 4), qp = lane & 15;
+            // token t = c / (kP / 4), super-blocks 4 (c % (kP / 4)) .. +3 of the phase
+            constexpr int kQ = P::kP / 4;
+            const int t = c / kQ, cq = c % kQ, u = 4 * cq + (lane >> 4), qp = lane & 15;
             const int x = 2 * (t & 3) + (u & 1);
-            const int sb = min(kPhase * ph + u, S - 1);
+            const int sb = min(P::kP * ph + u, S - 1);
             const uint32_t src = (uint32_t)min(t, N - 1) * (uint32_t)K + (uint32_t)sb * 256u + 16u * (uint32_t)(qp ^ x);
-            asm_copy16(qr, lds_addr(tok + 256 * t + 64 * (c & 3)), src);
+            asm_copy16(qr, lds_addr(tok + 16 * P::kP * t + 64 * cq), src);
         } else {
-            // words: token t = c' / 2, half c' % 2 (64 words = 8 super-blocks)
-            const int cw = c - P::kTokLoads, t = cw >> 1;
-            const int wi = min(8 * kPhase * ph + 64 * (cw & 1) + lane, C - 1);
+            // words: token t = c' / (kP / 8), part c' % (kP / 8) (64 words = 8 super-blocks)
+            constexpr int kH = P::kP / 8;
+            const int cw = c - P::kTokLoads, t = cw / kH, ch = cw % kH;
+            const int wi = min(8 * P::kP * ph + 64 * ch + lane, C - 1);
             const uint32_t src = ((uint32_t)min(t, N - 1) * (uint32_t)C + (uint32_t)wi) * 4u;
-            asm_copy4(dr, lds_addr(word + kWordRow * t + 64 * (cw & 1)), src);
+            asm_copy4(dr, lds_addr(word + P::kWordRow * t + 64 * ch), src);
         }
     }
 }
@@ -176,16 +184,18 @@ __device__ __forceinline__ void issue_step(const uint8_t* w, const uint32_t (&ba
 // Per-lane LDS offsets of the token operands and scale words, fixed for the
 // whole kernel: lane (row r, slot s, half h, token ti) reads chunk
 // c = 4h + 2pp + e of its slot's super-block: token slots
-// 256 ti + 16 s + ((2c + part) ^ x), x = 2 ti + (s & 1) (phase-local
+// 16 kP ti + 16 s + ((2c + part) ^ x), x = 2 ti + (s & 1) (phase-local
 // super-blocks of a step start at a multiple of 4, so the parity of the
-// lane's super-block is s & 1), and word 129 ti + 8 s + c.  Token group g
-// adds 1024 slots and 516 words.
+// lane's super-block is s & 1), and word (8 kP + 1) ti + 8 s + c.  Token
+// group g adds 4 token rows of slots and of words.
 struct TokOff {
     uint32_t tok[2][2][2];   // [pp][e][part], bytes
     uint32_t word[2][2];     // [pp][e], bytes
 };
 
+template <int G>
 __device__ __forceinline__ void init_tokoff(TokOff& to, int s, int h, int ti) {
+    typedef Phase<G> P;
     const int x = 2 * ti + (s & 1);
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp)
@@ -194,8 +204,8 @@ __device__ __forceinline__ void init_tokoff(TokOff& to, int s, int h, int ti) {
             const int c = 4 * h + 2 * pp + e;
 #pragma unroll
             for (int part = 0; part < 2; ++part)
-                to.tok[pp][e][part] = 16u * (uint32_t)(256 * ti + 16 * s + ((2 * c + part) ^ x));
-            to.word[pp][e] = 4u * (uint32_t)(kWordRow * ti + 8 * s + c);
+                to.tok[pp][e][part] = 16u * (uint32_t)(16 * P::kP * ti + 16 * s + ((2 * c + part) ^ x));
+            to.word[pp][e] = 4u * (uint32_t)(P::kWordRow * ti + 8 * s + c);
         }
 }
 
@@ -266,8 +276,8 @@ __device__ __forceinline__ void compute_step(const uint8_t* area, const uint8_t*
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const v4u a0 = *reinterpret_cast<const v4u*>(tb + to.tok[pp][e][0] + 16384 * g);
-                const v4u a1 = *reinterpret_cast<const v4u*>(tb + to.tok[pp][e][1] + 16384 * g);
+                const v4u a0 = *reinterpret_cast<const v4u*>(tb + to.tok[pp][e][0] + Phase<G>::kGroupBytes * g);
+                const v4u a1 = *reinterpret_cast<const v4u*>(tb + to.tok[pp][e][1] + Phase<G>::kGroupBytes * g);
                 v4i D = v4i{kMagicBits, kMagicBits, kMagicBits, kMagicBits};
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a0[0], b[0], D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a0[1], b[1], D, 0, 0, 0);
@@ -277,7 +287,8 @@ __device__ __forceinline__ void compute_step(const uint8_t* area, const uint8_t*
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[1], b[5], D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[2], b[6], D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[3], b[7], D, 0, 0, 0);
-                const uint32_t wv = *reinterpret_cast<const uint32_t*>(wb + to.word[pp][e] + 4 * kWordRow * 4 * g);
+                const uint32_t wv =
+                    *reinterpret_cast<const uint32_t*>(wb + to.word[pp][e] + Phase<G>::kGroupWordBytes * g);
                 const float da = half_lo(wv);
                 const float dass = da * (float)(int16_t)(uint16_t)(wv >> 16);
                 accm[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(dass, mrow, accm[g], 0, 0, 0);
@@ -314,9 +325,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
     const int S = K >> 8, C = K >> 5;
     const int TG = TQ * TPW, tile0 = blockIdx.x * TG;
     const int js = wv % TQ, o = wv / TQ;
-    const int NJ = kSlots / WPT;                 // steps per phase per tile and wave (4 / WPT)
+    constexpr int kP = P::kP;
+    const int NJ = kP / kSlots / WPT;            // steps per phase per tile and wave
     const int NS = NJ * TPW;                     // steps per phase per wave
-    const int nph = (S + kPhase - 1) / kPhase;
+    const int nph = (S + kP - 1) / kP;
     const int E = nph * NS;
 
     const u32x4 qr = raw_rsrc(q, (uint32_t)N * (uint32_t)K);
@@ -325,12 +337,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
     uint32_t wbase[5];
     init_wcopy(wbase, lane, (uint32_t)row_bytes);
     TokOff to;
-    init_tokoff(to, s, h, ti);
+    init_tokoff<G>(to, s, h, ti);
 
     // Step e of this wave: phase e / NS; within it step j = o + WPT (rem / TPW)
     // of tile js + TQ (rem % TPW).
     auto step_row0 = [&](int e) { return (tile0 + js + TQ * ((e % NS) % TPW)) * kRT; };
-    auto step_sb = [&](int e) { return kPhase * (e / NS) + kSlots * (o + WPT * ((e % NS) / TPW)); };
+    auto step_sb = [&](int e) { return kP * (e / NS) + kSlots * (o + WPT * ((e % NS) / TPW)); };
 
     // acc: the chunk folds (plain floats: the fold's asm takes them one by
     // one); accm: the min-term MFMA accumulator; acc2: both, moved every 32
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
     };
     auto run = [&](int e, int j, const uint8_t* area) {
         const int ph = e / NS, st = step_sb(e);
-        const int u0 = st - kPhase * ph;   // the step's first phase-local super-block (a multiple of 4)
+        const int u0 = st - kP * ph;   // the step's first phase-local super-block (a multiple of 4)
         compute_step<G>(area, reinterpret_cast<const uint8_t*>(tok[ph & 1] + 16 * u0),
                         reinterpret_cast<const uint8_t*>(word[ph & 1] + 8 * u0), to, st + s < S, r, s, h, acc[j],
                         accm[j]);
@@ -408,11 +420,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
     }
 
     // Partial sums red[(wave * TPW + j) * G + g][v][lane] over the token
-    // buffers and areas (every wave is past its last phase barrier).  Output
+    // buffers (every wave is past its last phase barrier).  Output
     // (tile js + TQ j, row rr, token 4g + v) adds, for o = 0 .. WPT - 1 in
     // order, the lanes rr + 8 s + 32 h of wave js + TQ o, h then s in order.
-    float* red = reinterpret_cast<float*>(&area0[0][0]);
-    static_assert(sizeof(area0) >= kMaxWaves * 2 * 2 * 4 * 64 * 4, "reduction fits");
+    float* red = reinterpret_cast<float*>(&tok[0][0]);
+    static_assert(sizeof(tok) >= kMaxWaves * TPW * G * 4 * 64 * 4, "reduction fits");
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -453,6 +465,7 @@ hipError_t launch_g(const uint8_t* w, int m, int k, const int8_t* q, const uint3
                     bool half_out, hipStream_t stream) {
     int tq, tpw, wpt;
     stream_layout(m, tq, tpw, wpt);
+    wpt = std::min(wpt, Phase<G>::kP / kSlots);   // the steps of a phase per tile
     return tpw == 2 ? launch_t<G, 2>(w, m, k, q, ds, n, out, half_out, tq, wpt, stream)
                     : launch_t<G, 1>(w, m, k, q, ds, n, out, half_out, tq, wpt, stream);
 }
@@ -464,6 +477,8 @@ hipError_t launch_mmq_fp32_stream(const uint8_t* w, int m, int k, const int8_t* 
     switch ((n + 3) / 4) {
         case 1: return launch_g<1>(w, m, k, q, ds, n, out, half_out, stream);
         case 2: return launch_g<2>(w, m, k, q, ds, n, out, half_out, stream);
+        case 3: return launch_g<3>(w, m, k, q, ds, n, out, half_out, stream);
+        case 4: return launch_g<4>(w, m, k, q, ds, n, out, half_out, stream);
         default: return hipErrorInvalidValue;
     }
 }

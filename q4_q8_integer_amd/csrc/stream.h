@@ -15,7 +15,7 @@ namespace mmq {
 hipError_t launch_mmq_fp32_stream(const uint8_t* w, int m, int k, const int8_t* q,
                                   const uint32_t* ds, int n, void* out, bool half_out,
                                   hipStream_t stream);
-constexpr int kStreamMaxN = 8;
+constexpr int kStreamMaxN = 16;
 
 // The stream kernel's work split for m rows: TG = tq * tpw tiles of 8 rows
 // per workgroup, about one workgroup per CU (256), at most 16 tiles each

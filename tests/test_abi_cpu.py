@@ -223,8 +223,8 @@ def test_fold_kernel_token_ranges(lib):
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_FEW, None) == KERNEL
     assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 17, A, 0, K_NARROW, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_NARROW, None) == KERNEL
-    # the stream kernel takes at most 8 tokens, q4_K only
-    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 9, A, 0, K_STREAM, None) == KERNEL
+    # the stream kernel takes at most 16 tokens, q4_K only
+    assert lib.mmq_q4k_q8_fold(A, 8, 512, A, A, 17, A, 0, K_STREAM, None) == KERNEL
     assert lib.mmq_q6k_q8_fold(A, 8, 512, A, A, 5, A, 0, K_STREAM, None) == KERNEL
 
 
@@ -284,7 +284,7 @@ def test_kernel_choice_q4k(lib, m, n, want):
     # super-blocks of 256
     (8192, 28672, 9, K_NARROW), (8192, 28672, 16, K_NARROW), (8192, 28672, 17, K_FEW),
     (8160, 28672, 12, K_FEW),       # 255 tiles of 32 rows
-    (28672, 8192, 9, K_FEW),        # 4 waves x 8 super-blocks
+    (28672, 8192, 17, K_FEW),
     (16384, 16384, 7, K_NARROW),
     (16384, 16384, 16, K_NARROW),   # 512 tiles: 4 waves x 16 super-blocks
     (8192, 8192, 12, K_FEW),        # 256 tiles but 8 waves x 4 super-blocks
@@ -305,6 +305,9 @@ def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
     (14328, 4096, 7, K_NARROW),     # 1791 tiles of 8
     (28672, 8448, 7, K_NARROW),     # 33 super-blocks: three token phases
     (8192, 28672, 7, K_NARROW), (8192, 28672, 4, K_DOT4),
+    # 9-12 tokens: the stream kernel where it fits and k > 4096
+    (28672, 8192, 9, K_STREAM), (28672, 8192, 12, K_STREAM), (28672, 8192, 13, K_FEW),
+    (14336, 4096, 9, K_FEW), (28672, 4352, 12, K_STREAM),
 ])
 def test_kernel_choice_stream(lib, m, k, n, want):
     assert lib.mmq_kernel_choice(0, m, k, n) == want

@@ -7,7 +7,7 @@ to 16 tokens and more above, default from 9 tokens, here also on fewer),
 dot4 (the vector-ALU kernel, default up to 5 tokens), narrow (the 4x4x4
 int8-MFMA kernel on LDS-staged weights, up to 16 tokens, default from 6) and
 stream (the narrow kernel's arithmetic with token operands shared in LDS by a
-workgroup of many 8-row tiles, up to 8 tokens).  Each kernel's binary16
+workgroup of many 8-row tiles, up to 16 tokens).  Each kernel's binary16
 output must equal its float32 output rounded to nearest-even, bit for bit,
 and the automatic choice must equal the kernel mmq_kernel_choice names."""
 import numpy as np
@@ -37,7 +37,10 @@ SHAPES = {
     # giving 4 waves per tile (1 or 2 tiles per workgroup), 2 (3 tiles) and 1 (5 tiles)
     binding.KERNEL_STREAM: [(1, 1, 256), (2, 9, 2304), (3, 33, 4352), (4, 200, 768), (5, 131, 11008),
                             (6, 17, 8192), (3, 2100, 1280), (7, 4111, 4352), (8, 5121, 1280),
-                            (4, 9000, 2304), (8, 64, 4096)],
+                            (4, 9000, 2304), (8, 64, 4096),
+                            # 9-16 tokens: three and four groups, token phases of 8 super-blocks
+                            (9, 1, 256), (12, 9, 2304), (13, 33, 4352), (16, 200, 768), (10, 131, 11008),
+                            (11, 2100, 1280), (14, 4111, 4352), (16, 9000, 2304)],
 }
 
 
@@ -175,7 +178,8 @@ def test_narrow_32_row_tiles_run_to_run_and_token_slice_bitwise():
     assert np.array_equal(a[5:8], s2)
 
 
-@pytest.mark.parametrize("n,m,k", [(7, 16392, 4352), (5, 20000, 512), (8, 24583, 8448)])
+@pytest.mark.parametrize("n,m,k", [(7, 16392, 4352), (5, 20000, 512), (8, 24583, 8448), (15, 20000, 512),
+                                   (16, 16392, 2304)])
 def test_stream_two_tiles_per_wave(n, m, k):
     """The stream kernel with two 8-row tiles per wave (from 2049 tiles on:
     10 to 16 tiles per workgroup), ragged in rows and in the last phase:
