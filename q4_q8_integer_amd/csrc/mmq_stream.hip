@@ -38,8 +38,12 @@
 //     q of super-block u at 16u + (q ^ x), x = 2 (t & 3) + (u & 1): the
 //     eight (token, super-block) pairs that a half-wave's read touches fall
 //     in eight different 4-bank groups;
-//   * scale words of a phase: token t's 8 kP words at dword (8 kP + 1) t + 8u + c;
-//     the odd row length puts the 32 words of one read in 32 banks.
+//   * scale words of a phase: token t's 8 kP words at dword (8 kP + 1) t + 8u + c
+//     as copied; after the phase barrier the workgroup converts them once to
+//     (da, da*ssum) float pairs at the same index (a second barrier), so the
+//     arithmetic reads one pair per chunk and group instead of a word and
+//     three conversions.  The odd row length keeps a read's pairs in
+//     distinct banks.
 #include <algorithm>
 
 #include "internal.h"
@@ -73,7 +77,7 @@ struct Phase {
     static constexpr int kWords = kTok * kWordRow;           // dwords
     static constexpr int kWordLoads = kTok * kP * 8 / 64;    // 256-byte copies (kP / 8 per token)
     static constexpr int kGroupBytes = 4 * 16 * kP * 16;     // token rows of one group
-    static constexpr int kGroupWordBytes = 4 * kWordRow * 4;  // words of one group
+    static constexpr int kGroupWordBytes = 4 * kWordRow * 8;  // (da, da*ssum) pairs of one group
 };
 
 // One 16-byte direct-to-LDS copy per lane (the weight steps): lane i writes
@@ -190,7 +194,7 @@ __device__ __forceinline__ void issue_step(const uint8_t* w, const uint32_t (&ba
 // group g adds 4 token rows of slots and of words.
 struct TokOff {
     uint32_t tok[2][2][2];   // [pp][e][part], bytes
-    uint32_t word[2][2];     // [pp][e], bytes
+    uint32_t word[2][2];     // [pp][e], bytes into the (da, da*ssum) pairs
 };
 
 template <int G>
@@ -205,7 +209,7 @@ __device__ __forceinline__ void init_tokoff(TokOff& to, int s, int h, int ti) {
 #pragma unroll
             for (int part = 0; part < 2; ++part)
                 to.tok[pp][e][part] = 16u * (uint32_t)(16 * P::kP * ti + 16 * s + ((2 * c + part) ^ x));
-            to.word[pp][e] = 4u * (uint32_t)(P::kWordRow * ti + 8 * s + c);
+            to.word[pp][e] = 8u * (uint32_t)(P::kWordRow * ti + 8 * s + c);
         }
 }
 
@@ -287,10 +291,8 @@ __device__ __forceinline__ void compute_step(const uint8_t* area, const uint8_t*
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[1], b[5], D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[2], b[6], D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_i32_4x4x4i8((int)a1[3], b[7], D, 0, 0, 0);
-                const uint32_t wv =
-                    *reinterpret_cast<const uint32_t*>(wb + to.word[pp][e] + Phase<G>::kGroupWordBytes * g);
-                const float da = half_lo(wv);
-                const float dass = da * (float)(int16_t)(uint16_t)(wv >> 16);
+                const float2 dd = *reinterpret_cast<const float2*>(wb + to.word[pp][e] + Phase<G>::kGroupWordBytes * g);
+                const float da = dd.x, dass = dd.y;
                 accm[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(dass, mrow, accm[g], 0, 0, 0);
                 fold_quad(acc[g], da, fmaf(dsce, as_float(D[0]), nk), fmaf(dsce, as_float(D[1]), nk),
                           fmaf(dsce, as_float(D[2]), nk), fmaf(dsce, as_float(D[3]), nk));
@@ -314,7 +316,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
     // compiler can tell the arrays apart (a pointer selected between two
     // arrays would make it wait for every copy before a token read).
     __shared__ __attribute__((aligned(16))) uint4 tok[2][P::kTokSlots];
-    __shared__ __attribute__((aligned(16))) uint32_t word[2][P::kWords];
+    __shared__ __attribute__((aligned(16))) uint32_t word[P::kWords];    // the next phase's words, as copied
+    __shared__ __attribute__((aligned(16))) float2 wpair[P::kWords];     // this phase's (da, da*ssum)
     __shared__ __attribute__((aligned(16))) uint8_t area0[kMaxWaves][kAreaBytes];
     __shared__ __attribute__((aligned(16))) uint8_t area1[kMaxWaves][kAreaBytes];
 
@@ -372,34 +375,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmq_stream_kernel(const uint8_
             }
         }
     };
+    // The words of a phase as (da, da*ssum) pairs, each thread a share.
+    auto convert_words = [&]() {
+        for (int i = threadIdx.x; i < P::kWords; i += blockDim.x) {
+            const uint32_t wd = word[i];
+            const float da = half_lo(wd);
+            wpair[i] = make_float2(da, da * (float)(int16_t)(uint16_t)(wd >> 16));   // exact
+        }
+    };
     // End of phase ph (after this wave's last step of it): every wave's copies
-    // of phase ph + 1 are complete, and phase ph's buffer is free.
+    // of phase ph + 1 are complete and phase ph's buffers are free; the words
+    // of phase ph + 1 are converted (a second barrier before their use).
     auto phase_end = [&](int ph) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
         __syncthreads();
+        if (ph + 1 < nph) {
+            convert_words();
+            __syncthreads();
+        }
     };
-    // At the top of the first step of phase p >= 1 (after its wait): the
-    // copies of phase p + 1, into the buffer of phase p - 1.  They have the
-    // step's compute to land; the next step's wait completes them.
+    // At the top of the first step of phase p (after its wait): the copies of
+    // phase p + 1, token rows into the buffer of phase p - 1, words into the
+    // copy buffer (phase p's were converted at the last phase end).  They
+    // have the step's compute to land; the next step's wait completes them.
     auto next_phase = [&](int e) {
         const int p = e / NS;
-        if (e == p * NS && p >= 1 && p + 1 < nph)
-            issue_phase<G>(qr, dr, p + 1, S, N, K, wv, W, lane, tok[(p + 1) & 1], word[(p + 1) & 1]);
+        if (e == p * NS && p + 1 < nph)
+            issue_phase<G>(qr, dr, p + 1, S, N, K, wv, W, lane, tok[(p + 1) & 1], word);
     };
     auto run = [&](int e, int j, const uint8_t* area) {
         const int ph = e / NS, st = step_sb(e);
         const int u0 = st - kP * ph;   // the step's first phase-local super-block (a multiple of 4)
         compute_step<G>(area, reinterpret_cast<const uint8_t*>(tok[ph & 1] + 16 * u0),
-                        reinterpret_cast<const uint8_t*>(word[ph & 1] + 8 * u0), to, st + s < S, r, s, h, acc[j],
+                        reinterpret_cast<const uint8_t*>(wpair + 8 * u0), to, st + s < S, r, s, h, acc[j],
                         accm[j]);
         flush(j, e);
         if ((e + 1) % NS == 0) phase_end(ph);
     };
 
-    issue_phase<G>(qr, dr, 0, S, N, K, wv, W, lane, tok[0], word[0]);
-    if (nph > 1) issue_phase<G>(qr, dr, 1, S, N, K, wv, W, lane, tok[1], word[1]);
+    issue_phase<G>(qr, dr, 0, S, N, K, wv, W, lane, tok[0], word);
     issue_step(w, wbase, step_row0(0), step_sb(0), M, row_bytes, area0[wv]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt(0));
+    __syncthreads();
+    convert_words();
     __syncthreads();
     // Steps in pairs (areas 0 and 1); with TPW = 2 the pair is one step of
     // each tile at the same k.
