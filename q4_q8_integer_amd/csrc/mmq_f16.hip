@@ -445,13 +445,15 @@ template <int TB, bool H, bool REP, bool QT, bool BIG>
 __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__ w,
                                                      const int8_t* __restrict__ q,
                                                      const uint32_t* __restrict__ ds,
-                                                     int M, int N, int K, int tiles_m,
+                                                     int M, int N, int K, int tiles_m, int tile_m0,
                                                      void* __restrict__ out) {
     __shared__ Stage stage[2];
     __shared__ StageB stage_b[2];
 
     const int tid = threadIdx.x;
-    const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
+    // row tiles tile_m0 .. tile_m0 + tiles_m - 1 of the M rows (a launch may
+    // cover part of them), token tiles of TB
+    const int bm = tile_m0 + blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
     const int row0 = bm * BM, tok0 = bn * TB;
     const int stages = K >> 7;
 
@@ -594,12 +596,33 @@ __global__ __launch_bounds__(NT) void mmq_f16_kernel(const uint8_t* __restrict__
 // tokens 99 -> 88 us per projection: its 4096-row projections have 128 tiles
 // of 128 tokens); with enough tiles the halved tiles lose (2630-token FFN
 // 565 -> 690 us: each converts the whole weight tile for half the tokens).
-static void tile_shape(int m, int n, int& tiles_m, bool& half_tiles, int64_t& tiles) {
-    tiles_m = (m + BM - 1) / BM;
-    const int64_t full = (int64_t)tiles_m * ((n + BN - 1) / BN);
-    half_tiles = full < 256;
-    const int tb = half_tiles ? BN / 2 : BN;
-    tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
+//
+// Where the 128-token tiles fill some rounds of 256 CUs and then part of one
+// more, the launch is cut by rows (split_m): the first split_m row tiles in
+// 128-token tiles, a whole number of rounds, and the remaining rows in
+// 64-token tiles, at most one round of half-size tiles in place of the tail
+// round (each output is the same arithmetic in either tile, bit for bit).
+// The 11008-row projections of the 7B layer set: 86 x 16 tiles at 2048
+// tokens = 80 x 16 + 6 x 32; 86 x 4 at 512 tokens = 64 x 4 + 22 x 8.
+struct TileShape {
+    int tiles_m;     // row tiles of 128
+    bool half;       // the whole launch in 64-token tiles
+    int split_m;     // 0, or the row tiles of the 128-token part
+};
+
+static TileShape tile_shape(int m, int n) {
+    TileShape t;
+    t.tiles_m = (m + BM - 1) / BM;
+    const int64_t nt = (n + BN - 1) / BN, full = (int64_t)t.tiles_m * nt;
+    t.half = full < 256;
+    t.split_m = 0;
+    if (!t.half && full % 256 != 0)
+        for (int r = t.tiles_m - 1; r >= 1; --r)
+            if ((int64_t)r * nt % 256 == 0) {
+                if ((int64_t)(t.tiles_m - r) * ((n + BN / 2 - 1) / (BN / 2)) <= 256) t.split_m = r;
+                break;
+            }
+    return t;
 }
 
 // The kernel instance for a launch: token tile, output type, weight layout,
@@ -613,46 +636,46 @@ static const void* pick_kernel(bool half_tiles, bool big) {
                : (const void*)mmq_f16_kernel<BN, H, REP, QT, false>;
 }
 
-static hipError_t launch(const void* f, const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
-                         int n, void* out, int tiles_m, int64_t tiles, hipStream_t stream) {
+static hipError_t launch_part(const void* f, const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
+                              int n, void* out, int tiles_m, int tile_m0, int tb, hipStream_t stream) {
     void* args[] = {(void*)&w, (void*)&q, (void*)&ds, (void*)&m, (void*)&n, (void*)&k,
-                    (void*)&tiles_m, (void*)&out};
+                    (void*)&tiles_m, (void*)&tile_m0, (void*)&out};
+    const int64_t tiles = (int64_t)tiles_m * ((n + tb - 1) / tb);
     return hipLaunchKernel(f, dim3((unsigned)tiles), dim3(NT), args, 0, stream);
+}
+
+// One launch, or the two parts of a row split, on the caller's stream.
+template <bool H, bool REP, bool QT>
+static hipError_t launch(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds, int n, void* out,
+                         hipStream_t stream) {
+    const TileShape t = tile_shape(m, n);
+    const bool big = (k >> 8) > kGroup;
+    if (t.split_m == 0)
+        return launch_part(pick_kernel<H, REP, QT>(t.half, big), w, m, k, q, ds, n, out, t.tiles_m, 0,
+                           t.half ? BN / 2 : BN, stream);
+    const hipError_t e = launch_part(pick_kernel<H, REP, QT>(false, big), w, m, k, q, ds, n, out, t.split_m, 0,
+                                     BN, stream);
+    if (e != hipSuccess) return e;
+    return launch_part(pick_kernel<H, REP, QT>(true, big), w, m, k, q, ds, n, out, t.tiles_m - t.split_m,
+                       t.split_m, BN / 2, stream);
 }
 
 hipError_t launch_mmq_fp32_f16(const uint8_t* w, int m, int k, const int8_t* q, const uint32_t* ds,
                                int n, void* out, bool half_out, hipStream_t stream) {
-    int tiles_m;
-    bool half_tiles;
-    int64_t tiles;
-    tile_shape(m, n, tiles_m, half_tiles, tiles);
-    const bool big = (k >> 8) > kGroup;
-    const void* f = half_out ? pick_kernel<true, false, false>(half_tiles, big)
-                             : pick_kernel<false, false, false>(half_tiles, big);
-    return launch(f, w, m, k, q, ds, n, out, tiles_m, tiles, stream);
+    return half_out ? launch<true, false, false>(w, m, k, q, ds, n, out, stream)
+                    : launch<false, false, false>(w, m, k, q, ds, n, out, stream);
 }
 
 hipError_t launch_mmq_fp32_f16_repacked(const uint8_t* wr, int m, int k, const int8_t* q,
                                         const uint32_t* ds, int n, float* out, hipStream_t stream) {
-    int tiles_m;
-    bool half_tiles;
-    int64_t tiles;
-    tile_shape(m, n, tiles_m, half_tiles, tiles);
-    const bool big = (k >> 8) > kGroup;
-    return launch(pick_kernel<false, true, false>(half_tiles, big), wr, m, k, q, ds, n, out, tiles_m, tiles,
-                  stream);
+    return launch<false, true, false>(wr, m, k, q, ds, n, out, stream);
 }
 
 hipError_t launch_mmq_fp32_f16_tiles(const uint8_t* w, bool repacked, int m, int k, const uint16_t* qt,
                                      const uint32_t* ds, int n, float* out, hipStream_t stream) {
-    int tiles_m;
-    bool half_tiles;
-    int64_t tiles;
-    tile_shape(m, n, tiles_m, half_tiles, tiles);
-    const bool big = (k >> 8) > kGroup;
-    const void* f = repacked ? pick_kernel<false, true, true>(half_tiles, big)
-                             : pick_kernel<false, false, true>(half_tiles, big);
-    return launch(f, w, m, k, reinterpret_cast<const int8_t*>(qt), ds, n, out, tiles_m, tiles, stream);
+    const int8_t* q = reinterpret_cast<const int8_t*>(qt);
+    return repacked ? launch<false, true, true>(w, m, k, q, ds, n, out, stream)
+                    : launch<false, false, true>(w, m, k, q, ds, n, out, stream);
 }
 
 }  // namespace mmq

@@ -198,3 +198,30 @@ def test_stream_two_tiles_per_wave(n, m, k):
                           got.cpu().numpy().astype(np.float16).view(np.uint16)), "f16 != rounded fp32"
     rq, rds = oracle.quantize(x)
     check_fp32(got.cpu().numpy(), oracle.out_f64(w, m, k, rq, rds), "stream two tiles per wave")
+
+
+def test_f16_row_split_launch():
+    """A binary16-kernel call whose 128-token tiles overshoot whole rounds of
+    256 runs in two launches cut by rows: 4220 rows (33 row tiles, the last
+    ragged) x 1024 tokens = 264 tiles -> 32 x 8 tiles of 128 tokens, then the
+    last row tile in 16 tiles of 64.  Sampled tokens against the oracle (every
+    token tile, both parts), the binary16 output bitwise the rounded float32
+    one, and the first 512 tokens (132 tiles of 64, one launch) bitwise equal
+    to the same rows of the split call."""
+    n, m, k = 1024, 4220, 512
+    note("f16 row split n=%d m=%d k=%d" % (n, m, k))
+    f = synth.random_fields(580, m, k, sc_zero_frac=0.1)
+    x = synth.random_activations(580, n, k, "outliers")
+    w = synth.pack_q4k(f)
+    wd = to_dev(w)
+    q, ds = gpu_quantize(x)
+    got = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_F16)
+    got16 = binding.fold_kernel(wd, m, k, q, ds, binding.KERNEL_F16, f16=True)
+    part = binding.fold_kernel(wd, m, k, q[:512].contiguous(), ds[:512].contiguous(), binding.KERNEL_F16)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.array_equal(got16.cpu().numpy().view(np.uint16), got.astype(np.float16).view(np.uint16))
+    assert np.array_equal(got[:512].view(np.uint32), part.cpu().numpy().view(np.uint32))
+    toks = np.r_[0:4, 127:130, 500:503, 1020:1024]
+    rq, rds = oracle.quantize(x[toks])
+    check_fp32(got[toks], oracle.out_f64(w, m, k, rq, rds), "f16 row split")
