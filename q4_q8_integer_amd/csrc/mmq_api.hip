@@ -65,54 +65,59 @@ using FoldLaunch = hipError_t (*)(const uint8_t*, int, int, const int8_t*, const
 bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block < (1LL << 32); }
 
 // Kernel behind the q4_K fold entry points for MMQ_KERNEL_AUTO, by token
-// count (measured on the 28672 x 8192 and 8192 x 28672 matrices):
-//   n <= 5:   the vector-ALU dot4 kernel (at 5 tokens 30.0 / 31.2 us against
-//             34.8 / 30.7 us for the narrow kernel), except the stream kernel
-//             at 3-4 tokens where it fits (below);
-//   n <= 8:   the narrow 4x4x4 int8-MFMA kernel (at 6 tokens 35.1 / 31.2 us
-//             against 36.1 / 32.7 for dot4; at 7 / 8 tokens 36.5 / 32 us
-//             against 38.6-40 / 38-42 us for dot4), except the stream kernel
-//             where it fits: at least 7 x 256 tiles of 8 rows (7 or more per
-//             workgroup, so that its LDS token copy serves many rows) and
-//             k <= 8192 (at most two token phases).  Swept with weights
-//             streamed from HBM: 28672 x 8192 at 4 tokens 26.7 us against
-//             28.4 for dot4, at 6 / 7 / 8 tokens 31.1-31.2 us against
-//             34.1-34.8 us for the narrow kernel; 14336 x 4096 ahead from 3
-//             tokens; on 8192 x 28672 and the 4096-row shapes the narrow
-//             kernel stays ahead, at 1-2 tokens dot4;
-//   n <= 16:  the stream kernel at 9-12 tokens where it fits and k > 4096
-//             (28672 x 8192 at 9 / 12 tokens 39.4-39.6 / 39.3-39.9 us
-//             against 41.5-41.7 / 45.0-45.1 us for the few-token kernel; at
-//             16 tokens the two are level, 47.2-48.5 against 47.5-47.6 us;
-//             on 14336 x 4096 the few-token kernel leads);
-//             the narrow kernel where its 32-row tiles give each wave at
-//             least 12 super-blocks (8192 x 28672 at 9 / 12 / 16 tokens
-//             36.7 / 37.1 / 43.5 us against 45.1 / 45.5 / 47.1 us for the
-//             few-token kernel; with 8 super-blocks per wave, on 28672 x
-//             8192, the two are level or the few-token kernel leads);
-//   n <= 32:  the few-token int8-MFMA kernels (one 16-token tile up to
-//             16 tokens, two tiles up to 32: 74-77 us against 87-89 us for
-//             the binary16 kernel on 28672 x 8192);
-//   n <= 64:  the few-token kernel, unless the binary16-MFMA kernel has
-//             enough 128 x 128 tiles to occupy the chip (>= 160: on 28672
-//             rows at 33 / 48 tokens 90.7 / 92.5 us against 97 / 101.5 us;
-//             with 64 tiles, on 8192 rows, it is three times slower);
-//   n > 64:   the binary16-MFMA kernel.
+// count and shape.  Set from timing sweeps of every kernel at 1-64 tokens
+// over 22 matrices from 1024 x 4096 to 32768 x 4096, 28672 x 8192 and
+// 8192 x 28672 (weights streamed from HBM; 478 cases): against the fastest
+// named kernel per case the choice loses 0.34% in the geometric mean, 16% at
+// most (the stream kernel on 6144-8160 rows, where it does not fit).
+//   dot4 (1-2 tokens, and 5 unless the narrow kernel has long rows): its
+//     workgroups of 16 rows fill the chip from about 10240 rows (8192 with
+//     rows of >= 64 super-blocks), and its waves split a row's super-blocks
+//     in 4-block steps, so it needs a multiple of 16 super-blocks: on
+//     4096-row matrices the narrow kernel is 2-86% faster, on 13824 x 5120
+//     (20 super-blocks) 23-51%;
+//   stream (3-4 and 6-16 tokens): where it fits (at least 7 x 256 tiles of 8
+//     rows, k <= 8192) and k is whole token phases (it computes every step
+//     of the last one: 16 super-blocks up to 8 tokens, 8 above; 24576 x 6144
+//     at 3-8 tokens is 8-18% slower than the narrow kernel); up to 8 tokens
+//     with 7 or 8 waves per workgroup (5-6 waves, from 9-12 tiles per
+//     workgroup, leave SIMDs idle: 20480 x 4096 5-13% behind), above 8
+//     where k > 4096 or a workgroup holds at least 14 tiles (one phase is
+//     paid back only over many rows: 14336 x 4096 at 9-16 tokens 8-24%
+//     behind the few-token kernel):
+//     28672 x 8192 at 4 / 7 / 12 / 16 tokens 25.9 / 30.9 / 39.3 / 45.1 us
+//     against 28.3 / 34.5 / 45.1 / 47.9 us for the next kernel;
+//   narrow (elsewhere up to 8 tokens; 9-16 where its 32-row tiles give each
+//     wave at least 12 super-blocks, or on at most 4096 rows): 8192 x 28672
+//     at 4 / 12 tokens 26.1 / 37.6 us against 28.7 / 45.8 us; 4096 x 14336
+//     at 1 / 12 tokens 8.2 / 13.6 us against 11.4 / 20.4 us;
+//   few-token int8-MFMA kernels (9-64 tokens otherwise): 11008 x 4096 at 12
+//     tokens 10.1 us against 12.5 us for the stream kernel;
+//   binary16-MFMA kernel: at 17-32 tokens where its 64-token tiles fill
+//     224-255 CUs in one round (28672 rows: 67.1-68.4 us against 70.2-78.5
+//     us; 24576 rows, 192 tiles, 8-10% behind; with 256 or more row tiles it
+//     takes 128-token tiles and loses), at
+//     33-64 tokens from 160 tiles (90.4 against 68.4 us at 33 tokens on
+//     28672 x 8192), and above 64 tokens.
 int q4k_auto_kernel(int64_t m, int64_t k, int64_t n) {
+    const int64_t S = k >> 8;
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
     const int w32 = mmq::narrow_waves32(m, k);
-    const bool narrow_long = w32 > 0 && (k >> 8) / w32 >= 12;
-    const bool stream = mmq::stream_fits(m, k);
-    return n <= 2                                      ? MMQ_KERNEL_DOT4
-           : n <= 4 && stream                          ? MMQ_KERNEL_STREAM
-           : n <= 5                                    ? MMQ_KERNEL_DOT4
-           : n <= 8 && stream                          ? MMQ_KERNEL_STREAM
-           : n <= 8                                    ? MMQ_KERNEL_NARROW
-           : n <= mmq::kNarrowMaxN && narrow_long      ? MMQ_KERNEL_NARROW
-           : n <= 12 && stream && (k >> 8) > 16        ? MMQ_KERNEL_STREAM
-           : n <= 32                                   ? MMQ_KERNEL_FEW
-           : n <= mmq::kSmallMaxN && f16_tiles < 160   ? MMQ_KERNEL_FEW
-                                                       : MMQ_KERNEL_F16;
+    const bool narrow_long = w32 > 0 && S / w32 >= 12;
+    // the stream kernel's tiles per workgroup and its waves (two tiles each above 8)
+    const int64_t tg = std::min<int64_t>(16, ((m + 7) / 8 + 255) / 256), tq = tg > 8 ? (tg + 1) / 2 : tg;
+    const bool stream = mmq::stream_fits(m, k) && S % 16 == 0 && tq >= 7;               // up to 8 tokens
+    const bool stream16 = mmq::stream_fits(m, k) && S % 8 == 0 && (S > 16 || tg >= 14);  // 9-16 tokens
+    const bool dot4 = S % 16 == 0 && (m >= 10240 || (m >= 8192 && S >= 64));
+    if (n <= 2) return dot4 ? MMQ_KERNEL_DOT4 : MMQ_KERNEL_NARROW;
+    if (n <= 4) return stream ? MMQ_KERNEL_STREAM : MMQ_KERNEL_NARROW;
+    if (n <= 5) return dot4 && !narrow_long ? MMQ_KERNEL_DOT4 : MMQ_KERNEL_NARROW;
+    if (n <= 8) return stream ? MMQ_KERNEL_STREAM : MMQ_KERNEL_NARROW;
+    if (n <= mmq::kNarrowMaxN)
+        return narrow_long || m <= 4096 ? MMQ_KERNEL_NARROW : stream16 ? MMQ_KERNEL_STREAM : MMQ_KERNEL_FEW;
+    if (n <= 32) return f16_tiles >= 224 && f16_tiles < 256 ? MMQ_KERNEL_F16 : MMQ_KERNEL_FEW;
+    if (n <= mmq::kSmallMaxN) return f16_tiles >= 160 ? MMQ_KERNEL_F16 : MMQ_KERNEL_FEW;
+    return MMQ_KERNEL_F16;
 }
 
 // The repacked-weight entry: above 16 tokens the binary16-MFMA kernel on the

@@ -267,8 +267,12 @@ def test_grid_limits_are_overflow_errors(lib):
 
 
 @pytest.mark.parametrize("m,n,want", [
-    (4096, 1, K_DOT4), (4096, 5, K_DOT4), (4096, 6, K_NARROW), (4096, 8, K_NARROW), (4096, 9, K_FEW),
-    (28672, 32, K_FEW),
+    # up to 4096 rows the narrow kernel takes 1-16 tokens (dot4's 16-row
+    # workgroups do not fill the chip there)
+    (4096, 1, K_NARROW), (4096, 5, K_NARROW), (4096, 6, K_NARROW), (4096, 8, K_NARROW), (4096, 9, K_NARROW),
+    (4096, 16, K_NARROW), (4096, 17, K_FEW), (10240, 1, K_DOT4), (10232, 1, K_NARROW),
+    # 17-32 tokens: the binary16 kernel where its 64-token tiles fill 224-255 CUs in one round
+    (28672, 32, K_F16), (28672, 17, K_F16), (28544, 17, K_FEW), (24576, 17, K_FEW), (32768, 32, K_FEW),
     (28672, 33, K_F16),            # 224 x 1 tiles of 128 x 128: enough for the chip
     (20480, 33, K_F16),            # 160 tiles: the threshold
     (20352, 33, K_FEW),            # 159 tiles
@@ -284,7 +288,9 @@ def test_kernel_choice_q4k(lib, m, n, want):
     # super-blocks of 256
     (8192, 28672, 9, K_NARROW), (8192, 28672, 16, K_NARROW), (8192, 28672, 17, K_FEW),
     (8160, 28672, 12, K_FEW),       # 255 tiles of 32 rows
-    (28672, 8192, 17, K_FEW),
+    (28672, 8192, 17, K_F16),       # 224 tiles of 64 tokens
+    (13824, 5120, 1, K_NARROW),     # 20 super-blocks per row: not dot4's multiple of 16
+    (8192, 28672, 1, K_DOT4), (8192, 8192, 1, K_NARROW),   # 8192 rows: dot4 only with >= 64 super-blocks
     (16384, 16384, 7, K_NARROW),
     (16384, 16384, 16, K_NARROW),   # 512 tiles: 4 waves x 16 super-blocks
     (8192, 8192, 12, K_FEW),        # 256 tiles but 8 waves x 4 super-blocks
@@ -296,18 +302,25 @@ def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
 
 
 @pytest.mark.parametrize("m,k,n,want", [
-    # 3-4 and 6-8 tokens: the stream kernel where it has at least 7 x 256
-    # tiles of 8 rows and k <= 8192; dot4 at 1-2 and 5 tokens; the narrow
-    # kernel at 6-8 elsewhere
+    # 3-4 and 6-16 tokens: the stream kernel where it has at least 7 x 256
+    # tiles of 8 rows, k <= 8192 in whole token phases, and up to 8 tokens 7
+    # or 8 waves per workgroup, above 8 k > 4096 or at least 14 tiles per
+    # workgroup; dot4 at 1-2 and 5 tokens; the narrow kernel elsewhere up to 8
     (28672, 8192, 1, K_DOT4), (28672, 8192, 2, K_DOT4), (28672, 8192, 3, K_STREAM),
     (28672, 8192, 4, K_STREAM), (28672, 8192, 5, K_DOT4), (28672, 8192, 6, K_STREAM),
-    (28672, 8192, 8, K_STREAM), (14336, 4096, 7, K_STREAM), (14329, 4096, 7, K_STREAM),
+    (28672, 8192, 8, K_STREAM), (14336, 4096, 7, K_STREAM), (14336, 4096, 3, K_STREAM),
     (14328, 4096, 7, K_NARROW),     # 1791 tiles of 8
+    (16384, 4096, 7, K_STREAM),     # 8 tiles and waves per workgroup
+    (18432, 4096, 7, K_NARROW),     # 9 tiles: 5 waves of two
+    (26624, 4096, 7, K_STREAM),     # 13 tiles: 7 waves
+    (24576, 6144, 7, K_NARROW),     # 24 super-blocks: a ragged 16-block phase
+    (24576, 6144, 12, K_STREAM),    # three 8-block phases
     (28672, 8448, 7, K_NARROW),     # 33 super-blocks: three token phases
-    (8192, 28672, 7, K_NARROW), (8192, 28672, 4, K_DOT4),
-    # 9-12 tokens: the stream kernel where it fits and k > 4096
-    (28672, 8192, 9, K_STREAM), (28672, 8192, 12, K_STREAM), (28672, 8192, 13, K_FEW),
-    (14336, 4096, 9, K_FEW), (28672, 4352, 12, K_STREAM),
+    (8192, 28672, 7, K_NARROW), (8192, 28672, 4, K_NARROW), (8192, 28672, 5, K_NARROW),
+    (28672, 8192, 9, K_STREAM), (28672, 8192, 12, K_STREAM), (28672, 8192, 13, K_STREAM),
+    (28672, 8192, 16, K_STREAM), (28672, 4096, 12, K_STREAM), (20480, 4096, 12, K_FEW),
+    (14336, 4096, 9, K_FEW),        # one phase over 7 tiles
+    (28672, 4352, 12, K_FEW),       # 17 super-blocks
 ])
 def test_kernel_choice_stream(lib, m, k, n, want):
     assert lib.mmq_kernel_choice(0, m, k, n) == want
