@@ -68,8 +68,8 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 // count and shape.  Set from timing sweeps of every kernel at 1-64 tokens
 // over 22 matrices from 1024 x 4096 to 32768 x 4096, 28672 x 8192 and
 // 8192 x 28672 (weights streamed from HBM; 478 cases): against the fastest
-// named kernel per case the choice loses 0.34% in the geometric mean, 16% at
-// most (the stream kernel on 6144-8160 rows, where it does not fit).
+// named kernel per case the choice loses 0.18% in the geometric mean, 8.4% at
+// most.
 //   dot4 (1-2 tokens, and 5 unless the narrow kernel has long rows): its
 //     workgroups of 16 rows fill the chip from about 10240 rows (8192 with
 //     rows of >= 64 super-blocks), and its waves split a row's super-blocks
@@ -84,11 +84,16 @@ bool threads_ok(int64_t blocks, int64_t per_block) { return blocks * per_block <
 //     workgroup, leave SIMDs idle: 20480 x 4096 5-13% behind), above 8
 //     where k > 4096 or a workgroup holds at least 14 tiles (one phase is
 //     paid back only over many rows: 14336 x 4096 at 9-16 tokens 8-24%
-//     behind the few-token kernel):
+//     behind the few-token kernel); and at 9-12 tokens on rows of at least
+//     64 super-blocks whatever the row count (6144 x 16384, 6144 x 28672 and
+//     8160 x 28672: 24.2 / 39.6 / 39.1 us against 27.3 / 44.3 / 45.2 us for
+//     the few-token kernel; at 13-16 tokens, or on rows of 32 super-blocks,
+//     the few-token kernel leads):
 //     28672 x 8192 at 4 / 7 / 12 / 16 tokens 25.9 / 30.9 / 39.3 / 45.1 us
 //     against 28.3 / 34.5 / 45.1 / 47.9 us for the next kernel;
 //   narrow (elsewhere up to 8 tokens; 9-16 where its 32-row tiles give each
-//     wave at least 12 super-blocks, or on at most 4096 rows): 8192 x 28672
+//     wave at least 11 super-blocks, or on at most 4096 rows; 8192 x 22528,
+//     11 per wave, at 12 tokens 28.9 us against 32.1 us for the stream kernel): 8192 x 28672
 //     at 4 / 12 tokens 26.1 / 37.6 us against 28.7 / 45.8 us; 4096 x 14336
 //     at 1 / 12 tokens 8.2 / 13.6 us against 11.4 / 20.4 us;
 //   few-token int8-MFMA kernels (9-64 tokens otherwise): 11008 x 4096 at 12
@@ -103,18 +108,21 @@ int q4k_auto_kernel(int64_t m, int64_t k, int64_t n) {
     const int64_t S = k >> 8;
     const int64_t f16_tiles = ((m + 127) / 128) * ((n + 127) / 128);
     const int w32 = mmq::narrow_waves32(m, k);
-    const bool narrow_long = w32 > 0 && S / w32 >= 12;
+    const bool narrow_long = w32 > 0 && S / w32 >= 11;
     // the stream kernel's tiles per workgroup and its waves (two tiles each above 8)
     const int64_t tg = std::min<int64_t>(16, ((m + 7) / 8 + 255) / 256), tq = tg > 8 ? (tg + 1) / 2 : tg;
     const bool stream = mmq::stream_fits(m, k) && S % 16 == 0 && tq >= 7;               // up to 8 tokens
     const bool stream16 = mmq::stream_fits(m, k) && S % 8 == 0 && (S > 16 || tg >= 14);  // 9-16 tokens
+    const bool stream12 = stream16 || (S % 8 == 0 && S >= 64);                           // 9-12 tokens
     const bool dot4 = S % 16 == 0 && (m >= 10240 || (m >= 8192 && S >= 64));
     if (n <= 2) return dot4 ? MMQ_KERNEL_DOT4 : MMQ_KERNEL_NARROW;
     if (n <= 4) return stream ? MMQ_KERNEL_STREAM : MMQ_KERNEL_NARROW;
     if (n <= 5) return dot4 && !narrow_long ? MMQ_KERNEL_DOT4 : MMQ_KERNEL_NARROW;
     if (n <= 8) return stream ? MMQ_KERNEL_STREAM : MMQ_KERNEL_NARROW;
     if (n <= mmq::kNarrowMaxN)
-        return narrow_long || m <= 4096 ? MMQ_KERNEL_NARROW : stream16 ? MMQ_KERNEL_STREAM : MMQ_KERNEL_FEW;
+        return narrow_long || m <= 4096                  ? MMQ_KERNEL_NARROW
+               : stream16 || (n <= 12 && stream12)       ? MMQ_KERNEL_STREAM
+                                                         : MMQ_KERNEL_FEW;
     if (n <= 32) return f16_tiles >= 224 && f16_tiles < 256 ? MMQ_KERNEL_F16 : MMQ_KERNEL_FEW;
     if (n <= mmq::kSmallMaxN) return f16_tiles >= 160 ? MMQ_KERNEL_F16 : MMQ_KERNEL_FEW;
     return MMQ_KERNEL_F16;

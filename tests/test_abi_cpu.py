@@ -284,10 +284,11 @@ def test_kernel_choice_q4k(lib, m, n, want):
 
 @pytest.mark.parametrize("m,k,n,want", [
     # 9-16 tokens: the narrow kernel where its 32-row tiles (at least 256 of
-    # them, 4 waves each from 512 on, else 8) give each wave at least 12
+    # them, 4 waves each from 512 on, else 8) give each wave at least 11
     # super-blocks of 256
     (8192, 28672, 9, K_NARROW), (8192, 28672, 16, K_NARROW), (8192, 28672, 17, K_FEW),
-    (8160, 28672, 12, K_FEW),       # 255 tiles of 32 rows
+    (8160, 28672, 13, K_FEW),       # 255 tiles of 32 rows: not the narrow kernel
+    (8160, 28672, 12, K_STREAM),    # the stream kernel's 9-12-token rule for long rows
     (28672, 8192, 17, K_F16),       # 224 tiles of 64 tokens
     (13824, 5120, 1, K_NARROW),     # 20 super-blocks per row: not dot4's multiple of 16
     (8192, 28672, 1, K_DOT4), (8192, 8192, 1, K_NARROW),   # 8192 rows: dot4 only with >= 64 super-blocks
@@ -295,7 +296,9 @@ def test_kernel_choice_q4k(lib, m, n, want):
     (16384, 16384, 16, K_NARROW),   # 512 tiles: 4 waves x 16 super-blocks
     (8192, 8192, 12, K_FEW),        # 256 tiles but 8 waves x 4 super-blocks
     (8192, 24576, 12, K_NARROW),    # 8 waves x 12
-    (8192, 22528, 12, K_FEW),       # 8 waves x 11
+    (8192, 22528, 12, K_NARROW),    # 8 waves x 11
+    (8192, 20480, 13, K_FEW),       # 8 waves x 10: not the narrow kernel
+    (8192, 20480, 12, K_STREAM),    # the stream kernel's 9-12-token rule for long rows
 ])
 def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
     assert lib.mmq_kernel_choice(0, m, k, n) == want
@@ -320,6 +323,8 @@ def test_kernel_choice_q4k_by_k(lib, m, k, n, want):
     (28672, 8192, 9, K_STREAM), (28672, 8192, 12, K_STREAM), (28672, 8192, 13, K_STREAM),
     (28672, 8192, 16, K_STREAM), (28672, 4096, 12, K_STREAM), (20480, 4096, 12, K_FEW),
     (14336, 4096, 9, K_FEW),        # one phase over 7 tiles
+    (6144, 16384, 12, K_STREAM),    # 9-12 tokens on rows of >= 64 super-blocks
+    (6144, 16384, 13, K_FEW), (8192, 8192, 9, K_FEW), (8192, 28672, 12, K_NARROW),
     (28672, 4352, 12, K_FEW),       # 17 super-blocks
 ])
 def test_kernel_choice_stream(lib, m, k, n, want):
